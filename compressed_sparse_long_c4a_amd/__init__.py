@@ -1,0 +1,285 @@
+"""Python binding of libcsa: compressed sparse attention decode on MI355X (gfx950).
+
+Argument marshalling only.  Every step runs in the HIP kernels of ``libcsa.so``
+(built from ``csrc/`` by ``build.build()``); torch supplies device memory and
+the current HIP stream.  There is no fallback: if the library is not built,
+``lib()`` raises.
+
+Calls (see include/csa.h for the exact semantics of each):
+
+* ``compress_insert`` -- compress + RMSNorm + RoPE + paged insert, rolling
+  state append and window-row write.
+* ``index_topk`` (or ``index_score`` then ``index_select``) -- indexer scores
+  and exact top-k over c4a entries.
+* ``sparse_attn_decode`` -- attention with K = V over the selected entries
+  plus the sliding window, inverse RoPE at the query position.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+ABI_VERSION = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+
+class _CCache(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("dim", ctypes.c_int32),
+        ("rows_per_block", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
+        ("bt_stride", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+_CP = ctypes.POINTER(_CCache)
+
+_SIGNATURES = {
+    "csa_abi_version": (_I, []),
+    "csa_status_str": (ctypes.c_char_p, [_I]),
+    "csa_num_entries": (ctypes.c_int64, [_I, ctypes.c_int64]),
+    "csa_compress_insert": (_I, [_P, _I, _I, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _F, _I,
+                                 _CP, _CP, _CP]),
+    "csa_index_workspace_size": (_SZ, [_I, _I, _I]),
+    "csa_index_topk": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _CP, _I, _P, _P, _P, _SZ]),
+    "csa_index_score": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _CP, _I, _P, _SZ]),
+    "csa_index_select": (_I, [_P, _I, _P, _P, _I, _I, _I, _P, _P, _P, _SZ]),
+    "csa_sparse_attn_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "csa_sparse_attn_decode": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _CP, _I, _P, _I, _CP, _I,
+                                    _F, _F, _I, _P, _P, _P, _SZ]),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libcsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run compressed_sparse_long_c4a_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        if L.csa_abi_version() != ABI_VERSION:
+            raise RuntimeError("libcsa ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().csa_status_str(status).decode()
+
+
+class CsaError(RuntimeError):
+    def __init__(self, what: str, status: int):
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+        self.status = status
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise CsaError(what, status)
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    if t in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise ValueError(f"unsupported element type {t}")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+    return t
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class PagedCache:
+    """A paged cache in device memory (layout of ``csa_cache`` in include/csa.h).
+
+    rows:        [num_blocks, rows_per_block, dim] float32 | bfloat16 | uint8 (fp8 E4M3 codes)
+    block_table: [batch, bt_stride] int32 physical block ids
+    scales:      [num_blocks, rows_per_block] float32, fp8 caches only
+    """
+
+    def __init__(self, rows: torch.Tensor, block_table: torch.Tensor, scales: torch.Tensor | None = None):
+        _dev(rows, "rows", ndim=3)
+        _dev(block_table, "block_table", torch.int32, 2)
+        self.dtype = dtype_code(rows.dtype)
+        if self.dtype == FP8_E4M3:
+            if scales is None:
+                raise ValueError("fp8 cache needs scales")
+            _dev(scales, "scales", torch.float32, 2)
+            if tuple(scales.shape) != tuple(rows.shape[:2]):
+                raise ValueError("scales must be [num_blocks, rows_per_block]")
+        self.rows, self.block_table, self.scales = rows, block_table, scales
+
+    @property
+    def dim(self) -> int:
+        return self.rows.shape[2]
+
+    @property
+    def rows_per_block(self) -> int:
+        return self.rows.shape[1]
+
+    def c(self) -> _CCache:
+        return _CCache(self.rows.data_ptr(), _ptr(self.scales), self.dtype, self.rows.shape[2],
+                       self.rows.shape[1], self.rows.shape[0], self.block_table.data_ptr(),
+                       self.block_table.shape[1])
+
+
+def _cref(cache: PagedCache | None):
+    return None if cache is None else ctypes.pointer(cache.c())
+
+
+def num_entries(ratio: int, num_tokens: int) -> int:
+    """Compressed entries after num_tokens raw tokens (floor(num_tokens / ratio))."""
+    return lib().csa_num_entries(ratio, num_tokens)
+
+
+def compress_insert(ratio: int, ctx_lens: torch.Tensor, cu_new: torch.Tensor, new_raw: torch.Tensor,
+                    cu_entries: torch.Tensor, gate_logits: torch.Tensor, state: PagedCache,
+                    out: PagedCache, swa: PagedCache | None = None, gamma: torch.Tensor | None = None,
+                    eps: float = 1e-6, rope_base: float = 10000.0, rope_dims: int = 64) -> None:
+    """Emit the entries completed by new raw rows, append the rolling state, write window rows."""
+    _dev(ctx_lens, "ctx_lens", torch.int32, 1)
+    _dev(cu_new, "cu_new", torch.int32, 1)
+    _dev(cu_entries, "cu_entries", torch.int32, 1)
+    _dev(new_raw, "new_raw", (torch.float32, torch.bfloat16), 2)
+    _dev(gate_logits, "gate_logits", torch.float32, 2)
+    if gamma is not None:
+        _dev(gamma, "gamma", torch.float32, 1)
+    batch = ctx_lens.shape[0]
+    if cu_new.shape[0] != batch + 1 or cu_entries.shape[0] != batch + 1:
+        raise ValueError("cu_new and cu_entries need batch + 1 entries")
+    st = lib().csa_compress_insert(
+        _stream(), ratio, batch, ctx_lens.data_ptr(), cu_new.data_ptr(), new_raw.shape[0],
+        _ptr(new_raw), dtype_code(new_raw.dtype), cu_entries.data_ptr(), gate_logits.shape[0],
+        _ptr(gate_logits), _ptr(gamma), eps, rope_base, rope_dims, _cref(state), _cref(out), _cref(swa))
+    _check(st, "csa_compress_insert")
+
+
+def index_workspace_size(total_q: int, max_context: int, k: int) -> int:
+    return lib().csa_index_workspace_size(total_q, max_context, k)
+
+
+def _index_common(cu_q, q_pos, q_idx, head_w):
+    _dev(cu_q, "cu_q", torch.int32, 1)
+    _dev(q_pos, "q_pos", torch.int32, 1)
+    _dev(q_idx, "q_idx", (torch.bfloat16, torch.float32), 3)
+    _dev(head_w, "head_w", torch.float32, 2)
+    total_q, heads, d = q_idx.shape
+    if d != 128 or tuple(head_w.shape) != (total_q, heads) or q_pos.shape[0] != total_q:
+        raise ValueError("q_idx must be [total_q, heads, 128] and head_w [total_q, heads]")
+    return cu_q.shape[0] - 1, total_q, heads
+
+
+def index_topk(cu_q, q_pos, q_idx, head_w, idx_cache: PagedCache, k: int, max_context: int,
+               with_scores: bool = False, workspace: torch.Tensor | None = None):
+    """Top-k entry ids [total_q, k] int32 (ascending, -1 padded) and optionally their scores."""
+    batch, total_q, heads = _index_common(cu_q, q_pos, q_idx, head_w)
+    dev = q_idx.device
+    topk = torch.empty((total_q, k), dtype=torch.int32, device=dev)
+    scores = torch.empty((total_q, k), dtype=torch.float32, device=dev) if with_scores else None
+    ws_bytes = index_workspace_size(total_q, max_context, k)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().csa_index_topk(_stream(), batch, cu_q.data_ptr(), q_pos.data_ptr(), total_q, max_context,
+                              q_idx.data_ptr(), dtype_code(q_idx.dtype), heads, head_w.data_ptr(),
+                              _cref(idx_cache), k, topk.data_ptr(), _ptr(scores), workspace.data_ptr(),
+                              workspace.numel())
+    _check(st, "csa_index_topk")
+    return topk, scores
+
+
+def index_score(cu_q, q_pos, q_idx, head_w, idx_cache: PagedCache, k: int, max_context: int,
+                workspace: torch.Tensor) -> None:
+    """First half of index_topk: scores and chunk bounds into ``workspace``."""
+    batch, total_q, heads = _index_common(cu_q, q_pos, q_idx, head_w)
+    st = lib().csa_index_score(_stream(), batch, cu_q.data_ptr(), q_pos.data_ptr(), total_q, max_context,
+                               q_idx.data_ptr(), dtype_code(q_idx.dtype), heads, head_w.data_ptr(),
+                               _cref(idx_cache), k, workspace.data_ptr(), workspace.numel())
+    _check(st, "csa_index_score")
+
+
+def index_select(cu_q, q_pos, k: int, max_context: int, workspace: torch.Tensor,
+                 topk: torch.Tensor, scores: torch.Tensor | None = None) -> None:
+    """Second half of index_topk: exact selection from the scores in ``workspace``."""
+    _dev(topk, "topk", torch.int32, 2)
+    st = lib().csa_index_select(_stream(), cu_q.shape[0] - 1, cu_q.data_ptr(), q_pos.data_ptr(),
+                                q_pos.shape[0], max_context, k, topk.data_ptr(), _ptr(scores),
+                                workspace.data_ptr(), workspace.numel())
+    _check(st, "csa_index_select")
+
+
+def sparse_attn_workspace_size(total_q: int, n_heads: int, dim: int, ratio: int, has_topk: bool,
+                               k: int, max_context: int, window: int) -> int:
+    return lib().csa_sparse_attn_workspace_size(total_q, n_heads, dim, ratio, int(has_topk), k,
+                                                max_context, window)
+
+
+def sparse_attn_decode(cu_q, q_pos, q, kv: PagedCache, ratio: int, topk_idx, swa: PagedCache,
+                       window: int, softmax_scale: float, max_context: int, rope_base: float = 10000.0,
+                       rope_dims: int = 64, with_lse: bool = False, out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None):
+    """out [total_q, H, dim] float32 (inverse-RoPE'd) and optionally lse [total_q, H]."""
+    _dev(cu_q, "cu_q", torch.int32, 1)
+    _dev(q_pos, "q_pos", torch.int32, 1)
+    _dev(q, "q", (torch.bfloat16, torch.float32), 3)
+    total_q, heads, dim = q.shape
+    k = 0
+    if topk_idx is not None:
+        _dev(topk_idx, "topk_idx", torch.int32, 2)
+        if topk_idx.shape[0] != total_q:
+            raise ValueError("topk_idx must have one row per query")
+        k = topk_idx.shape[1]
+    if out is None:
+        out = torch.empty((total_q, heads, dim), dtype=torch.float32, device=q.device)
+    lse = torch.empty((total_q, heads), dtype=torch.float32, device=q.device) if with_lse else None
+    ws_bytes = sparse_attn_workspace_size(total_q, heads, dim, ratio, topk_idx is not None, k,
+                                          max_context, window)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib().csa_sparse_attn_decode(
+        _stream(), cu_q.shape[0] - 1, cu_q.data_ptr(), q_pos.data_ptr(), total_q, max_context,
+        q.data_ptr(), dtype_code(q.dtype), heads, _cref(kv), ratio, _ptr(topk_idx), k, _cref(swa),
+        window, softmax_scale, rope_base, rope_dims, out.data_ptr(), _ptr(lse), workspace.data_ptr(),
+        workspace.numel())
+    _check(st, "csa_sparse_attn_decode")
+    return out, lse

@@ -1,0 +1,186 @@
+// The C ABI of libcsa: argument validation, workspace sizing and launch.  Nothing here
+// allocates memory or synchronises the host.
+#include <algorithm>
+
+#include "csa.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxContextIndex = 8 * 1024 * 1024;  // select kernel: <= 1024 chunks of 2048 entries
+
+bool dtype_ok(int dt) { return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP8_E4M3; }
+
+// A cache descriptor with the given geometry (dim < 0: any dim).
+bool cache_ok(const csa_cache* c, int rows_per_block, int dim) {
+  if (!c || !c->rows || !c->block_table) return false;
+  if (!dtype_ok(c->dtype) || c->rows_per_block != rows_per_block) return false;
+  if (dim >= 0 && c->dim != dim) return false;
+  if (c->dim <= 0 || c->bt_stride <= 0 || c->num_blocks <= 0) return false;
+  if (c->dtype == CSA_FP8_E4M3 && !c->scales) return false;
+  return true;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_status_str(int status) {
+  switch (status) {
+    case CSA_OK: return "ok";
+    case CSA_EINVAL: return "invalid argument";
+    case CSA_ENOTSUP: return "unsupported dtype / dim / head combination";
+    case CSA_EWORKSPACE: return "workspace too small";
+    case CSA_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int64_t csa_num_entries(int ratio, int64_t num_tokens) {
+  if ((ratio != 4 && ratio != 128) || num_tokens < 0) return -1;
+  return num_tokens / ratio;
+}
+
+int csa_compress_insert(csa_stream_t stream, int ratio, int batch, const int32_t* ctx_lens,
+                        const int32_t* cu_new, int total_new, const void* new_raw, int raw_dtype,
+                        const int32_t* cu_entries, int total_entries, const float* gate_logits,
+                        const float* gamma, float eps, float rope_base, int rope_dims,
+                        const csa_cache* state, const csa_cache* out, const csa_cache* swa) {
+  if (ratio != 4 && ratio != 128) return CSA_EINVAL;
+  if (batch <= 0 || total_new < 0 || total_entries < 0) return CSA_EINVAL;
+  if (!ctx_lens || !cu_new || !cu_entries || !state || !out) return CSA_EINVAL;
+  if (total_new > 0 && !new_raw) return CSA_EINVAL;
+  if (total_entries > 0 && !gate_logits) return CSA_EINVAL;
+  if (raw_dtype != CSA_F32 && raw_dtype != CSA_BF16) return CSA_ENOTSUP;
+  if (!(eps >= 0.f) || !(rope_base > 0.f)) return CSA_EINVAL;
+  if (!cache_ok(state, 256, -1)) return CSA_EINVAL;
+  const int dim = state->dim;
+  if (state->dtype != raw_dtype) return CSA_EINVAL;
+  if (!cache_ok(out, 256 / ratio, dim)) return CSA_EINVAL;
+  if (swa && !cache_ok(swa, 256, dim)) return CSA_EINVAL;
+  if (dim < 2 || dim > 1024 || (dim & 1)) return CSA_ENOTSUP;
+  if (rope_dims < 2 || (rope_dims & 1) || rope_dims > dim || rope_dims > 128) return CSA_EINVAL;
+  if (total_new == 0 && total_entries == 0) return CSA_OK;
+  csa::CompressLaunch L{ratio, batch, ctx_lens, cu_new, total_new, new_raw, raw_dtype, cu_entries,
+                        total_entries, gate_logits, gamma, eps, rope_base, rope_dims, state, out,
+                        swa};
+  return hip_status(csa::launch_compress(L, (hipStream_t)stream));
+}
+
+size_t csa_index_workspace_size(int total_q, int max_context, int k) {
+  if (total_q <= 0 || max_context <= 0 || k <= 0) return 0;
+  return csa::index_workspace_bytes(total_q, max_context, k);
+}
+
+static int index_check(int batch, const int32_t* cu_q, const int32_t* q_pos, int total_q,
+                       int max_context, int k, size_t ws_bytes, const void* ws) {
+  if (batch <= 0 || total_q < 0 || !cu_q || !q_pos) return CSA_EINVAL;
+  if (max_context <= 0 || max_context > kMaxContextIndex) return CSA_EINVAL;
+  if (k <= 0 || k > 65536) return CSA_EINVAL;
+  if (total_q > 0 && (!ws || ws_bytes < csa::index_workspace_bytes(total_q, max_context, k)))
+    return CSA_EWORKSPACE;
+  return CSA_OK;
+}
+
+static int score_check(const void* q_idx, int q_dtype, int n_heads_idx, const float* head_w,
+                       const csa_cache* idx_cache) {
+  if (!q_idx || !head_w) return CSA_EINVAL;
+  if (!cache_ok(idx_cache, 64, 128)) return CSA_EINVAL;
+  if (q_dtype == CSA_BF16) {
+    if (n_heads_idx < 1 || n_heads_idx > 64) return CSA_ENOTSUP;
+    if (idx_cache->dtype == CSA_F32) return CSA_ENOTSUP;
+  } else if (q_dtype == CSA_F32) {
+    if (n_heads_idx < 1) return CSA_EINVAL;
+  } else {
+    return CSA_ENOTSUP;
+  }
+  return CSA_OK;
+}
+
+int csa_index_score(csa_stream_t stream, int batch, const int32_t* cu_q, const int32_t* q_pos,
+                    int total_q, int max_context, const void* q_idx, int q_dtype, int n_heads_idx,
+                    const float* head_w, const csa_cache* idx_cache, int k, void* workspace,
+                    size_t workspace_bytes) {
+  int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace);
+  if (st != CSA_OK) return st;
+  st = score_check(q_idx, q_dtype, n_heads_idx, head_w, idx_cache);
+  if (st != CSA_OK || total_q == 0) return st;
+  csa::IndexLaunch L{batch, cu_q, q_pos, total_q, max_context, q_idx, q_dtype, n_heads_idx,
+                     head_w, idx_cache, k};
+  const csa::IndexWorkspace ws = csa::index_workspace_carve(workspace, total_q, max_context, k);
+  return hip_status(csa::launch_index_score(L, ws, (hipStream_t)stream));
+}
+
+int csa_index_select(csa_stream_t stream, int batch, const int32_t* cu_q, const int32_t* q_pos,
+                     int total_q, int max_context, int k, int32_t* topk_idx, float* topk_score,
+                     void* workspace, size_t workspace_bytes) {
+  int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace);
+  if (st != CSA_OK) return st;
+  if (!topk_idx) return CSA_EINVAL;
+  if (total_q == 0) return CSA_OK;
+  csa::IndexLaunch L{batch, cu_q, q_pos, total_q, max_context, nullptr, 0, 0, nullptr, nullptr, k};
+  const csa::IndexWorkspace ws = csa::index_workspace_carve(workspace, total_q, max_context, k);
+  return hip_status(csa::launch_index_select(L, topk_idx, topk_score, ws, (hipStream_t)stream));
+}
+
+int csa_index_topk(csa_stream_t stream, int batch, const int32_t* cu_q, const int32_t* q_pos,
+                   int total_q, int max_context, const void* q_idx, int q_dtype, int n_heads_idx,
+                   const float* head_w, const csa_cache* idx_cache, int k, int32_t* topk_idx,
+                   float* topk_score, void* workspace, size_t workspace_bytes) {
+  int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace);
+  if (st != CSA_OK) return st;
+  st = score_check(q_idx, q_dtype, n_heads_idx, head_w, idx_cache);
+  if (st != CSA_OK) return st;
+  if (!topk_idx) return CSA_EINVAL;
+  if (total_q == 0) return CSA_OK;
+  csa::IndexLaunch L{batch, cu_q, q_pos, total_q, max_context, q_idx, q_dtype, n_heads_idx,
+                     head_w, idx_cache, k};
+  const csa::IndexWorkspace ws = csa::index_workspace_carve(workspace, total_q, max_context, k);
+  hipError_t e = csa::launch_index_score(L, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return CSA_EHIP;
+  return hip_status(csa::launch_index_select(L, topk_idx, topk_score, ws, (hipStream_t)stream));
+}
+
+size_t csa_sparse_attn_workspace_size(int total_q, int n_heads, int dim, int ratio, int has_topk,
+                                      int k, int max_context, int window) {
+  if (total_q <= 0 || n_heads <= 0 || dim <= 0 || (ratio != 4 && ratio != 128) || max_context <= 0 ||
+      window < 0)
+    return 0;
+  const csa::AttnPlan p = csa::attn_plan(total_q, n_heads, ratio, has_topk, k, max_context, window);
+  return csa::attn_workspace_bytes(total_q, n_heads, dim, p);
+}
+
+int csa_sparse_attn_decode(csa_stream_t stream, int batch, const int32_t* cu_q,
+                           const int32_t* q_pos, int total_q, int max_context, const void* q,
+                           int q_dtype, int n_heads, const csa_cache* kv, int ratio,
+                           const int32_t* topk_idx, int k, const csa_cache* swa, int window,
+                           float softmax_scale, float rope_base, int rope_dims, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes) {
+  if (ratio != 4 && ratio != 128) return CSA_EINVAL;
+  if (batch <= 0 || total_q < 0 || !cu_q || !q_pos || !q || !out) return CSA_EINVAL;
+  if (max_context <= 0 || window < 0 || window > 4096) return CSA_EINVAL;
+  if (topk_idx && (k <= 0 || k > 65536)) return CSA_EINVAL;
+  if (!cache_ok(kv, 256 / ratio, -1) || !cache_ok(swa, 256, kv->dim)) return CSA_EINVAL;
+  if (kv->dtype != swa->dtype) return CSA_ENOTSUP;
+  if (kv->dim != 576 && kv->dim != 512) return CSA_ENOTSUP;
+  if (q_dtype != CSA_BF16 && q_dtype != CSA_F32) return CSA_ENOTSUP;
+  if (n_heads < 1 || n_heads > 128) return CSA_ENOTSUP;
+  if (rope_dims != 64) return CSA_ENOTSUP;
+  if (!(rope_base > 0.f)) return CSA_EINVAL;
+  if (total_q == 0) return CSA_OK;
+  const int has_topk = topk_idx != nullptr;
+  const csa::AttnPlan p =
+      csa::attn_plan(total_q, n_heads, ratio, has_topk, has_topk ? k : 0, max_context, window);
+  if (!workspace || workspace_bytes < csa::attn_workspace_bytes(total_q, n_heads, kv->dim, p))
+    return CSA_EWORKSPACE;
+  csa::AttnLaunch L{batch, cu_q, q_pos, total_q, max_context, q, q_dtype, n_heads, kv, ratio,
+                    topk_idx, has_topk ? k : 0, swa, window, softmax_scale, rope_base, rope_dims,
+                    out, lse};
+  return hip_status(csa::launch_sparse_attn(L, p, workspace, (hipStream_t)stream));
+}
+
+}  // extern "C"

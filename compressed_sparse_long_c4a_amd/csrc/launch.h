@@ -1,0 +1,94 @@
+// Internal launch entry points behind the C ABI (arguments already validated by api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "csa.h"
+
+namespace csa {
+
+// ---------------------------------------------------------------- compress
+struct CompressLaunch {
+  int ratio, batch;
+  const int32_t* ctx_lens;
+  const int32_t* cu_new;
+  int total_new;
+  const void* new_raw;
+  int raw_dtype;
+  const int32_t* cu_entries;
+  int total_entries;
+  const float* logits;
+  const float* gamma;
+  float eps, rope_base;
+  int rope_dims;
+  const csa_cache* state;
+  const csa_cache* out;
+  const csa_cache* swa;
+};
+hipError_t launch_compress(const CompressLaunch& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- indexer
+// Entries handled by one workgroup of the score / filter kernels.
+constexpr int kIndexChunk = 2048;
+
+struct IndexWorkspace {
+  float* scores;       // [total_q][n_cap]
+  uint32_t* bounds;    // [total_q][chunks]   key lower bound of each full chunk
+  uint2* cand;         // [total_q][n_cap]    (key, entry) candidates, chunk-sparse
+  int32_t* cand_cnt;   // [total_q][chunks]
+  int chunks;          // per query
+  int64_t n_cap;       // chunks * kIndexChunk
+};
+size_t index_workspace_bytes(int total_q, int max_context, int k);
+IndexWorkspace index_workspace_carve(void* ws, int total_q, int max_context, int k);
+
+struct IndexLaunch {
+  int batch;
+  const int32_t* cu_q;
+  const int32_t* q_pos;
+  int total_q, max_context;
+  const void* q_idx;
+  int q_dtype, n_heads;
+  const float* head_w;
+  const csa_cache* idx_cache;
+  int k;
+};
+hipError_t launch_index_score(const IndexLaunch& a, const IndexWorkspace& ws, hipStream_t stream);
+hipError_t launch_index_select(const IndexLaunch& a, int32_t* topk_idx, float* topk_score,
+                               const IndexWorkspace& ws, hipStream_t stream);
+
+// ---------------------------------------------------------------- attention
+struct AttnPlan {
+  int splits;          // row splits per (query, head group)
+  int rows_per_split;  // multiple of 32
+  int head_groups;     // ceil(n_heads / 16)
+  int64_t max_rows;
+};
+AttnPlan attn_plan(int total_q, int n_heads, int ratio, int has_topk, int k, int max_context,
+                   int window);
+size_t attn_workspace_bytes(int total_q, int n_heads, int dim, const AttnPlan& p);
+
+struct AttnLaunch {
+  int batch;
+  const int32_t* cu_q;
+  const int32_t* q_pos;
+  int total_q, max_context;
+  const void* q;
+  int q_dtype, n_heads;
+  const csa_cache* kv;
+  int ratio;
+  const int32_t* topk_idx;
+  int k;
+  const csa_cache* swa;
+  int window;
+  float softmax_scale, rope_base;
+  int rope_dims;
+  float* out;
+  float* lse;
+};
+hipError_t launch_sparse_attn(const AttnLaunch& a, const AttnPlan& p, void* workspace,
+                              hipStream_t stream);
+
+}  // namespace csa

@@ -1,0 +1,233 @@
+/*
+ * csa.h -- one layer of compressed sparse attention decode on AMD Instinct
+ * MI355X (gfx950): compress -> index/top-k -> sparse K=V attention ->
+ * inverse RoPE.
+ *
+ * Sources (the method is defined by these pages; section names as printed):
+ *   [vLLM-V4]      "DeepSeek V4 in vLLM: Efficient Long-context Attention"
+ *                  (digest of the vLLM team's blog post): section 2 design
+ *                  principles; section 3 part 1 keeping the KV cache packed;
+ *                  section 3 part 2 keeping the GPU busy; appendix (why
+ *                  inverse RoPE, exact position ranges and causality, exact
+ *                  k values, why the short window).
+ *   [SGLang-pools] "SGLang KV Cache storage pool architecture": section 3
+ *                  (the 576 = 512 + 64 MLA row shared by K and V) and
+ *                  section 4 (the 132-byte fp8 indexer row).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked "host".  All memory is owned
+ *     by the caller; the library never allocates and never frees.  Scratch
+ *     memory is the caller's `workspace`, sized by the *_workspace_size
+ *     queries.  A `csa_cache` descriptor itself lives in host memory.
+ *   - Every call is asynchronous on `stream` and never synchronises the
+ *     host; buffers must stay alive until the stream has passed the call.
+ *   - Host-visible arguments are validated before anything is launched; on a
+ *     non-zero status nothing was launched.  CSA_EHIP reports a failed launch
+ *     (hipGetLastError after launching).  No C++ exception crosses the ABI.
+ *   - Device-side contents (lengths, positions, block-table entries, top-k
+ *     ids) are trusted: values outside the documented ranges are undefined
+ *     behaviour, except where a call states how it treats them.
+ *   - The functions keep no state between calls and may be called from
+ *     several threads on different streams.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+/* A hipStream_t (struct ihipStream_t*); NULL is the null stream. */
+typedef struct ihipStream_t* csa_stream_t;
+
+/* Element types of stored rows and of query inputs. */
+typedef enum {
+  CSA_F32 = 0,       /* IEEE float32 */
+  CSA_BF16 = 1,      /* bfloat16 */
+  CSA_FP8_E4M3 = 2   /* OCP E4M3 ("e4m3fn") codes with one float32 scale per row */
+} csa_dtype;
+
+/* Status codes. */
+enum {
+  CSA_OK = 0,
+  CSA_EINVAL = -1,      /* a required pointer is NULL or a size/argument is out of range */
+  CSA_ENOTSUP = -2,     /* a combination of dtype / dim / heads this build does not implement */
+  CSA_EWORKSPACE = -3,  /* workspace smaller than the matching *_workspace_size() */
+  CSA_EHIP = -4         /* the HIP runtime reported an error while launching */
+};
+
+/*
+ * One paged cache ([vLLM-V4] section 3 part 1: every compressed layer uses a
+ * logical block of 256 native positions).  Logical row r of sequence b --
+ * an entry index for compressed caches, a raw token position for window and
+ * compressor-state caches -- lives in physical block
+ * block_table[b * bt_stride + r / rows_per_block] at slot r % rows_per_block.
+ * rows_per_block is therefore 64 for a c4a cache (256 / 4 entries), 2 for a
+ * c128a cache (256 / 128) and 256 for window and state caches.
+ *
+ * Row layout: `dim` contiguous elements.  Main KV rows are the shared key and
+ * value, 512 latent dimensions followed by the 64 RoPE dimensions
+ * ([SGLang-pools] section 3); indexer rows are 128 dimensions.  FP8 rows keep
+ * their float32 scales in a separate [num_blocks][rows_per_block] array
+ * (value = code * scale; 128 codes + 4 scale bytes = the 132-byte indexer row
+ * of [SGLang-pools] section 4).  Scales must be positive.
+ */
+typedef struct csa_cache {
+  void*          rows;            /* [num_blocks][rows_per_block][dim] elements of `dtype` (fp8: uint8 codes) */
+  float*         scales;          /* [num_blocks][rows_per_block] float32 for CSA_FP8_E4M3, else NULL */
+  int32_t        dtype;           /* csa_dtype */
+  int32_t        dim;             /* elements per row */
+  int32_t        rows_per_block;  /* 64 (c4a), 2 (c128a) or 256 (window, state) */
+  int32_t        num_blocks;      /* physical blocks in `rows` */
+  const int32_t* block_table;     /* [batch][bt_stride] physical block ids, each in [0, num_blocks) */
+  int32_t        bt_stride;       /* logical blocks per sequence in block_table */
+} csa_cache;
+
+/* CSA_ABI_VERSION of the loaded library. */
+int csa_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* csa_status_str(int status);
+
+/*
+ * Host helper: compressed entries after `num_tokens` raw tokens, floor(num_tokens / ratio)
+ * ([vLLM-V4] appendix, exact position ranges: entry i of c4a ends at 4i + 3,
+ * of c128a at 128i + 127).  Returns -1 if ratio is not 4 or 128 or num_tokens < 0.
+ */
+int64_t csa_num_entries(int ratio, int64_t num_tokens);
+
+/*
+ * csa_compress_insert -- the fused compressor ([vLLM-V4] section 3 part 2,
+ * first fusion: compress + RMSNorm + RoPE + cache insert; one instance per
+ * head dimension, main KV d = 576 or indexer d = 128).
+ *
+ * ratio 4 (c4a) or 128 (c128a); coff = 2 or 1; window W = coff * ratio raw rows
+ * (8 or 128).  Sequence b held ctx_lens[b] raw tokens before the call and
+ * receives new_raw rows [cu_new[b], cu_new[b+1]) at positions ctx_lens[b], ...
+ * For every entry j completed by the call (its anchor a_j = ratio*j + ratio - 1
+ * is one of the new positions; the call's entries for b are
+ * j = n(ctx_lens[b]) .. n(ctx_lens[b] + new_b) - 1, in that order):
+ *   x_r = raw row at position s_j + r, r in [0, W), s_j = ratio*j - (coff-1)*ratio,
+ *         0 for negative positions ([vLLM-V4] appendix, exact position ranges);
+ *   w   = softmax(gate_logits[cu_entries[b] + (j - n(ctx_lens[b]))][0..W));
+ *   y   = sum_r w_r x_r;  n = y / sqrt(mean(y^2) + eps) * gamma  (whole row);
+ *   c   = RoPE_{a_j}(n): the last rope_dims dimensions rotated in consecutive
+ *         pairs (2i, 2i+1) by a_j * rope_base^(-2i/rope_dims) (angles in float64);
+ *   out row j = c rounded to out->dtype (fp8: scale = amax/448, codes RNE).
+ * Raw rows at positions below ctx_lens[b] are read from `state` (which must hold
+ * the last W positions); the new rows among the last W positions after the call
+ * are written to `state` (the rolling residual registered as sliding-window KV,
+ * [vLLM-V4] section 3 part 1).  If `swa` is not NULL, every new row x_p is also
+ * written there as RoPE_p(x_p) in swa->dtype (the uncompressed window rows).
+ *
+ * Arguments:
+ *   ctx_lens   [batch] int32, >= 0.        cu_new [batch+1] int32, cu_new[0] = 0,
+ *   total_new  = cu_new[batch] (host).     new_raw [total_new][dim] of raw_dtype (F32 or BF16).
+ *   cu_entries [batch+1] int32 prefix sums of the per-sequence entry counts above;
+ *   total_entries = cu_entries[batch] (host).  gate_logits [total_entries][W] float32.
+ *   gamma [dim] float32 or NULL (= 1).  eps >= 0.  rope_base > 0.  rope_dims even,
+ *   2..min(dim, 128).  state: rows_per_block 256, dtype = raw_dtype, same dim.
+ *   out: rows_per_block 256 / ratio, dim = state dim, any dtype.  swa: NULL or
+ *   rows_per_block 256, same dim, any dtype.  dim <= 1024.
+ * Cache rows must not alias new_raw; out, state and swa must be distinct memory.
+ */
+int csa_compress_insert(csa_stream_t stream, int ratio, int batch,
+                        const int32_t* ctx_lens, const int32_t* cu_new, int total_new,
+                        const void* new_raw, int raw_dtype,
+                        const int32_t* cu_entries, int total_entries, const float* gate_logits,
+                        const float* gamma, float eps, float rope_base, int rope_dims,
+                        const csa_cache* state, const csa_cache* out, const csa_cache* swa);
+
+/*
+ * csa_index_topk -- indexer score and top-k over c4a entries ([vLLM-V4]
+ * section 2: DeepSeek Sparse Attention, the query attends to the top-k
+ * compressed tokens; appendix: causality 4j + 3 <= t and default k).
+ *
+ * Query i (of sequence b, cu_q[b] <= i < cu_q[b+1]) sits at position
+ * t = q_pos[i]; its candidates are the c4a entries j < n(t + 1) (those with
+ * anchor 4j + 3 <= t), capped at n(max_context).  Its score for entry j is
+ *     s_j = sum_h head_w[i][h] * max(0, q_idx[i][h] . k_j)
+ * with k_j the stored indexer key (fp8 code * scale).  The k' = min(k, n)
+ * best are written to topk_idx[i][0..k') in ascending entry order; the rest
+ * of the row is -1.  Among exactly equal scores lower entry ids win.
+ * topk_score (optional) receives the matching float32 scores (0 for padding).
+ *
+ *   cu_q [batch+1], q_pos [total_q] int32 (0 <= t < max_context).
+ *   q_idx [total_q][n_heads_idx][128] of q_dtype: CSA_BF16 (1 <= n_heads_idx <= 64)
+ *         or CSA_F32 (any n_heads_idx >= 1).
+ *   head_w [total_q][n_heads_idx] float32.
+ *   idx_cache: dim 128, rows_per_block 64, dtype FP8_E4M3 or BF16 (any dtype
+ *         with CSA_F32 queries).
+ *   1 <= k <= 65536.  topk_idx [total_q][k] int32.  topk_score [total_q][k] or NULL.
+ *   workspace of at least csa_index_workspace_size(total_q, max_context, k) bytes.
+ */
+size_t csa_index_workspace_size(int total_q, int max_context, int k);
+
+int csa_index_topk(csa_stream_t stream, int batch, const int32_t* cu_q, const int32_t* q_pos,
+                   int total_q, int max_context, const void* q_idx, int q_dtype, int n_heads_idx,
+                   const float* head_w, const csa_cache* idx_cache, int k,
+                   int32_t* topk_idx, float* topk_score, void* workspace, size_t workspace_bytes);
+
+/*
+ * The two halves of csa_index_topk, for callers that schedule or time them
+ * separately.  csa_index_score writes every candidate's score (and per-chunk
+ * selection bounds) into `workspace`; csa_index_select reads them back and
+ * writes topk_idx / topk_score.  Called back to back on one stream with the
+ * same arguments and workspace they are exactly csa_index_topk.
+ */
+int csa_index_score(csa_stream_t stream, int batch, const int32_t* cu_q, const int32_t* q_pos,
+                    int total_q, int max_context, const void* q_idx, int q_dtype, int n_heads_idx,
+                    const float* head_w, const csa_cache* idx_cache, int k,
+                    void* workspace, size_t workspace_bytes);
+
+int csa_index_select(csa_stream_t stream, int batch, const int32_t* cu_q, const int32_t* q_pos,
+                     int total_q, int max_context, int k, int32_t* topk_idx, float* topk_score,
+                     void* workspace, size_t workspace_bytes);
+
+/*
+ * csa_sparse_attn_decode -- multi-query attention with K = V over the selected
+ * compressed entries plus the uncompressed sliding window, then inverse RoPE
+ * ([vLLM-V4] section 2: shared K/V, top-k sparse attention, window of 128;
+ * appendix: Output = Attention(Q, K, V) R_t^{-1}; c128a attends to all of its
+ * entries, framed as top-k 8192; window rows [t-127, t]).
+ *
+ * For query i at position t = q_pos[i] of sequence b the row set is
+ *   { kv row j : j in topk_idx[i][0..k), 0 <= j < n_t }   (n_t = n(t + 1) for `ratio`;
+ *                                                          ids outside are padding, skipped)
+ *   or, when topk_idx is NULL, { kv row j : 0 <= j < min(n_t, n(max_context)) };
+ *   plus { swa row p : max(0, t - window + 1) <= p <= t }.
+ * Each row serves as key and value.  For every head h:
+ *   z_r = softmax_scale * q[i][h] . row_r;  o = sum_r softmax(z)_r row_r  (full dim);
+ *   out[i][h] = o with its last rope_dims dimensions rotated by -t (R_t^{-1});
+ *   lse[i][h] = log(sum_r exp(z_r)) (natural log; -inf and out = 0 if no rows).
+ * List entries should be distinct (a repeated id is attended twice).
+ *
+ *   q [total_q][n_heads][dim] of q_dtype (CSA_BF16 or CSA_F32), already rotated.
+ *   kv: rows_per_block 256 / ratio; swa: rows_per_block 256; both with the same
+ *       dim (512 or 576) and the same dtype (F32, BF16 or FP8_E4M3).  rope_dims = 64.
+ *   1 <= n_heads <= 128.  topk_idx [total_q][k] int32 or NULL (then k is ignored).
+ *   0 <= window <= 4096.  out [total_q][n_heads][dim] float32.  lse [total_q][n_heads] or NULL.
+ *   workspace of at least csa_sparse_attn_workspace_size(...) bytes with the same
+ *   total_q, n_heads, dim, ratio, topk_idx != NULL, k, max_context and window.
+ */
+size_t csa_sparse_attn_workspace_size(int total_q, int n_heads, int dim, int ratio, int has_topk,
+                                      int k, int max_context, int window);
+
+int csa_sparse_attn_decode(csa_stream_t stream, int batch, const int32_t* cu_q,
+                           const int32_t* q_pos, int total_q, int max_context,
+                           const void* q, int q_dtype, int n_heads,
+                           const csa_cache* kv, int ratio, const int32_t* topk_idx, int k,
+                           const csa_cache* swa, int window, float softmax_scale,
+                           float rope_base, int rope_dims, float* out, float* lse,
+                           void* workspace, size_t workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

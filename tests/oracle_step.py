@@ -1,0 +1,165 @@
+"""Run the CPU oracle on one step's generator inputs, and compare GPU results with it.
+
+Test infrastructure: imports only ``oracle`` and the generator's CPU tensors.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import attention, compress, formats, geometry, indexer
+from oracle.paged import PagedCache
+
+DT = {torch.float32: "f32", torch.bfloat16: "bf16", torch.uint8: "fp8"}
+
+
+def np_rows(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def oracle_cache(triple) -> PagedCache:
+    rows, scales, bt = triple
+    return PagedCache(np_rows(rows), DT[rows.dtype], bt.numpy().copy(),
+                      None if scales is None else scales.numpy().copy())
+
+
+def raw_values(t: torch.Tensor) -> tuple[np.ndarray, str]:
+    return np_rows(t), DT[t.dtype]
+
+
+def run_oracle(cfg, d: dict, queries=None, topk_override=None) -> dict:
+    """The step on the oracle.  ``queries``: indices of the queries to evaluate (default all)."""
+    res: dict = {}
+    kv, swa = oracle_cache(d["kv"]), oracle_cache(d["swa"])
+    state = oracle_cache(d["state"])
+    idx = oracle_cache(d["idx"]) if "idx" in d else None
+    gamma = None if d.get("gamma") is None else d["gamma"].numpy().astype(np.float64)
+    if "compress" in cfg.stages:
+        raw, rdt = raw_values(d["new_raw"])
+        ent, win = compress.compress_insert(
+            cfg.ratio, d["ctx_lens"].tolist(), d["cu_new"].tolist(), raw, rdt, d["cu_entries"].tolist(),
+            d["logits"].numpy(), gamma, cfg.eps, cfg.rope_base, 64, state, kv, swa)
+        res["entries"], res["window_rows"] = ent, win
+    if "compress_idx" in cfg.stages:
+        raw, rdt = raw_values(d["new_idx_raw"])
+        idx_state = oracle_cache(d["idx_state"])
+        ent, _ = compress.compress_insert(
+            4, d["ctx_lens"].tolist(), d["cu_new"].tolist(), raw, rdt, d["cu_entries"].tolist(),
+            d["idx_logits"].numpy(), None, cfg.eps, cfg.rope_base, 64, idx_state, idx, None)
+        res["idx_entries"] = ent
+        res["idx_state"] = idx_state
+    res["kv"], res["swa"], res["state"], res["idx"] = kv, swa, state, idx
+
+    cu_q = d["cu_q"].tolist()
+    q_pos = d["q_pos"].tolist()
+    total_q = len(q_pos)
+    qsel = list(range(total_q)) if queries is None else list(queries)
+    seq = np.searchsorted(np.array(cu_q), np.arange(total_q), side="right") - 1
+    q = formats.decode_stored(np_rows(d["q"]), DT[d["q"].dtype])
+    res["queries"] = qsel
+    res["topk"], res["scores"], res["out"], res["lse"] = {}, {}, {}, {}
+    if "index" in cfg.stages:
+        q_idx = formats.decode_stored(np_rows(d["q_idx"]), DT[d["q_idx"].dtype])
+        w = d["head_w"].numpy().astype(np.float64)
+        for i in qsel:
+            s = indexer.query_scores(idx, int(seq[i]), q_pos[i], q_idx[i], w[i])
+            res["scores"][i] = s
+            res["topk"][i] = indexer.topk(s, cfg.k)
+    for i in qsel:
+        if "attn" not in cfg.stages:
+            break
+        if topk_override is not None:
+            ids = topk_override[i]
+        elif "index" in cfg.stages:
+            ids = res["topk"][i]
+        else:
+            ids = None if "topk" not in d else d["topk"][i].numpy()
+        b, t = int(seq[i]), q_pos[i]
+        rows = attention.gather_rows(kv, swa, b, t, cfg.ratio, ids, cfg.window)
+        o, l = attention.attend(q[i], rows, cfg.softmax_scale)
+        from oracle.rope import inverse_rope
+        res["out"][i] = inverse_rope(o, t, cfg.rope_base, 64)
+        res["lse"][i] = l
+    return res
+
+
+# ------------------------------------------------------------------ comparisons
+
+def half_ulp_bf16(c: np.ndarray) -> np.ndarray:
+    a = np.maximum(np.abs(c), 2.0 ** -126)
+    e = np.floor(np.log2(a))
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
+def half_ulp_fp8(c: np.ndarray) -> np.ndarray:
+    a = np.maximum(np.abs(c), 2.0 ** -6)
+    e = np.floor(np.log2(a))
+    return np.ldexp(1.0, (e - 4).astype(np.int64))
+
+
+def check_rounded_row(gpu_vals: np.ndarray, exact: np.ndarray, fmt: str, gpu_scale=None, ref_scale=None):
+    """A stored row is acceptable if every element is a rounding of a value within delta of the
+    exact one: |stored - exact| <= half an ulp of exact + delta, where
+    delta = 1e-5 |exact| + 1e-6 max|row| is the float32 accuracy of the fused kernel (errors of
+    float32 arithmetic scale with the row's magnitude, not with an element that cancels to
+    nearly zero).  fp8 rows are compared in code units; their scales must agree to 1e-6."""
+    if fmt == "fp8":
+        assert gpu_scale is not None and ref_scale is not None
+        ok_s = abs(float(gpu_scale) - float(ref_scale)) <= 1e-6 * abs(float(ref_scale))
+        vals = gpu_vals / float(gpu_scale)
+        c = exact / float(ref_scale)
+        half = half_ulp_fp8(c)
+    else:
+        ok_s = True
+        vals, c = gpu_vals, exact
+        half = half_ulp_bf16(c) if fmt == "bf16" else np.zeros_like(c)
+    delta = 1e-5 * np.abs(c) + 1e-6 * float(np.max(np.abs(c)))
+    err = np.abs(vals - c)
+    tol = half + delta + 1e-30
+    return bool(ok_s and np.all(err <= tol)), float(np.max(err / tol))
+
+
+def topk_acceptable(gpu_ids: np.ndarray, scores: np.ndarray, k: int, rel: float = 1e-5):
+    """R11: |G| = k', every id scoring above tau(1+rel) is in G, every id in G scores >= tau(1-rel).
+    Also checks the output form: ascending ids, no duplicates, -1 padding."""
+    n = len(scores)
+    kk = min(k, n)
+    g = gpu_ids[gpu_ids >= 0]
+    if len(g) != kk or np.any(gpu_ids[kk:] != -1) or np.any(gpu_ids[:kk] < 0):
+        return False, "size/padding"
+    if len(np.unique(g)) != kk or np.any(np.diff(g) <= 0):
+        return False, "not strictly ascending"
+    if np.any(g >= n):
+        return False, "non-causal id"
+    if kk == 0:
+        return True, "empty"
+    tau = np.sort(scores)[::-1][kk - 1]
+    band = rel * max(abs(float(tau)), 1e-30)
+    must = np.nonzero(scores > tau + band)[0]
+    if not np.all(np.isin(must, g)):
+        return False, "missing a clear winner"
+    if np.any(scores[g] < tau - band):
+        return False, "contains a clear loser"
+    return True, "ok"
+
+
+def allclose_out(gpu: np.ndarray, ref: np.ndarray, atol: float = 1e-5, rtol: float = 2e-3):
+    err = np.abs(gpu - ref)
+    tol = atol + rtol * np.abs(ref)
+    return bool(np.all(err <= tol)), float(np.max(err / tol))
+
+
+def decode_gpu_rows(rows: torch.Tensor, scales, blocks_slots):
+    """Stored values of the given (block, slot) rows of a GPU cache copied to CPU."""
+    r = rows.cpu()
+    dt = DT[r.dtype]
+    blk, slot = blocks_slots
+    vals = np_rows(r[blk, slot])
+    sc = None if scales is None else scales.cpu().numpy()[blk, slot]
+    return formats.decode_stored(vals, dt, sc if dt == "fp8" else None), sc
+
+
+__all__ = ["run_oracle", "check_rounded_row", "topk_acceptable", "allclose_out", "geometry"]

@@ -1,0 +1,97 @@
+"""The C ABI on the CPU: the library loads, exports every function include/csa.h declares,
+and rejects bad host-visible arguments before launching anything (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import compressed_sparse_long_c4a_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from compressed_sparse_long_c4a_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree(csa):
+    assert set(declared_functions()) == set(csa.EXPORTED)
+
+
+def test_exports_every_declared_symbol(csa):
+    L = ctypes.CDLL(csa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_host_helpers(csa):
+    L = csa.lib()
+    assert L.csa_abi_version() == 1
+    assert L.csa_num_entries(4, 1 << 20) == 262144
+    assert L.csa_num_entries(128, 1 << 20) == 8192
+    assert L.csa_num_entries(4, 1023) == 255
+    assert L.csa_num_entries(5, 10) == -1
+    assert csa.status_str(csa.EINVAL) == "invalid argument"
+    assert L.csa_index_workspace_size(0, 100, 4) == 0
+    assert L.csa_index_workspace_size(4, 1 << 20, 2048) > 4 * 262144 * 12
+    assert L.csa_sparse_attn_workspace_size(4, 128, 576, 4, 1, 2048, 1 << 20, 128) > 0
+
+
+def test_validation_rejects_before_launch(csa):
+    L = csa.lib()
+    c = csa._CCache(1, None, csa.BF16, 576, 64, 10, 1, 8)     # fake (never dereferenced) pointers
+    st = csa._CCache(1, None, csa.BF16, 576, 256, 10, 1, 8)
+    P = ctypes.pointer
+    # bad ratio
+    assert L.csa_compress_insert(None, 5, 1, 1, 1, 1, 1, csa.BF16, 1, 1, 1, None, 1e-6, 1e4, 64,
+                                 P(st), P(c), None) == csa.EINVAL
+    # state dtype must equal the raw dtype
+    assert L.csa_compress_insert(None, 4, 1, 1, 1, 1, 1, csa.F32, 1, 1, 1, None, 1e-6, 1e4, 64,
+                                 P(st), P(c), None) == csa.EINVAL
+    # fp8 cache without scales
+    c8 = csa._CCache(1, None, csa.FP8_E4M3, 576, 64, 10, 1, 8)
+    assert L.csa_compress_insert(None, 4, 1, 1, 1, 1, 1, csa.BF16, 1, 1, 1, None, 1e-6, 1e4, 64,
+                                 P(st), P(c8), None) == csa.EINVAL
+    # odd rope dims
+    assert L.csa_compress_insert(None, 4, 1, 1, 1, 1, 1, csa.BF16, 1, 1, 1, None, 1e-6, 1e4, 63,
+                                 P(st), P(c), None) == csa.EINVAL
+    # index: workspace too small, k out of range, unsupported heads
+    ic = csa._CCache(1, 1, csa.FP8_E4M3, 128, 64, 10, 1, 8)
+    assert L.csa_index_topk(None, 1, 1, 1, 1, 1024, 1, csa.BF16, 64, 1, P(ic), 8, 1, None, 1, 16) \
+        == csa.EWORKSPACE
+    assert L.csa_index_topk(None, 1, 1, 1, 1, 1024, 1, csa.BF16, 64, 1, P(ic), 0, 1, None, 1, 1 << 40) \
+        == csa.EINVAL
+    assert L.csa_index_topk(None, 1, 1, 1, 1, 1024, 1, csa.BF16, 65, 1, P(ic), 8, 1, None, 1, 1 << 40) \
+        == csa.ENOTSUP
+    # attention: dim, heads, rope dims, dtype mismatch
+    kv = csa._CCache(1, None, csa.BF16, 576, 64, 10, 1, 8)
+    sw = csa._CCache(1, None, csa.BF16, 576, 256, 10, 1, 8)
+    args = [None, 1, 1, 1, 1, 1024, 1, csa.BF16, 64, P(kv), 4, 1, 16, P(sw), 128, 0.04, 1e4, 64, 1,
+            None, 1, 1 << 40]
+    # (the unmodified argument list is valid and is never passed: it would launch)
+    bad = list(args)
+    bad[8] = 129
+    assert L.csa_sparse_attn_decode(*bad) == csa.ENOTSUP
+    bad = list(args)
+    bad[17] = 32
+    assert L.csa_sparse_attn_decode(*bad) == csa.ENOTSUP
+    sw8 = csa._CCache(1, 1, csa.FP8_E4M3, 576, 256, 10, 1, 8)
+    bad = list(args)
+    bad[13] = P(sw8)
+    assert L.csa_sparse_attn_decode(*bad) == csa.ENOTSUP
+    bad = list(args)
+    bad[21] = 8
+    assert L.csa_sparse_attn_decode(*bad) == csa.EWORKSPACE

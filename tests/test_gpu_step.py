@@ -1,0 +1,27 @@
+"""Whole-step parity on the GPU: the HIP library against the oracle on reduced workloads.
+
+Each case runs every stage of its workload (compress, index/top-k, attention) through the C
+ABI on identical seeded inputs and applies the acceptance rules of tests/pipeline_check.py.
+"""
+
+import pytest
+
+from tests import pipeline_check as P
+from workloads import configs as C
+
+CASES = {
+    "ref_c4a_fp32": C.REF,
+    "c4a_fp8_decode": P.SMALL_DECODE,
+    "c4a_bf16_decode": C.scaled(C.C4A_128K_B32, (20480, 12288, 8191, 4102), k=512),
+    "c128a_bf16_decode": C.scaled(C.C128A_1M_B8, (16384, 8192, 19456 - 1000, 300), gamma=True),
+    "c4a_bf16_prefill": C.scaled(C.C4A_PREFILL_64K, (2048 + 512,), new_tokens=512, q_per_seq=512, k=128),
+}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", list(CASES))
+def test_step_parity(gpu, name):
+    cfg = CASES[name]
+    print(f"case {name}: {cfg}", flush=True)
+    rep = P.run_step_parity(cfg, verbose=True)
+    assert not rep["fail"], rep["fail"][:10]

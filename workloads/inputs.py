@@ -1,0 +1,78 @@
+"""Input recipe of one step of a workload (CPU tensors), built only from seeded draws.
+
+Array sizes follow the workload descriptions: a c4a entry has 8 compression logits and a
+c128a entry 128; the sequence holds floor(L / ratio) compressed entries after L raw tokens;
+window and compressor-state caches are backed only around the positions a step can touch.
+Values are synthetic draws (see gen.py); rows the step itself writes are drawn too and are
+overwritten by the step.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from .configs import StepConfig
+from .gen import Gen, paged_rows
+
+LOGITS_PER_ENTRY = {4: 8, 128: 128}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def draw(cfg: StepConfig) -> dict:
+    g = Gen(cfg.seed)
+    B, R, D = cfg.batch, cfg.ratio, cfg.dim
+    Wc = LOGITS_PER_ENTRY[R]
+    L1 = list(cfg.ctx_after)
+    L0 = [l - cfg.new_tokens for l in L1]
+    assert min(L0) >= 0
+    n0 = [l // R for l in L0]
+    n1 = [l // R for l in L1]
+    e = [b - a for a, b in zip(n0, n1)]
+    d: dict = {"L0": L0, "L1": L1}
+    d["ctx_lens"] = torch.tensor(L0, dtype=torch.int32)
+    d["cu_new"] = torch.arange(B + 1, dtype=torch.int32) * cfg.new_tokens
+    d["cu_entries"] = torch.tensor([0] + list(torch.tensor(e).cumsum(0).tolist()), dtype=torch.int32)
+    raw_t = TORCH_DTYPE[cfg.raw_dtype]
+    d["new_raw"] = g.normal("new_raw", (B * cfg.new_tokens, D), raw_t)
+    d["logits"] = g.normal("logits", (sum(e), Wc))
+    d["gamma"] = g.uniform("gamma", (D,), 0.5, 1.5) if cfg.gamma else None
+
+    maxL = max(L1)
+    kv = paged_rows(g, "kv", B, 256 // R, D, cfg.kv_dtype, max(n1), [(0, n) for n in n1])
+    swa = paged_rows(g, "swa", B, 256, D, cfg.kv_dtype, maxL,
+                     [(max(0, a - cfg.window), b) for a, b in zip(L0, L1)])
+    state = paged_rows(g, "state", B, 256, D, cfg.raw_dtype, maxL,
+                       [(max(0, a - Wc), b) for a, b in zip(L0, L1)])
+    d["kv"], d["swa"], d["state"] = kv, swa, state
+
+    q_first = [b - cfg.q_per_seq for b in L1]
+    d["q_pos"] = torch.tensor([q + i for q in q_first for i in range(cfg.q_per_seq)], dtype=torch.int32)
+    d["cu_q"] = torch.arange(B + 1, dtype=torch.int32) * cfg.q_per_seq
+    total_q = B * cfg.q_per_seq
+    d["q"] = g.normal("q", (total_q, cfg.n_heads, D), TORCH_DTYPE[cfg.q_dtype])
+
+    if cfg.has_indexer:
+        d["idx"] = paged_rows(g, "idx", B, 64, 128, cfg.idx_dtype, max(n1), [(0, n) for n in n1])
+        d["q_idx"] = g.normal("q_idx", (total_q, cfg.idx_heads, 128), TORCH_DTYPE[cfg.idx_q_dtype])
+        d["head_w"] = g.uniform("head_w", (total_q, cfg.idx_heads))
+        if "compress_idx" in cfg.stages:
+            d["new_idx_raw"] = g.normal("new_idx_raw", (B * cfg.new_tokens, 128), raw_t)
+            d["idx_logits"] = g.normal("idx_logits", (sum(e), Wc))
+            d["idx_state"] = paged_rows(g, "idx_state", B, 256, 128, cfg.raw_dtype, maxL,
+                                        [(max(0, a - Wc), b) for a, b in zip(L0, L1)])
+    return d
+
+
+def random_topk(cfg: StepConfig, d: dict, fill: float = 1.0, seed_name: str = "topk") -> torch.Tensor:
+    """A synthetic top-k list per query: distinct ids below each query's causal limit, in random
+    order, with the tail padded by -1 (``fill`` = fraction of the k slots used)."""
+    g = Gen(cfg.seed)
+    rows = []
+    for i, t in enumerate(d["q_pos"].tolist()):
+        limit = (t + 1) // cfg.ratio
+        cnt = min(limit, int(cfg.k * fill))
+        ids = g.distinct_ints(f"{seed_name}.{i}", cnt, max(limit, 1)) if cnt else torch.zeros(0, dtype=torch.int32)
+        row = torch.full((cfg.k,), -1, dtype=torch.int32)
+        row[:cnt] = ids
+        rows.append(row)
+    return torch.stack(rows)
