@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark one layer's compressed sparse attention decode step on one MI355X.
+
+Workload (default): c4a decode at 1M context, batch 4, sequences at the four compression
+boundary residues (contexts 2^20 - {0,1,2,3}), fp8 E4M3 main KV with a per-token float32
+scale, fp8 indexer keys (64 heads x 128), 128 query heads of 576, top-k 2048, window 128.
+A step is the whole hot path: compress the new token (main KV + window row, and indexer
+key), index scores + exact top-k, sparse K=V attention + inverse RoPE.  Inputs are resident
+in HBM before timing; steps rotate over several copies of the caches so that repeated steps
+cannot be served from the 256 MB Infinity Cache.
+
+Prints one JSON line.  --gpus N > 1 is not supported (one GPU only).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "c4a sparse decode query-tokens/s and achieved HBM GB/s at 1M context"
+HBM_PEAK_GBS = 8000.0
+INDEX_ROW_BYTES = 132          # 128 fp8 codes + one float32 scale
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "index_score_mfma_c4a_1m_b4_counters.txt")
+INDEX_SRC = os.path.join(ROOT, "compressed_sparse_long_c4a_amd", "csrc", "index.hip")
+
+
+def row_bytes(dtype: str, dim: int) -> int:
+    return {"f32": 4 * dim, "bf16": 2 * dim, "fp8": dim + 4}[dtype]
+
+
+def algorithmic_bytes(cfg, d) -> dict:
+    """Bytes the method must move in one step (no scratch, no re-reads), per stage."""
+    B, H, D, W = cfg.batch, cfg.n_heads, cfg.dim, cfg.window
+    total_q = d["q_pos"].shape[0]
+    qpos = d["q_pos"].tolist()
+    n_vis = [(t + 1) // cfg.ratio for t in qpos]
+    kvrow = row_bytes(cfg.kv_dtype, D)
+    rawb = 2 if cfg.raw_dtype == "bf16" else 4
+    Wc = 8 if cfg.ratio == 4 else 128
+    e = int(d["cu_entries"][-1])
+    new = int(d["cu_new"][-1])
+    out = {}
+    if "compress" in cfg.stages:
+        out["compress"] = (e * (Wc * D * rawb + Wc * 4 + kvrow)          # window rows, logits, entry
+                           + new * (D * rawb + kvrow + D * rawb))          # raw row, window row, state row
+    if "compress_idx" in cfg.stages:
+        out["compress_idx"] = e * (Wc * 128 * rawb + Wc * 4 + INDEX_ROW_BYTES) + new * 2 * 128 * rawb
+    if "index" in cfg.stages:
+        qb = 2 if cfg.idx_q_dtype == "bf16" else 4
+        out["index_score"] = sum(n_vis) * INDEX_ROW_BYTES + total_q * cfg.idx_heads * (128 * qb + 4)
+        out["index_select"] = total_q * cfg.k * 4
+    if "attn" in cfg.stages:
+        rows = sum((min(cfg.k, n) if "index" in cfg.stages else n) + min(W, t + 1) for n, t in zip(n_vis, qpos))
+        qb = 2 if cfg.q_dtype == "bf16" else 4
+        out["attn"] = rows * kvrow + total_q * H * (D * qb + D * 4 + 4)
+    return out
+
+
+def counters_traffic():
+    """HBM bytes per index-score launch from the committed rocprofv3 counter summary, or None
+    when there is none or it was taken from a different version of the kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    for line in open(COUNTERS_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src_hash = hashlib.sha1(open(INDEX_SRC, "rb").read()).hexdigest()
+    if kv.get("source_sha1") != src_hash:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def clone_caches(g: dict) -> dict:
+    from compressed_sparse_long_c4a_amd import PagedCache
+    from compressed_sparse_long_c4a_amd.pipeline import CACHE_KEYS
+    r = dict(g)
+    for k in CACHE_KEYS:
+        if k in g:
+            c = g[k]
+            r[k] = PagedCache(c.rows.clone(), c.block_table.clone(), None if c.scales is None else c.scales.clone())
+    return r
+
+
+def cpu_baseline(cfg, d) -> dict:
+    from threadpoolctl import threadpool_info
+    from tests import oracle_step as O
+    caches = O.prepare(d)
+    t0 = time.perf_counter()
+    O.run_oracle(cfg, d, caches=caches)
+    dt = time.perf_counter() - t0
+    total_q = d["q_pos"].shape[0]
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": total_q / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole step of the same workload ({total_q} queries: compress, index "
+                      f"scores and top-k, attention, inverse RoPE) on the float64 oracle, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--config", default=None, help="workload name (default: the 1M c4a fp8 decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the sharded path is a design, not part of this build)", file=sys.stderr)
+        return 2
+
+    import torch
+    from compressed_sparse_long_c4a_amd import pipeline
+    from workloads import configs, inputs
+
+    cfg = configs.HEADLINE
+    if args.config:
+        cfg = {c.name: c for c in configs.CONFIGS}[args.config]
+    torch.cuda.set_device(0)
+    print(f"# drawing inputs for {cfg.name}", file=sys.stderr, flush=True)
+    d = inputs.draw(cfg)
+    g0 = pipeline.to_device(d)
+    reps = [g0] + [clone_caches(g0) for _ in range(max(1, args.replicas) - 1)]
+    step = pipeline.Step(cfg, g0, with_scores=False)
+    torch.cuda.synchronize()
+    print("# inputs resident; warming up", file=sys.stderr, flush=True)
+
+    K, Wm = args.steps, args.warmup
+    for i in range(Wm):
+        step.run(reps[i % len(reps)], with_lse=False)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    has_index = "index" in cfg.stages
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        g = reps[i % len(reps)]
+        if "compress" in cfg.stages:
+            step.compress(g)
+        if "compress_idx" in cfg.stages:
+            step.compress_idx(g)
+        if has_index:
+            ev[i][0].record()
+            step.index_score(g)
+            ev[i][1].record()
+            step.index_select(g)
+        step.attn(g, with_lse=False)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    score_ms = statistics.mean(a.elapsed_time(b) for a, b in ev) if has_index else None
+    print(f"# timed {K} steps: {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # per-stage breakdown (separate pass, events around every stage)
+    stages = {}
+    names = [s for s in ("compress", "compress_idx", "index_score", "index_select", "attn")
+             if (s in cfg.stages) or (s.startswith("index") and has_index)]
+    evs = {s: [] for s in names}
+    for i in range(min(K, 100)):
+        g = reps[i % len(reps)]
+        for s in names:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            getattr(step, s)(g) if s != "attn" else step.attn(g, with_lse=False)
+            b.record()
+            evs[s].append((a, b))
+    torch.cuda.synchronize()
+    for s in names:
+        stages[s] = round(statistics.median(a.elapsed_time(b) for a, b in evs[s]) * 1e3, 2)
+
+    # the same step captured in a HIP graph (one step per cache replica), replayed
+    graph_ms = None
+    if not args.no_graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for g in reps:
+                    step.run(g, with_lse=False)
+            torch.cuda.current_stream().wait_stream(s)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for g in reps:
+                    step.run(g, with_lse=False)
+            graph.replay()
+            torch.cuda.synchronize()
+            reps_n = max(1, K // len(reps))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps_n):
+                graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            graph_ms = a.elapsed_time(b) / (reps_n * len(reps))
+        except Exception as exc:  # graph capture is reported, never required
+            print(f"# graph variant unavailable: {exc}", file=sys.stderr)
+
+    ab = algorithmic_bytes(cfg, d)
+    step_bytes = sum(ab.values())
+    total_q = d["q_pos"].shape[0]
+    value = total_q / (ms_step / 1e3)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "hbm_gbs": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
+        "hbm_frac": round(step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": step_bytes,
+        "stages_us": stages,
+        "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 5),
+        "config": {
+            "workload": cfg.name, "ratio": cfg.ratio, "batch": cfg.batch,
+            "context": list(cfg.ctx_after), "new_tokens": cfg.new_tokens,
+            "queries_per_seq": cfg.q_per_seq, "heads": cfg.n_heads, "dim": cfg.dim,
+            "kv_dtype": cfg.kv_dtype, "indexer": f"{cfg.idx_heads}x128 {cfg.idx_dtype}" if has_index else None,
+            "top_k": cfg.k if has_index else None, "window": cfg.window,
+            "cache_replicas": len(reps), "arithmetic": "fp8/bf16 operands on bf16 MFMA, fp32 accumulate",
+        },
+    }
+    if has_index:
+        achieved = ab["index_score"] / (score_ms / 1e3) / 1e9
+        result["roofline"] = {
+            "kernel": "index_score_mfma", "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": counters_traffic(), "launch_us": round(score_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": ab["index_score"],
+        }
+    if not args.no_cpu_baseline:
+        print("# timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, d)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -10,6 +10,7 @@ import torch
 
 from oracle import attention, compress, formats, geometry, indexer
 from oracle.paged import PagedCache
+from oracle.rope import inverse_rope
 
 DT = {torch.float32: "f32", torch.bfloat16: "bf16", torch.uint8: "fp8"}
 
@@ -30,12 +31,19 @@ def raw_values(t: torch.Tensor) -> tuple[np.ndarray, str]:
     return np_rows(t), DT[t.dtype]
 
 
-def run_oracle(cfg, d: dict, queries=None, topk_override=None) -> dict:
-    """The step on the oracle.  ``queries``: indices of the queries to evaluate (default all)."""
+def prepare(d: dict) -> dict:
+    """Oracle copies of the step's caches (input preparation, not part of the step)."""
+    c = {name: oracle_cache(d[name]) for name in ("kv", "swa", "state", "idx", "idx_state") if name in d}
+    return c
+
+
+def run_oracle(cfg, d: dict, queries=None, topk_override=None, caches: dict | None = None) -> dict:
+    """The step on the oracle.  ``queries``: indices of the queries to evaluate (default all).
+    ``caches``: the result of prepare(d) (made here when not given); they are updated in place."""
     res: dict = {}
-    kv, swa = oracle_cache(d["kv"]), oracle_cache(d["swa"])
-    state = oracle_cache(d["state"])
-    idx = oracle_cache(d["idx"]) if "idx" in d else None
+    caches = prepare(d) if caches is None else caches
+    kv, swa, state = caches["kv"], caches["swa"], caches["state"]
+    idx = caches.get("idx")
     gamma = None if d.get("gamma") is None else d["gamma"].numpy().astype(np.float64)
     if "compress" in cfg.stages:
         raw, rdt = raw_values(d["new_raw"])
@@ -45,7 +53,7 @@ def run_oracle(cfg, d: dict, queries=None, topk_override=None) -> dict:
         res["entries"], res["window_rows"] = ent, win
     if "compress_idx" in cfg.stages:
         raw, rdt = raw_values(d["new_idx_raw"])
-        idx_state = oracle_cache(d["idx_state"])
+        idx_state = caches["idx_state"]
         ent, _ = compress.compress_insert(
             4, d["ctx_lens"].tolist(), d["cu_new"].tolist(), raw, rdt, d["cu_entries"].tolist(),
             d["idx_logits"].numpy(), None, cfg.eps, cfg.rope_base, 64, idx_state, idx, None)
@@ -80,7 +88,6 @@ def run_oracle(cfg, d: dict, queries=None, topk_override=None) -> dict:
         b, t = int(seq[i]), q_pos[i]
         rows = attention.gather_rows(kv, swa, b, t, cfg.ratio, ids, cfg.window)
         o, l = attention.attend(q[i], rows, cfg.softmax_scale)
-        from oracle.rope import inverse_rope
         res["out"][i] = inverse_rope(o, t, cfg.rope_base, 64)
         res["lse"][i] = l
     return res
