@@ -117,6 +117,10 @@ def main() -> int:
     ap.add_argument("--config", default=None, help="workload name (default: the 1M c4a fp8 decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--two-stream", action="store_true",
+                    help="also time the schedule with the main-KV compress on a second stream")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 256 MiB device-to-device copy (a reference for byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -139,6 +143,13 @@ def main() -> int:
     torch.cuda.synchronize()
     print("# inputs resident; warming up", file=sys.stderr, flush=True)
 
+    if args.calibrate_copy:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     K, Wm = args.steps, args.warmup
     for i in range(Wm):
         step.run(reps[i % len(reps)], with_lse=False)
@@ -147,25 +158,28 @@ def main() -> int:
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     has_index = "index" in cfg.stages
+    for g in reps:                       # marshal the C calls of every replica once
+        step.fast(g)
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
-        g = reps[i % len(reps)]
-        if "compress" in cfg.stages:
-            step.compress(g)
-        if "compress_idx" in cfg.stages:
-            step.compress_idx(g)
-        if has_index:
-            ev[i][0].record()
-            step.index_score(g)
-            ev[i][1].record()
-            step.index_select(g)
-        step.attn(g, with_lse=False)
+        step.fast(reps[i % len(reps)], ev[i] if has_index else None)
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
     score_ms = statistics.mean(a.elapsed_time(b) for a, b in ev) if has_index else None
     print(f"# timed {K} steps: {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # the pages' two-stream schedule (main-KV compress beside the indexer), for comparison
+    ms_two = None
+    if args.two_stream and has_index and "compress" in cfg.stages:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(K):
+            step.run_overlapped(reps[i % len(reps)], with_lse=False)
+        b.record()
+        torch.cuda.synchronize()
+        ms_two = a.elapsed_time(b) / K
 
     # per-stage breakdown (separate pass, events around every stage)
     stages = {}
@@ -190,14 +204,15 @@ def main() -> int:
         try:
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
+            run = lambda g, with_lse: step.fast(g)
             with torch.cuda.stream(s):
                 for g in reps:
-                    step.run(g, with_lse=False)
+                    run(g, with_lse=False)
             torch.cuda.current_stream().wait_stream(s)
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
                 for g in reps:
-                    step.run(g, with_lse=False)
+                    run(g, with_lse=False)
             graph.replay()
             torch.cuda.synchronize()
             reps_n = max(1, K // len(reps))
@@ -233,6 +248,7 @@ def main() -> int:
         "algorithmic_bytes_per_step": step_bytes,
         "stages_us": stages,
         "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 5),
+        "ms_per_step_two_stream": None if ms_two is None else round(ms_two, 5),
         "config": {
             "workload": cfg.name, "ratio": cfg.ratio, "batch": cfg.batch,
             "context": list(cfg.ctx_after), "new_tokens": cfg.new_tokens,

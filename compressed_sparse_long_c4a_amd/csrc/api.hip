@@ -151,6 +151,7 @@ size_t csa_sparse_attn_workspace_size(int total_q, int n_heads, int dim, int rat
       window < 0)
     return 0;
   const csa::AttnPlan p = csa::attn_plan(total_q, n_heads, ratio, has_topk, k, max_context, window);
+  if (p.max_rows > csa::kAttnMaxRows) return 0;
   return csa::attn_workspace_bytes(total_q, n_heads, dim, p);
 }
 
@@ -175,6 +176,7 @@ int csa_sparse_attn_decode(csa_stream_t stream, int batch, const int32_t* cu_q,
   const int has_topk = topk_idx != nullptr;
   const csa::AttnPlan p =
       csa::attn_plan(total_q, n_heads, ratio, has_topk, has_topk ? k : 0, max_context, window);
+  if (p.max_rows > csa::kAttnMaxRows) return CSA_ENOTSUP;
   if (!workspace || workspace_bytes < csa::attn_workspace_bytes(total_q, n_heads, kv->dim, p))
     return CSA_EWORKSPACE;
   csa::AttnLaunch L{batch, cu_q, q_pos, total_q, max_context, q, q_dtype, n_heads, kv, ratio,

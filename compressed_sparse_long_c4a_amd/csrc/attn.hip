@@ -6,14 +6,17 @@
 // inverse RoPE: with v_n = k_n = R_n k the output must be multiplied by R_m^{-1}, leaving
 // R_{n-m}.  [vLLM-V4] appendix, exact k values: c128a attends to every entry (top-k = 8192).
 //
-// Kernel 1 (attn_partial), grid (row split, 16-head group, query), 4 waves:
-//   every wave owns the 16 heads of its group and walks its own 32-row blocks of the split
-//   (blocks w, w+4, ...), keeping a private online softmax and output; the four waves are
-//   merged through LDS at the end and one partial (m, l, O) per head leaves the workgroup.
+// Kernel 1 (attn_partial), grid (row split, 16-head group, query), 4 waves = 2 pairs:
+//   the addresses (and fp8 scales) of the split's rows are resolved once into LDS; each pair
+//   of waves walks its own 32-row blocks (blocks p, p+2, ...) with a private online softmax,
+//   and the two waves of a pair split the row dimensions in halves: each computes the partial
+//   logits over its half, the halves are summed through LDS (one barrier per block, double
+//   buffered), and each wave accumulates the output for its half of the dims.  The two pairs
+//   are merged through LDS at the end; one partial (m, l, O) per head leaves the workgroup.
 //   Per 32-row block (two 16-row tiles T0, T1):
 //     QK : S^T[16 rows x 16 heads] = R_T . Q^T on MFMA 16x16x32 bf16.  Lane (r, g) holds row
-//          r of the tile, 8 dims per k-step, loaded straight from HBM (no LDS): the row
-//          gather and the MFMA operand layout coincide.
+//          r of the tile, 8 dims per k-step, loaded straight from HBM: the row gather and the
+//          MFMA operand layout coincide.
 //     PV : O^T[dims x heads] += R^T . P^T.  The transposed operand R^T is produced on the
 //          matrix cores by a "selection" MFMA, R_T . Sel_h with Sel_h a 0/1 matrix picking 16
 //          of the 32 dims of a k-step: its output layout (4 rows x 1 dim per lane) is exactly
@@ -22,9 +25,11 @@
 //          into bf16 hi + lo parts (two MFMAs) so PV keeps ~16 significant bits.
 //   fp8 rows (code * per-row scale): codes widen exactly to bf16; the scale multiplies the
 //   logit and P.  float32 rows / queries are split hi + lo as well.
-// Kernel 2 (attn_merge), grid (16-head group, query): combines the splits by their softmax
-//   statistics, normalises, applies R_t^{-1} to the last rope_dims dims (angles in float64)
-//   and writes out / lse.
+// Kernel 2 (attn_merge), grid (4-head group, query), one wave per head: combines the splits
+//   by their softmax statistics, normalises, applies R_t^{-1} to the last rope_dims dims
+//   (angles formed and reduced in float64) and writes out / lse.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -34,6 +39,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSplits = 256;
+constexpr int kRowsPerSplit = 1024;  // most rows a workgroup handles (addresses staged in LDS)
 
 struct Args {
   int batch, n_heads, ratio, k, has_topk, window, n_max, rows_per_split, splits, hgp;
@@ -47,13 +53,6 @@ struct Args {
   float* part_ml;   // [total_q][splits][hgp][2]  (m in log2 units, l)
 };
 
-// Dimension held in slot j of lane group g at k-step ks.
-template <int DT>
-__device__ __forceinline__ int dim_of_slot(int ks, int g, int j) {
-  if (DT == CSA_FP8_E4M3) return 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) + j;
-  return 32 * ks + 8 * g + j;
-}
-
 __device__ __forceinline__ bf16x8 f32x8_to_bf16(const float* x) {
   bf16x8 r;
 #pragma unroll
@@ -61,51 +60,39 @@ __device__ __forceinline__ bf16x8 f32x8_to_bf16(const float* x) {
   return r;
 }
 
-// One 16-row tile as seen by lane (r, g): row r's slots for every k-step.
-template <int DT, int DIM>
-struct Tile {
-  static constexpr int NKS = DIM / 32;
-  static constexpr int NREG = DT == CSA_FP8_E4M3 ? NKS / 2 : (DT == CSA_BF16 ? NKS : 1);
-  uint4 d[NREG];
+
+// Half a row (HKS k-steps of 32 dims) of one 16-row tile as seen by lane (r, g): the 8 dims
+// 32 ks + 8 g .. +7 of row r for each of its k-steps.
+template <int DT, int HKS>
+struct HalfTile {
+  static constexpr int NREG = DT == CSA_FP8_E4M3 ? HKS : (DT == CSA_BF16 ? HKS : 1);
+  typedef typename std::conditional<DT == CSA_FP8_E4M3, uint2, uint4>::type Word;
+  Word d[NREG];
   const float* f32row;  // float32 rows are re-read per k-step instead of held in registers
 
-  __device__ __forceinline__ void load(const void* rows, int64_t prow, bool valid, int g) {
-    if (DT == CSA_F32) {
-      f32row = valid ? (const float*)rows + prow * DIM : nullptr;
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) d[i] = make_uint4(0, 0, 0, 0);
-    if (!valid) return;
-    if (DT == CSA_FP8_E4M3) {
-      const uint8_t* base = (const uint8_t*)rows + prow * DIM + 16 * g;
-#pragma unroll
-      for (int kp = 0; kp < NREG; ++kp) d[kp] = *(const uint4*)(base + 64 * kp);
+  // `row` is always a loadable row (padding rows point at a safe row and are masked later).
+  __device__ __forceinline__ void load(const char* row, int ks0, int g) {
+    if constexpr (DT == CSA_F32) {
+      f32row = (const float*)row + 32 * ks0 + 8 * g;
     } else {
-      const uint16_t* base = (const uint16_t*)rows + prow * DIM + 8 * g;
+      constexpr int ESZ = DT == CSA_BF16 ? 2 : 1;
+      const char* base = row + (32 * ks0 + 8 * g) * ESZ;
 #pragma unroll
-      for (int ks = 0; ks < NREG; ++ks) d[ks] = *(const uint4*)(base + 32 * ks);
+      for (int kk = 0; kk < HKS; ++kk) d[kk] = *(const Word*)(base + 32 * kk * ESZ);
     }
   }
 
-  // bf16 operand for k-step ks (exact for bf16 and fp8 rows); lo = residual for float32 rows.
-  __device__ __forceinline__ void frag(int ks, int g, bf16x8& hi, bf16x8& lo) const {
-    if (DT == CSA_BF16) {
-      hi = __builtin_bit_cast(bf16x8, d[ks]);
-    } else if (DT == CSA_FP8_E4M3) {
-      const uint4 v = d[ks >> 1];
-      const uint32_t w0 = (ks & 1) ? v.z : v.x, w1 = (ks & 1) ? v.w : v.y;
-      float x[8];
-      fp8x2_to_f32<false>(w0, x[0], x[1]);
-      fp8x2_to_f32<true>(w0, x[2], x[3]);
-      fp8x2_to_f32<false>(w1, x[4], x[5]);
-      fp8x2_to_f32<true>(w1, x[6], x[7]);
-      hi = f32x8_to_bf16(x);
+  // bf16 operand for local k-step kk (exact for bf16 and fp8 rows); lo = residual of float32 rows.
+  __device__ __forceinline__ void frag(int kk, bf16x8& hi, bf16x8& lo) const {
+    if constexpr (DT == CSA_BF16) {
+      hi = __builtin_bit_cast(bf16x8, d[kk]);
+    } else if constexpr (DT == CSA_FP8_E4M3) {
+      hi = fp8x8_to_bf16x8(d[kk].x, d[kk].y);
     } else {
-      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (f32row) {
-        const float4 a = *(const float4*)(f32row + 32 * ks + 8 * g);
-        const float4 b = *(const float4*)(f32row + 32 * ks + 8 * g + 4);
+      float x[8];
+      {
+        const float4 a = *(const float4*)(f32row + 32 * kk);
+        const float4 b = *(const float4*)(f32row + 32 * kk + 4);
         x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
         x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
       }
@@ -119,37 +106,54 @@ struct Tile {
 };
 
 template <int DT, int QDT, int DIM>
-__global__ __launch_bounds__(256, 1) void attn_partial(Args a) {
+__global__ __launch_bounds__(256) void attn_partial(Args a) {
   constexpr int NKS = DIM / 32;
+  constexpr int HKS = NKS / 2;  // k-steps per wave of a pair
   constexpr bool ROW_LO = DT == CSA_F32;
   constexpr bool Q_LO = QDT == CSA_F32;
-  __shared__ float o_sh[16][DIM + 4];
-  __shared__ float m_sh[4][16], l_sh[4][16];
+  // byte offset of each row from the main cache's row base (window rows included), so every
+  // row address is derived from a kernel argument and the loads are known to be global
+  __shared__ int64_t off_sh[kRowsPerSplit];
+  __shared__ float scale_sh[kRowsPerSplit];  // row scale (1 for bf16/f32 rows); 0 marks padding
+  __shared__ float xs[2][4][64][8];  // partial logits, [buffer][wave][lane][T*4 + jj]
+  // bf16 / fp8 rows: each wave's bf16 half-rows of the current block (row stride padded by 16 B),
+  // read back transposed for PV; the merge at the end reuses the space.  float32 rows use the
+  // selection MFMA instead and need only the merge buffer.
+  constexpr int TROW = (DIM / 2) * 2 + 16;          // bytes per half-row in LDS
+  constexpr int TILE_BYTES = ROW_LO ? 0 : 4 * 32 * TROW;
+  constexpr int MERGE_BYTES = 16 * (DIM + 4) * 4;
+  __shared__ __attribute__((aligned(16))) char tile_sh[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
+  float (*o_sh)[DIM + 4] = reinterpret_cast<float (*)[DIM + 4]>(tile_sh);
+  __shared__ float ml_sh[2][16][2];
 
   const int s = blockIdx.x, hg = blockIdx.y, qi = blockIdx.z;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int pair = wv >> 1, half = wv & 1;
   const int ln = lane & 15, lg = lane >> 4;
-  const int b = seq_of(a.cu_q, a.batch, qi);
+  const int b = seq_of_wave(a.cu_q, a.batch, qi);
   const int t = a.q_pos[qi];
   const int n_vis = min((t + 1) / a.ratio, a.n_max);
   const int n_c = a.has_topk ? a.k : n_vis;
   const int n_w = min(a.window, t + 1);
   const int n_rows = n_c + n_w;
   const int r_begin = s * a.rows_per_split;
-  const int r_end = min(r_begin + a.rows_per_split, n_rows);
+  // a query without any visible row (no window and no entry yet) attends to nothing
+  const int nrows = (n_w > 0 || n_vis > 0) ? max(0, min(a.rows_per_split, n_rows - r_begin)) : 0;
   const int H = a.n_heads;
+  const int ks0 = half * HKS;
+  constexpr int ESZ = DT == CSA_F32 ? 4 : (DT == CSA_BF16 ? 2 : 1);
 
-  // Q^T as the B operand: lane (head ln, group lg) holds q[h][dim_of_slot(ks, lg, 0..7)].
-  bf16x8 qb[NKS], qb_lo[Q_LO ? NKS : 1];
+  // Q^T as the B operand: lane (head ln, group lg) holds q[h][32 ks + 8 lg + 0..7].
+  bf16x8 qb[HKS], qb_lo[Q_LO ? HKS : 1];
   {
     const int h = 16 * hg + ln;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int d0 = dim_of_slot<DT>(ks, lg, 0);
-      if (QDT == CSA_BF16) {
+    for (int kk = 0; kk < HKS; ++kk) {
+      const int d0 = 32 * (ks0 + kk) + 8 * lg;
+      if constexpr (QDT == CSA_BF16) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (h < H) v = *(const uint4*)((const uint16_t*)a.q + ((int64_t)qi * H + h) * DIM + d0);
-        qb[ks] = __builtin_bit_cast(bf16x8, v);
+        qb[kk] = __builtin_bit_cast(bf16x8, v);
       } else {
         float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (h < H) {
@@ -157,15 +161,58 @@ __global__ __launch_bounds__(256, 1) void attn_partial(Args a) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) x[i] = src[i];
         }
-        qb[ks] = f32x8_to_bf16(x);
+        qb[kk] = f32x8_to_bf16(x);
         float r[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r[i] = x[i] - (float)qb[ks][i];
-        if constexpr (Q_LO) qb_lo[ks] = f32x8_to_bf16(r);
+        for (int i = 0; i < 8; ++i) r[i] = x[i] - (float)qb[kk][i];
+        if constexpr (Q_LO) qb_lo[kk] = f32x8_to_bf16(r);
       }
     }
   }
-  // Sel_h as the B operand: slot (lg, j) -> output column 8 (lg - 2h) + j for lg in {2h, 2h+1}.
+  // ---- resolve the split's rows once: address and scale, padding rows -> a safe row.
+  // Each thread owns up to kRowsPerSplit / 256 rows; the list reads, then the block-table
+  // reads, then the scale reads of all its rows are issued together.
+  if (nrows > 0) {  // (all staged positions are then rows of this query)
+    constexpr int RPT = kRowsPerSplit / 256;
+    const int64_t swa_off = (int64_t)((uintptr_t)a.swa.rows - (uintptr_t)a.kv.rows);
+    const int64_t safe = n_w > 0 ? swa_off + phys_row(a.swa, b, t) * (DIM * ESZ)
+                                 : phys_row(a.kv, b, max(n_vis - 1, 0)) * (DIM * ESZ);
+    int ent[RPT];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int i = tid + 256 * u;
+      const int pos = r_begin + min(i, nrows - 1);
+      ent[u] = pos < n_c ? (a.has_topk ? a.topk[(int64_t)qi * a.k + pos] : pos) : -1;
+    }
+    int64_t prow[RPT];
+    bool is_kv[RPT], ok[RPT];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int i = tid + 256 * u;
+      const int pos = r_begin + min(i, nrows - 1);
+      is_kv[u] = pos < n_c;
+      ok[u] = i < nrows && (!is_kv[u] || (ent[u] >= 0 && ent[u] < n_vis));
+      prow[u] = is_kv[u] ? (ok[u] ? phys_row(a.kv, b, ent[u]) : 0)
+                         : phys_row(a.swa, b, t - n_w + 1 + (pos - n_c));
+    }
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int i = tid + 256 * u;
+      if (i < nrows) {
+        const int64_t base = is_kv[u] ? 0 : swa_off;
+        float sc = 0.f;
+        if (ok[u]) {
+          if constexpr (DT == CSA_FP8_E4M3) sc = (is_kv[u] ? a.kv.scales : a.swa.scales)[prow[u]];
+          else sc = 1.0f;
+        }
+        off_sh[i] = ok[u] ? base + prow[u] * (DIM * ESZ) : safe;
+        scale_sh[i] = sc;
+      }
+    }
+  }
+
+  // Sel_h as the B operand (float32 rows only): slot (lg, j) -> output column 8 (lg - 2h) + j
+  // for lg in {2h, 2h+1}.
   bf16x8 sel[2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
@@ -174,76 +221,69 @@ __global__ __launch_bounds__(256, 1) void attn_partial(Args a) {
       sel[hh][j] = (__bf16)((lg == 2 * hh + (ln >> 3) && j == (ln & 7)) ? 1.0f : 0.0f);
   }
 
-  f32x4 o[NKS][2];
+  f32x4 o[HKS][2];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    o[ks][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    o[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < HKS; ++kk) {
+    o[kk][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    o[kk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float m_run = -INFINITY, l_run = 0.f;
+  __syncthreads();
 
-  for (int row0 = r_begin + 32 * wv; row0 < r_end; row0 += 128) {
-    // ---- gather: lane (ln, lg) loads row ln of tile T0 (rows row0..+15) and T1 (+16..+31)
-    Tile<DT, DIM> tile[2];
-    float rscale[2];
-    int rvalid[2];
+  const int nblocks = (nrows + 31) >> 5;
+  const int iters = (nblocks + 1) >> 1;
+  // Row loads are unconditional (clamped to the split's last row, which is always loadable):
+  // the wait counters then keep the next block in flight while this one is computed.
+  auto load_block = [&](int it, HalfTile<DT, HKS>* tl) {
+    const int bi = 2 * min(it, iters - 1) + pair;
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const int pos = row0 + 16 * T + ln;
-      bool valid = false;
-      const DevCache* c = &a.kv;
-      int64_t prow = 0;
-      if (pos < r_end) {
-        if (pos < n_c) {
-          const int j = a.has_topk ? a.topk[(int64_t)qi * a.k + pos] : pos;
-          if (j >= 0 && j < n_vis) {
-            valid = true;
-            prow = phys_row(a.kv, b, j);
-          }
-        } else {
-          const int p = t - n_w + 1 + (pos - n_c);
-          valid = true;
-          c = &a.swa;
-          prow = phys_row(a.swa, b, p);
-        }
-      }
-      tile[T].load(c->rows, prow, valid, lg);
-      rscale[T] = valid ? (DT == CSA_FP8_E4M3 ? c->scales[prow] : 1.0f) : 0.f;
-      rvalid[T] = valid;
-    }
+    for (int T = 0; T < 2; ++T)
+      tl[T].load((const char*)a.kv.rows + off_sh[min(32 * bi + 16 * T + ln, nrows - 1)], ks0, lg);
+  };
 
-    // ---- S^T = R . Q^T
+  auto process_block = [&](int it, const HalfTile<DT, HKS>* tile, int buf) {
+    const int bi = 2 * it + pair;
+    const bool active = bi < nblocks;
+    const int row0 = 32 * bi;
+    // partial S^T = R_half . Q_half^T
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    for (int kk = 0; kk < HKS; ++kk) {
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         bf16x8 rh, rl;
-        tile[T].frag(ks, lg, rh, rl);
-        sacc[T] = mfma16x16x32(rh, qb[ks], sacc[T]);
-        if constexpr (Q_LO) sacc[T] = mfma16x16x32(rh, qb_lo[ks], sacc[T]);
-        if constexpr (ROW_LO) sacc[T] = mfma16x16x32(rl, qb[ks], sacc[T]);
+        tile[T].frag(kk, rh, rl);
+        if constexpr (!ROW_LO)
+          *(bf16x8*)(tile_sh + wv * 32 * TROW + (16 * T + ln) * TROW + 2 * (32 * kk + 8 * lg)) = rh;
+        sacc[T] = mfma16x16x32(rh, qb[kk], sacc[T]);
+        if constexpr (Q_LO) sacc[T] = mfma16x16x32(rh, qb_lo[kk], sacc[T]);
+        if constexpr (ROW_LO) sacc[T] = mfma16x16x32(rl, qb[kk], sacc[T]);
       }
     }
-
-    // ---- online softmax; lane (head ln, lg) holds rows 4 lg + jj of T0 and T1
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) xs[buf][wv][lane][4 * T + jj] = sacc[T][jj];
+    barrier_lds();  // the next block's row loads stay in flight
     float z[2][4], sc[2][4];
     float mloc = -INFINITY;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int src = 4 * lg + jj;
-        const int v = __shfl(rvalid[T], src, kWave);
-        sc[T][jj] = __shfl(rscale[T], src, kWave);
-        z[T][jj] = v ? sacc[T][jj] * sc[T][jj] * a.sm_scale2 : -INFINITY;
+        const float sum = xs[buf][2 * pair][lane][4 * T + jj] + xs[buf][2 * pair + 1][lane][4 * T + jj];
+        const int r = row0 + 16 * T + 4 * lg + jj;
+        const float rs = (active && r < nrows) ? scale_sh[r] : 0.f;
+        sc[T][jj] = rs;
+        z[T][jj] = rs != 0.f ? sum * rs * a.sm_scale2 : -INFINITY;
         mloc = fmaxf(mloc, z[T][jj]);
       }
     }
+    if (!active) return;
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
     const float m_new = fmaxf(m_run, mloc);
-    if (m_new == -INFINITY) continue;  // every row so far is padding (uniform per head)
+    if (m_new == -INFINITY) return;  // every row so far is padding (uniform per wave)
     const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
     m_run = m_new;
     float pv[8];
@@ -258,10 +298,12 @@ __global__ __launch_bounds__(256, 1) void attn_partial(Args a) {
       }
     }
     l_run = l_run * alpha + psum;
+    if (__ballot(alpha != 1.0f)) {  // rescale only when some head's running max moved
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      o[ks][0] *= alpha;
-      o[ks][1] *= alpha;
+      for (int kk = 0; kk < HKS; ++kk) {
+        o[kk][0] *= alpha;
+        o[kk][1] *= alpha;
+      }
     }
     bf16x8 p_hi = f32x8_to_bf16(pv), p_lo;
     {
@@ -270,65 +312,93 @@ __global__ __launch_bounds__(256, 1) void attn_partial(Args a) {
       for (int i = 0; i < 8; ++i) r[i] = pv[i] - (float)p_hi[i];
       p_lo = f32x8_to_bf16(r);
     }
-
-    // ---- O^T += R^T . P^T, R^T made by the selection MFMA
+    if constexpr (!ROW_LO) {
+      // O^T += R^T . P^T over this wave's half of the dims.  The A operand (16 dims x 8 rows per
+      // lane) is read transposed from the wave's LDS tile: two ds_read_b64_tr_b16 per fragment,
+      // the first over rows 4 lg .. 4 lg + 3 of T0 and the second over the same rows of T1,
+      // which is the row order of P^T in the softmax registers.
+      __attribute__((address_space(3))) char* tbase =
+          (__attribute__((address_space(3))) char*)(tile_sh + wv * 32 * TROW);
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 r0h, r0l, r1h, r1l;
-      tile[0].frag(ks, lg, r0h, r0l);
-      tile[1].frag(ks, lg, r1h, r1l);
+      for (int kk = 0; kk < HKS; ++kk) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 c0 = mfma16x16x32(r0h, sel[hh], zero);
-        const f32x4 c1 = mfma16x16x32(r1h, sel[hh], zero);
-        bf16x8 at;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          at[jj] = (__bf16)c0[jj];
-          at[4 + jj] = (__bf16)c1[jj];
+        for (int hh = 0; hh < 2; ++hh) {
+          const int col = 2 * (32 * kk + 16 * hh + 4 * (ln & 3));
+          const int r0 = 4 * lg + (ln >> 2);
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(tbase + r0 * TROW + col));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(tbase + (16 + r0) * TROW + col));
+          const bf16x8 at = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[kk][hh] = mfma16x16x32(at, p_hi, o[kk][hh]);
+          o[kk][hh] = mfma16x16x32(at, p_lo, o[kk][hh]);
         }
-        o[ks][hh] = mfma16x16x32(at, p_hi, o[ks][hh]);
-        o[ks][hh] = mfma16x16x32(at, p_lo, o[ks][hh]);
-        if constexpr (ROW_LO) {
+      }
+    } else {
+      // float32 rows: R^T made by the selection MFMA from the register tiles (hi and lo parts)
+#pragma unroll
+      for (int kk = 0; kk < HKS; ++kk) {
+        bf16x8 r0h, r0l, r1h, r1l;
+        tile[0].frag(kk, r0h, r0l);
+        tile[1].frag(kk, r1h, r1l);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+          const f32x4 c0 = mfma16x16x32(r0h, sel[hh], zero);
+          const f32x4 c1 = mfma16x16x32(r1h, sel[hh], zero);
           const f32x4 d0 = mfma16x16x32(r0l, sel[hh], zero);
           const f32x4 d1 = mfma16x16x32(r1l, sel[hh], zero);
-          bf16x8 al;
+          bf16x8 at, al;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
+            at[jj] = (__bf16)c0[jj];
+            at[4 + jj] = (__bf16)c1[jj];
             al[jj] = (__bf16)d0[jj];
             al[4 + jj] = (__bf16)d1[jj];
           }
-          o[ks][hh] = mfma16x16x32(al, p_hi, o[ks][hh]);
+          o[kk][hh] = mfma16x16x32(at, p_hi, o[kk][hh]);
+          o[kk][hh] = mfma16x16x32(at, p_lo, o[kk][hh]);
+          o[kk][hh] = mfma16x16x32(al, p_hi, o[kk][hh]);
         }
       }
     }
+  };
+
+  if (iters > 0) {
+    HalfTile<DT, HKS> ta[2], tb[2];
+    load_block(0, ta);
+    for (int it = 0; it < iters; it += 2) {
+      load_block(it + 1, tb);
+      process_block(it, ta, 0);
+      load_block(it + 2, ta);
+      if (it + 1 < iters) process_block(it + 1, tb, 1);
+    }
   }
 
-  // ---- merge the four waves of the workgroup through LDS
+  // ---- merge the two pairs through LDS (the two waves of a pair hold identical m and l)
+  __syncthreads();  // the merge buffer reuses the row tiles
   float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
-  if (lg == 0) {
-    m_sh[wv][ln] = m_run;
-    l_sh[wv][ln] = l_tot;
+  if (half == 0 && lg == 0) {
+    ml_sh[pair][ln][0] = m_run;
+    ml_sh[pair][ln][1] = l_tot;
   }
   __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, m_sh[w][ln]);
+  const float M = fmaxf(ml_sh[0][ln][0], ml_sh[1][ln][0]);
   const float f = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);
-  for (int w = 0; w < 4; ++w) {
-    if (wv == w) {
+  for (int p = 1; p >= 0; --p) {
+    if (pair == p) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int kk = 0; kk < HKS; ++kk) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const int m = 4 * lg + jj;  // output column of the selection = row of O^T
-            const int d = dim_of_slot<DT>(ks, 2 * hh + (m >> 3), m & 7);
-            const float v = f * o[ks][hh][jj];
-            if (w == 0) o_sh[ln][d] = v; else o_sh[ln][d] += v;
+            // output column m of the selection is dim 32 ks + 16 hh + m
+            const int d = 32 * (ks0 + kk) + 16 * hh + 4 * lg + jj;
+            const float v = f * o[kk][hh][jj];
+            if (p == 1) o_sh[ln][d] = v; else o_sh[ln][d] += v;
           }
         }
       }
@@ -336,17 +406,18 @@ __global__ __launch_bounds__(256, 1) void attn_partial(Args a) {
     __syncthreads();
   }
   const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg;
-  for (int i = threadIdx.x; i < 16 * DIM; i += 256) {
-    const int h = i / DIM, d = i - h * DIM;
-    a.part_o[(pbase + h) * DIM + d] = o_sh[h][d];
+  for (int i = tid; i < 16 * DIM / 4; i += 256) {
+    const int h = i / (DIM / 4), d = 4 * (i - h * (DIM / 4));
+    *(float4*)(a.part_o + (pbase + h) * DIM + d) =
+        make_float4(o_sh[h][d], o_sh[h][d + 1], o_sh[h][d + 2], o_sh[h][d + 3]);
   }
-  if (threadIdx.x < 16) {
-    const int h = threadIdx.x;
-    float Mh = -INFINITY;
-    for (int w = 0; w < 4; ++w) Mh = fmaxf(Mh, m_sh[w][h]);
+  if (tid < 16) {
+    const int h = tid;
+    const float m0 = ml_sh[0][h][0], m1 = ml_sh[1][h][0];
+    const float Mh = fmaxf(m0, m1);
     float L = 0.f;
-    for (int w = 0; w < 4; ++w)
-      if (m_sh[w][h] != -INFINITY) L += exp2f(m_sh[w][h] - Mh) * l_sh[w][h];
+    if (m0 != -INFINITY) L += exp2f(m0 - Mh) * ml_sh[0][h][1];
+    if (m1 != -INFINITY) L += exp2f(m1 - Mh) * ml_sh[1][h][1];
     a.part_ml[(pbase + h) * 2 + 0] = Mh;
     a.part_ml[(pbase + h) * 2 + 1] = L;
   }
@@ -354,60 +425,93 @@ __global__ __launch_bounds__(256, 1) void attn_partial(Args a) {
 
 struct MergeArgs {
   int n_heads, splits, hgp, dim, rope_dims;
-  double rope_base;
   const int32_t* q_pos;
   const float* part_o;
   const float* part_ml;
   float* out;
   float* lse;
+  RopeTable rope;
 };
 
+// One wave per (query, head): split weights from the partial statistics, weighted sum of the
+// partial outputs, normalisation and R_t^{-1} on the last rope_dims dims.  The partial rows of
+// the head are first streamed into LDS with every load of a lane in flight at once.
+constexpr int kMergeStage = 8 * 576;  // floats of staged partial rows per wave (8 splits of 576)
+
 __global__ __launch_bounds__(256) void attn_merge(MergeArgs a) {
-  __shared__ float wgt[kMaxSplits][16];
-  __shared__ float cs[64], sn[64];
-  const int hg = blockIdx.x, qi = blockIdx.y, tid = threadIdx.x;
+  __shared__ float wgt[4][kMaxSplits];
+  __shared__ float cs[4][64], sn[4][64];
+  __shared__ float4 stage[4][kMergeStage / 4];
+  const int qi = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int h = 4 * blockIdx.x + wv;
+  const bool on = h < a.n_heads;  // whole waves only
   const int t = a.q_pos[qi];
-  if (tid < a.rope_dims / 2) rope_cos_sin(-(double)t, tid, a.rope_dims, a.rope_base, cs[tid], sn[tid]);
   const int64_t qbase = (int64_t)qi * a.splits;
-  if (tid < 16) {
-    const int h = tid;
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[((qbase + s) * a.hgp + 16 * hg + h) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float m = a.part_ml[((qbase + s) * a.hgp + 16 * hg + h) * 2];
+  float M = -INFINITY, L = 0.f;
+  if (on) {
+    if (lane < a.rope_dims / 2) rope_cos_sin(-(double)t, a.rope.theta[lane], cs[wv][lane], sn[wv][lane]);
+    for (int s = lane; s < a.splits; s += 64) M = fmaxf(M, a.part_ml[((qbase + s) * a.hgp + h) * 2]);
+    M = wave_max(M);
+    for (int s = lane; s < a.splits; s += 64) {
+      const float m = a.part_ml[((qbase + s) * a.hgp + h) * 2];
       const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-      wgt[s][h] = w;
-      L += w * a.part_ml[((qbase + s) * a.hgp + 16 * hg + h) * 2 + 1];
+      wgt[wv][s] = w;
+      L += w * a.part_ml[((qbase + s) * a.hgp + h) * 2 + 1];
     }
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
-    for (int s = 0; s < a.splits; ++s) wgt[s][h] *= inv;
-    const int hh = 16 * hg + h;
-    if (a.lse && hh < a.n_heads)
-      a.lse[(int64_t)qi * a.n_heads + hh] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    L = wave_sum(L);
+    if (a.lse && lane == 0) a.lse[(int64_t)qi * a.n_heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
   __syncthreads();
+  if (!on) return;
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const int dim4 = a.dim / 4;
+  const int64_t stride4 = (int64_t)a.hgp * dim4;
+  const float4* src = (const float4*)a.part_o + (qbase * a.hgp + h) * dim4;
   const int half = a.dim / 2;
-  const int rope0 = a.dim - a.rope_dims;
-  for (int i = tid; i < 16 * half; i += 256) {
-    const int h = i / half, d0 = 2 * (i - h * half);
-    const int hh = 16 * hg + h;
-    if (hh >= a.n_heads) continue;
-    float v0 = 0.f, v1 = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float w = wgt[s][h];
-      const float2 p = *(const float2*)(a.part_o + ((qbase + s) * a.hgp + hh) * a.dim + d0);
-      v0 = fmaf(w, p.x, v0);
-      v1 = fmaf(w, p.y, v1);
+  const int rope0 = (a.dim - a.rope_dims) / 2;
+  float acc[6][2];  // this lane's pairs: pp = lane + 64 u (up to 288 pairs)
+#pragma unroll
+  for (int u = 0; u < 6; ++u) acc[u][0] = acc[u][1] = 0.f;
+  const int per = kMergeStage / a.dim;  // splits staged at a time
+  constexpr int LPL = kMergeStage / 4 / 64;  // float4 loads per lane per staging round
+  for (int s0 = 0; s0 < a.splits; s0 += per) {
+    const int ns = min(per, a.splits - s0);
+    const int n4 = ns * dim4;
+    float4 v[LPL];
+#pragma unroll
+    for (int u = 0; u < LPL; ++u) {  // clamped, unconditional: all loads in flight together
+      const int i = min(lane + 64 * u, n4 - 1);
+      const int s = i / dim4, c = i - s * dim4;
+      v[u] = src[(s0 + s) * stride4 + c];
     }
-    if (d0 >= rope0) {
-      const int pi = (d0 - rope0) >> 1;
-      const float c = cs[pi], sv = sn[pi];
+#pragma unroll
+    for (int u = 0; u < LPL; ++u)
+      if (lane + 64 * u < n4) stage[wv][lane + 64 * u] = v[u];
+    const float* st = (const float*)stage[wv];
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int pp = lane + 64 * u;
+      if (pp < half) {
+        for (int s = 0; s < ns; ++s) {
+          const float w = wgt[wv][s0 + s];
+          acc[u][0] = fmaf(w, st[s * a.dim + 2 * pp], acc[u][0]);
+          acc[u][1] = fmaf(w, st[s * a.dim + 2 * pp + 1], acc[u][1]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 6; ++u) {
+    const int pp = lane + 64 * u;
+    if (pp >= half) continue;
+    float v0 = acc[u][0] * inv, v1 = acc[u][1] * inv;
+    if (pp >= rope0) {
+      const float c = cs[wv][pp - rope0], sv = sn[wv][pp - rope0];
       const float r0 = v0 * c - v1 * sv, r1 = v0 * sv + v1 * c;
       v0 = r0;
       v1 = r1;
     }
-    *(float2*)(a.out + ((int64_t)qi * a.n_heads + hh) * a.dim + d0) = make_float2(v0, v1);
+    *(float2*)(a.out + ((int64_t)qi * a.n_heads + h) * a.dim + 2 * pp) = make_float2(v0, v1);
   }
 }
 
@@ -440,12 +544,9 @@ AttnPlan attn_plan(int total_q, int n_heads, int ratio, int has_topk, int k, int
   const int64_t units = (int64_t)total_q * p.head_groups;
   // aim at one 256-thread workgroup per compute unit (256 CUs), at least 4 blocks per group
   int64_t bpw = std::max<int64_t>(4, (blocks32 * units + 255) / 256);
-  bpw = std::min(bpw, blocks32);
-  int64_t splits = (blocks32 + bpw - 1) / bpw;
-  if (splits > kMaxSplits) {
-    bpw = (blocks32 + kMaxSplits - 1) / kMaxSplits;
-    splits = (blocks32 + bpw - 1) / bpw;
-  }
+  bpw = std::min<int64_t>(std::min(bpw, blocks32), kRowsPerSplit / 32);
+  // callers keep max_rows <= kMaxSplits * kRowsPerSplit, so splits <= kMaxSplits
+  const int64_t splits = (blocks32 + bpw - 1) / bpw;
   p.splits = (int)splits;
   p.rows_per_split = (int)(bpw * 32);
   return p;
@@ -496,13 +597,13 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, const AttnPlan& p, void* work
   m.hgp = a.hgp;
   m.dim = dim;
   m.rope_dims = L.rope_dims;
-  m.rope_base = (double)L.rope_base;
+  m.rope = make_rope_table(L.rope_base, L.rope_dims);
   m.q_pos = L.q_pos;
   m.part_o = a.part_o;
   m.part_ml = a.part_ml;
   m.out = L.out;
   m.lse = L.lse;
-  hipLaunchKernelGGL(attn_merge, dim3(p.head_groups, L.total_q), dim3(256), 0, stream, m);
+  hipLaunchKernelGGL(attn_merge, dim3((L.n_heads + 3) / 4, L.total_q), dim3(256), 0, stream, m);
   return hipGetLastError();
 }
 

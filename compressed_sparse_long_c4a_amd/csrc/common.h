@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "csa.h"
 
 namespace csa {
@@ -13,13 +15,20 @@ constexpr int kWave = 64;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Device-side copy of a csa_cache descriptor (passed to kernels by value).
+// Device-side copy of a csa_cache descriptor (passed to kernels by value).  rows_per_block is
+// a power of two (2, 64 or 256) and is kept as its log2 so paged addressing needs no division.
 struct DevCache {
   void* rows;
   float* scales;
   const int32_t* bt;
-  int32_t dtype, dim, rpb, bt_stride;
+  int32_t dtype, dim, rpb_shift, bt_stride;
 };
+
+inline int log2_exact(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
 
 inline DevCache to_dev(const csa_cache* c) {
   DevCache d{};
@@ -29,7 +38,7 @@ inline DevCache to_dev(const csa_cache* c) {
   d.bt = c->block_table;
   d.dtype = c->dtype;
   d.dim = c->dim;
-  d.rpb = c->rows_per_block;
+  d.rpb_shift = log2_exact(c->rows_per_block);
   d.bt_stride = c->bt_stride;
   return d;
 }
@@ -37,8 +46,20 @@ inline DevCache to_dev(const csa_cache* c) {
 // Physical row index of logical row r of sequence b: block_table[b][r / rpb] * rpb + r % rpb
 // (256-position logical blocks; 64 or 2 compressed entries, or 256 raw rows, per block).
 __device__ __forceinline__ int64_t phys_row(const DevCache& c, int b, int64_t r) {
-  const int32_t blk = c.bt[(int64_t)b * c.bt_stride + (int32_t)(r / c.rpb)];
-  return (int64_t)blk * c.rpb + (r % c.rpb);
+  const int32_t blk = c.bt[(int64_t)b * c.bt_stride + (int32_t)(r >> c.rpb_shift)];
+  return ((int64_t)blk << c.rpb_shift) + (r & ((1 << c.rpb_shift) - 1));
+}
+
+// theta_i = rope_base^(-2i/rope_dims) for i < rope_dims/2, computed on the host in float64.
+struct RopeTable {
+  double theta[64];
+};
+
+inline RopeTable make_rope_table(float base, int rope_dims) {
+  RopeTable t{};
+  for (int i = 0; i < rope_dims / 2 && i < 64; ++i)
+    t.theta[i] = std::pow((double)base, -2.0 * (double)i / (double)rope_dims);
+  return t;
 }
 
 // Sequence owning flat index i, given prefix sums cu[0..batch] (empty sequences allowed).
@@ -49,6 +70,16 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int batch, int i) {
     if (cu[mid] <= i) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Same as seq_of with one round trip for batch <= 64: every lane of the calling wave loads
+// one prefix sum and a ballot finds the last sequence starting at or before i.
+__device__ __forceinline__ int seq_of_wave(const int32_t* cu, int batch, int i) {
+  if (batch > 64) return seq_of(cu, batch, i);
+  const int lane = threadIdx.x & 63;
+  const bool le = lane < batch && cu[lane] <= i;
+  const unsigned long long m = __ballot(le);
+  return m ? 63 - __clzll(m) : 0;
 }
 
 // ---------------------------------------------------------------- formats
@@ -63,6 +94,17 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
   auto v = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
   a = v[0];
   b = v[1];
+}
+
+// Eight OCP E4M3 codes (two words) to eight bfloat16 values; exact (every E4M3 value is a
+// bfloat16 value), two codes per conversion instruction.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 __device__ __forceinline__ float fp8_to_f32(uint8_t c) {
@@ -88,6 +130,13 @@ __device__ __forceinline__ uint32_t f2key(float f) {
 __device__ __forceinline__ float key2f(uint32_t k) {
   const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
   return __uint_as_float(u);
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for its
+// outstanding global loads (which __syncthreads() would drain), so prefetched loads stay in
+// flight across the barrier.  Use only where the barrier protects LDS data.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ---------------------------------------------------------------- reductions
@@ -140,14 +189,14 @@ __device__ __forceinline__ int block_exscan256(int v, int* sh, int* total) {
   return base + incl - v;
 }
 
-// RoPE angle position * base^(-2i/rope_dims), formed and reduced in float64.
-__device__ __forceinline__ void rope_cos_sin(double position, int i, int rope_dims, double base,
-                                             float& c, float& s) {
-  const double theta = pow(base, -2.0 * (double)i / (double)rope_dims);
-  double sd, cd;
-  sincos(position * theta, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+// cos/sin of the RoPE angle position * theta: the product is formed in float64 and reduced to
+// [-pi, pi] there (|angle| reaches ~1e6 at 1M positions, where float32 would be off by ~0.05 rad),
+// then the reduced angle is evaluated in float32.
+__device__ __forceinline__ void rope_cos_sin(double position, double theta, float& c, float& s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  const double x = position * theta;
+  const double r = x - two_pi * rint(x * (1.0 / two_pi));
+  sincosf((float)r, &s, &c);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -81,50 +81,84 @@ __device__ void pick_bin_wave0(const uint32_t* hist, int need, int* out) {
   }
 }
 
-// Lower bound (16-bit key prefix) of the kc-th largest of the C scores in sc_sh.
-__device__ uint32_t chunk_bound(const float* sc_sh, int kc, uint32_t* hist, int* misc) {
+__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return min(min(red[0], red[1]), min(red[2], red[3]));
+}
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// Bits needed to hold v (0 for v = 0).
+__device__ __forceinline__ int bit_len(uint32_t v) { return v ? 32 - __clz((int)v) : 0; }
+
+// Lower bound of the kc-th largest of the C scores in sc_sh: one 256-bin histogram over the
+// chunk's own key range [kmin, kmax]; the bound is the lower edge of the bin that holds the
+// kc-th largest key.
+__device__ uint32_t chunk_bound(const float* sc_sh, int kc, uint32_t* hist, int* misc, uint32_t* red) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0;
-  int need = kc;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = 24 - 8 * pass;
-    hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < C; i += 256) {
-      const uint32_t key = f2key(sc_sh[i]);
-      if (pass == 0 || (key >> 24) == (prefix >> 24)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < kWave) pick_bin_wave0(hist, need, misc);
-    __syncthreads();
-    prefix |= (uint32_t)misc[0] << shift;
-    need -= misc[1];
-    __syncthreads();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int i = tid; i < C; i += 256) {
+    const uint32_t key = f2key(sc_sh[i]);
+    lo = min(lo, key);
+    hi = max(hi, key);
   }
-  return prefix;
+  lo = block_min_u32(lo, red);
+  hi = block_max_u32(hi, red);
+  const int shift = max(0, bit_len(hi - lo) - 8);
+  hist[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < C; i += 256) atomicAdd(&hist[((f2key(sc_sh[i]) - lo) >> shift) & 255u], 1u);
+  __syncthreads();
+  if (tid < kWave) pick_bin_wave0(hist, kc, misc);
+  __syncthreads();
+  const uint32_t bound = lo + ((uint32_t)misc[0] << shift);
+  __syncthreads();
+  return bound;
 }
 
 // Shared tail of both score kernels: write the chunk's bound when the chunk is full.
 __device__ void finish_chunk(const ScoreArgs& a, int qi, int chunk, int n, int nloc,
-                             const float* sc_sh, uint32_t* hist, int* misc) {
+                             const float* sc_sh, uint32_t* hist, int* misc, uint32_t* red) {
   const int kprime = min(a.k, n);
   const int m_full = n / C;
   if (nloc == C && kprime < n && m_full > 0) {
     const int kc = (kprime + m_full - 1) / m_full;
     uint32_t bound = 0;
-    if (kc <= C) bound = chunk_bound(sc_sh, kc, hist, misc);
+    if (kc <= C) bound = chunk_bound(sc_sh, kc, hist, misc, red);
     if (threadIdx.x == 0) a.bounds[(int64_t)qi * a.chunks + chunk] = bound;
   }
 }
 
 // ---- MFMA score kernel: bf16 queries, fp8 or bf16 keys, HT tiles of 16 heads (<= 64 heads).
+// Wave w of the workgroup takes the 16-entry tiles w, w+4, ... of the chunk, so in group gi
+// the four waves cover the four 64-entry blocks 4 gi .. 4 gi + 3 together.  The physical ids
+// of the chunk's blocks are fetched once; key loads run one group ahead of the MFMA work
+// (two register buffers), so a wave always has a group of keys in flight.
+template <int KEY_DT>
+struct KeyGroup {
+  static constexpr int NW = KEY_DT == CSA_FP8_E4M3 ? 2 : 4;  // 16-byte words per lane per tile
+  uint4 raw[4][NW];
+  float scale[4];
+};
+
 template <int KEY_DT, int HT>
 __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
   __shared__ float sc_sh[C];
   __shared__ uint32_t hist[256];
   __shared__ int misc[4];
+  __shared__ uint32_t red[4];
   const int chunk = blockIdx.x, qi = blockIdx.y;
-  const int b = seq_of(a.cu_q, a.batch, qi);
+  const int b = seq_of_wave(a.cu_q, a.batch, qi);
   const int n = query_entries(a.q_pos, qi, a.n_max);
   const int64_t j0 = (int64_t)chunk * C;
   if (j0 >= n) return;
@@ -132,10 +166,85 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const int H = a.n_heads;
+  constexpr int NW = KeyGroup<KEY_DT>::NW;
 
-  // A operand: lane (head ln of tile mt, group lg) holds q[h][32 lg + 8 ks + 0..7].
+  // physical block ids of the chunk (C / 64 = 32 blocks): lane i of every wave holds block i
+  const int nblk = (nloc + 63) >> 6;
+  const int32_t* btrow = a.cache.bt + (int64_t)b * a.cache.bt_stride + (j0 >> 6);
+  const int32_t my_blk = lane < nblk ? btrow[lane] : 0;
+
+  const int ntiles = (nloc + 15) >> 4;
   bf16x8 qa[HT][4];
   float wt[HT][4];
+
+  // Loads and stores are unconditional (the wait counters then let the next group stay in
+  // flight): entries past the chunk's end read the chunk's last row and write their unused
+  // scores inside this chunk's own slice of the workspace.
+  auto load_group = [&](int gi, KeyGroup<KEY_DT>& kg) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int tile = min(16 * gi + 4 * u + wv, ntiles - 1);
+      const int eloc = min(tile * 16 + ln, nloc - 1);
+      const int blk = __builtin_amdgcn_readlane(my_blk, min(4 * gi + u, nblk - 1));
+      const int64_t prow = ((int64_t)blk << 6) + (eloc & 63);
+      if constexpr (KEY_DT == CSA_FP8_E4M3) {
+        const uint4* src = (const uint4*)((const uint8_t*)a.cache.rows + prow * 128 + 32 * lg);
+        kg.raw[u][0] = src[0];
+        kg.raw[u][1] = src[1];
+        kg.scale[u] = a.cache.scales[prow];
+      } else {
+        const uint4* src = (const uint4*)((const uint16_t*)a.cache.rows + prow * 128 + 32 * lg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kg.raw[u][i] = src[i];
+        kg.scale[u] = 1.f;
+      }
+    }
+  };
+
+  auto compute_group = [&](int gi, const KeyGroup<KEY_DT>& kg) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int tile = 16 * gi + 4 * u + wv;
+      bf16x8 kb[4];
+      if constexpr (KEY_DT == CSA_FP8_E4M3) {
+        const uint32_t wd[8] = {kg.raw[u][0].x, kg.raw[u][0].y, kg.raw[u][0].z, kg.raw[u][0].w,
+                                kg.raw[u][1].x, kg.raw[u][1].y, kg.raw[u][1].z, kg.raw[u][1].w};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[ks] = fp8x8_to_bf16x8(wd[2 * ks], wd[2 * ks + 1]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[ks] = __builtin_bit_cast(bf16x8, kg.raw[u][ks]);
+      }
+      // k-step outer, head tile inner: consecutive MFMAs are independent
+      f32x4 acc[HT];
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(qa[mt][ks], kb[ks], acc[mt]);
+      float sacc = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sacc = fmaf(wt[mt][jj], fmaxf(acc[mt][jj], 0.f), sacc);
+      sacc += __shfl_xor(sacc, 16, kWave);
+      sacc += __shfl_xor(sacc, 32, kWave);
+      sacc *= kg.scale[u];
+      // tile < C / 16 always, so every lane's slot is inside this chunk's workspace slice
+      const int eloc = tile * 16 + ln;
+      a.scores[(int64_t)qi * a.n_cap + j0 + eloc] = sacc;
+      sc_sh[eloc] = sacc;
+    }
+  };
+
+  // every chunk runs the same fully unrolled sequence of C / 256 groups with no runtime
+  // conditions, so the wait counters keep one group of keys in flight behind the MFMA work
+  constexpr int NG = C / 256;
+  KeyGroup<KEY_DT> kg[2];
+  load_group(0, kg[0]);
+  // (issued after the first keys) A operand: lane (head ln of tile mt, group lg) holds
+  // q[h][32 lg + 8 ks + 0..7].
   const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)qi * H * 128;
 #pragma unroll
   for (int mt = 0; mt < HT; ++mt) {
@@ -153,83 +262,13 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
     }
   }
 
-  const int ntiles = (nloc + 15) >> 4;
-  constexpr int U = 4;  // tiles in flight per wave
-  for (int base = wv; base < ntiles; base += 4 * U) {
-    uint4 raw[U][KEY_DT == CSA_FP8_E4M3 ? 2 : 4];
-    float scale[U];
-    bool valid[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tile = base + 4 * u;
-      const int eloc = tile * 16 + ln;
-      valid[u] = tile < ntiles && eloc < nloc;
-      scale[u] = 0.f;
-#pragma unroll
-      for (int i = 0; i < (KEY_DT == CSA_FP8_E4M3 ? 2 : 4); ++i) raw[u][i] = make_uint4(0, 0, 0, 0);
-      if (valid[u]) {
-        const int64_t prow = phys_row(a.cache, b, j0 + eloc);
-        if (KEY_DT == CSA_FP8_E4M3) {
-          const uint4* src = (const uint4*)((const uint8_t*)a.cache.rows + prow * 128 + 32 * lg);
-          raw[u][0] = src[0];
-          raw[u][1] = src[1];
-          scale[u] = a.cache.scales[prow];
-        } else {
-          const uint4* src = (const uint4*)((const uint16_t*)a.cache.rows + prow * 128 + 32 * lg);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) raw[u][i] = src[i];
-          scale[u] = 1.f;
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tile = base + 4 * u;
-      if (tile >= ntiles) break;
-      bf16x8 kb[4];
-      if (KEY_DT == CSA_FP8_E4M3) {
-        const uint32_t wd[8] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w,
-                                raw[u][1].x, raw[u][1].y, raw[u][1].z, raw[u][1].w};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          bf16x8 f;
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            float x0, x1, x2, x3;
-            fp8x2_to_f32<false>(wd[2 * ks + h2], x0, x1);
-            fp8x2_to_f32<true>(wd[2 * ks + h2], x2, x3);
-            f[4 * h2 + 0] = (__bf16)x0;
-            f[4 * h2 + 1] = (__bf16)x1;
-            f[4 * h2 + 2] = (__bf16)x2;
-            f[4 * h2 + 3] = (__bf16)x3;
-          }
-          kb[ks] = f;
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb[ks] = __builtin_bit_cast(bf16x8, raw[u][ks]);
-      }
-      float s = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < HT; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(qa[mt][ks], kb[ks], acc);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) s = fmaf(wt[mt][jj], fmaxf(acc[jj], 0.f), s);
-      }
-      s += __shfl_xor(s, 16, kWave);
-      s += __shfl_xor(s, 32, kWave);
-      s *= scale[u];
-      const int eloc = tile * 16 + ln;
-      if (lg == 0 && valid[u]) {
-        a.scores[(int64_t)qi * a.n_cap + j0 + eloc] = s;
-        sc_sh[eloc] = s;
-      }
-    }
+  for (int gi = 0; gi < NG; ++gi) {
+    if (gi + 1 < NG) load_group(gi + 1, kg[(gi + 1) & 1]);
+    compute_group(gi, kg[gi & 1]);
   }
   __syncthreads();
-  finish_chunk(a, qi, chunk, n, nloc, sc_sh, hist, misc);
+  finish_chunk(a, qi, chunk, n, nloc, sc_sh, hist, misc, red);
 }
 
 // ---- float32 queries (any key dtype): plain per-entry dot products.
@@ -239,8 +278,9 @@ __global__ __launch_bounds__(256) void index_score_f32(ScoreArgs a) {
   __shared__ float w_sh[64];
   __shared__ uint32_t hist[256];
   __shared__ int misc[4];
+  __shared__ uint32_t red[4];
   const int chunk = blockIdx.x, qi = blockIdx.y;
-  const int b = seq_of(a.cu_q, a.batch, qi);
+  const int b = seq_of_wave(a.cu_q, a.batch, qi);
   const int n = query_entries(a.q_pos, qi, a.n_max);
   const int64_t j0 = (int64_t)chunk * C;
   if (j0 >= n) return;
@@ -278,7 +318,7 @@ __global__ __launch_bounds__(256) void index_score_f32(ScoreArgs a) {
   __syncthreads();
   for (int eloc = threadIdx.x; eloc < nloc; eloc += 256)
     a.scores[(int64_t)qi * a.n_cap + j0 + eloc] = sc_sh[eloc];
-  finish_chunk(a, qi, chunk, n, nloc, sc_sh, hist, misc);
+  finish_chunk(a, qi, chunk, n, nloc, sc_sh, hist, misc, red);
 }
 
 // ---- filter: compact the chunk's entries with key >= tau_lo, in entry order.
@@ -321,6 +361,7 @@ __global__ __launch_bounds__(256) void index_filter(SelArgs a) {
   if (kprime == n) return;  // select takes every candidate directly
   const uint32_t tau = query_tau_lo(a, qi, n, red);
   const int nloc = (int)min((int64_t)C, n - j0);
+  static_assert(C == 256 * 8, "the filter gives each of its 256 threads 8 entries of a chunk");
   const int base = threadIdx.x * 8;
   uint32_t key[8];
   int cnt = 0;
@@ -347,6 +388,44 @@ __global__ __launch_bounds__(256) void index_filter(SelArgs a) {
 }
 
 // ---- select: exact k-th largest among the candidates, winners in ascending entry order.
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+
+template <typename T, typename Op>
+__device__ __forceinline__ T sel_block_reduce(T v, T* red, Op op) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = op(v, (T)__shfl_xor(v, o, kWave));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  T r = red[0];
+#pragma unroll
+  for (int i = 1; i < kSelWaves; ++i) r = op(r, red[i]);
+  return r;
+}
+
+// Exclusive prefix sum over the select block; total in *total.  sh holds kSelWaves ints.
+__device__ __forceinline__ int sel_exscan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) sh[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) {
+    base += i < w ? sh[i] : 0;
+    tot += sh[i];
+  }
+  *total = tot;
+  return base + incl - v;
+}
+
 template <bool IN_LDS>
 __device__ __forceinline__ uint2 cand_at(const uint2* cand_sh, const uint2* gcand, const int* off_sh,
                                          int nchunks, int g) {
@@ -362,18 +441,26 @@ __device__ __forceinline__ uint2 cand_at(const uint2* cand_sh, const uint2* gcan
 template <bool IN_LDS>
 __device__ void select_core(const SelArgs& a, int qi, int m, int kprime, const uint2* cand_sh,
                             const uint2* gcand, const int* off_sh, int nchunks, uint32_t* hist,
-                            int* misc, int* scan_sh) {
+                            int* misc, int* scan_sh, uint32_t* red) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0;
+  // radix select on d = key - lo over the candidates' own range, 8 bits per pass from the top
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int g = tid; g < m; g += kSelThreads) {
+    const uint32_t key = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x;
+    lo = min(lo, key);
+    hi = max(hi, key);
+  }
+  lo = sel_block_reduce(lo, red, [](uint32_t x, uint32_t y) { return min(x, y); });
+  hi = sel_block_reduce(hi, red, [](uint32_t x, uint32_t y) { return max(x, y); });
+  uint32_t prefix = 0;  // decided high digits of d
   int need = kprime;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    hist[tid] = 0;
+  for (int top = bit_len(hi - lo); top > 0; top -= 8) {
+    const int shift = max(0, top - 8);
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int g = tid; g < m; g += 256) {
-      const uint32_t key = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x;
-      if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
-        atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    for (int g = tid; g < m; g += kSelThreads) {
+      const uint32_t d = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x - lo;
+      if (top >= 32 || (d >> top) == (prefix >> top)) atomicAdd(&hist[(d >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (tid < kWave) pick_bin_wave0(hist, need, misc);
@@ -382,15 +469,15 @@ __device__ void select_core(const SelArgs& a, int qi, int m, int kprime, const u
     need -= misc[1];
     __syncthreads();
   }
-  const uint32_t tau = prefix;   // the kprime-th largest key
-  const int ties_needed = need;  // how many keys equal to tau are selected
+  const uint32_t tau = prefix + lo;  // the kprime-th largest key
+  const int ties_needed = need;      // how many keys equal to tau are selected
   // contiguous ranges per thread keep entry order through both scans
-  const int per = (m + 255) / 256;
+  const int per = (m + kSelThreads - 1) / kSelThreads;
   const int g0 = min(m, tid * per), g1 = min(m, g0 + per);
   int eq = 0;
   for (int g = g0; g < g1; ++g) eq += cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x == tau;
   int tot;
-  int tie_rank = block_exscan256(eq, scan_sh, &tot);
+  const int tie_rank = sel_exscan(eq, scan_sh, &tot);
   int sel = 0;
   {
     int tr = tie_rank;
@@ -400,7 +487,7 @@ __device__ void select_core(const SelArgs& a, int qi, int m, int kprime, const u
       else if (key == tau) { sel += tr < ties_needed; ++tr; }
     }
   }
-  int pos = block_exscan256(sel, scan_sh + 4, &tot);
+  int pos = sel_exscan(sel, scan_sh + kSelWaves, &tot);
   int32_t* out = a.topk_idx + (int64_t)qi * a.k;
   float* outs = a.topk_score ? a.topk_score + (int64_t)qi * a.k : nullptr;
   int tr = tie_rank;
@@ -417,57 +504,58 @@ __device__ void select_core(const SelArgs& a, int qi, int m, int kprime, const u
   }
 }
 
-__global__ __launch_bounds__(256) void index_select(SelArgs a) {
+__global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
   __shared__ uint2 cand_sh[kSelCap];
   __shared__ int off_sh[kMaxChunks + 1];
   __shared__ uint32_t hist[256];
   __shared__ int misc[4];
-  __shared__ int scan_sh[8];
+  __shared__ int scan_sh[2 * kSelWaves];
+  __shared__ uint32_t red[kSelWaves];
   const int qi = blockIdx.x, tid = threadIdx.x;
   const int n = query_entries(a.q_pos, qi, a.n_max);
   const int kprime = min(a.k, n);
   int32_t* out = a.topk_idx + (int64_t)qi * a.k;
   float* outs = a.topk_score ? a.topk_score + (int64_t)qi * a.k : nullptr;
-  for (int i = kprime + tid; i < a.k; i += 256) {
+  for (int i = kprime + tid; i < a.k; i += kSelThreads) {
     out[i] = -1;
     if (outs) outs[i] = 0.f;
   }
   if (kprime == 0) return;
   const float* sc = a.scores + (int64_t)qi * a.n_cap;
   if (kprime == n) {  // every causal entry is selected
-    for (int i = tid; i < n; i += 256) {
+    for (int i = tid; i < n; i += kSelThreads) {
       out[i] = i;
       if (outs) outs[i] = sc[i];
     }
     return;
   }
-  // prefix sums of the per-chunk candidate counts
+  // prefix sums of the per-chunk candidate counts (one chunk per thread)
   const int nchunks = (n + C - 1) / C;
-  constexpr int kPer = kMaxChunks / 256;
-  int cnt[kPer];
-  int local = 0;
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int c = tid * kPer + r;
-    cnt[r] = c < nchunks ? a.cand_cnt[(int64_t)qi * a.chunks + c] : 0;
-    local += cnt[r];
-  }
+  const int cnt = tid < nchunks ? a.cand_cnt[(int64_t)qi * a.chunks + tid] : 0;
   int m;
-  int off = block_exscan256(local, scan_sh, &m);
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    off_sh[tid * kPer + r] = off;
-    off += cnt[r];
-  }
+  off_sh[tid] = sel_exscan(cnt, scan_sh, &m);
   if (tid == 0) off_sh[kMaxChunks] = m;
   __syncthreads();
   const uint2* gcand = a.cand + (int64_t)qi * a.n_cap;
   if (m <= kSelCap) {
-    for (int g = tid; g < m; g += 256) cand_sh[g] = cand_at<false>(nullptr, gcand, off_sh, nchunks, g);
+    // gather the chunk-sparse candidates densely, eight independent loads in flight per thread
+    for (int base = 0; base < m; base += 8 * kSelThreads) {
+      uint2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int g = base + u * kSelThreads + tid;
+        v[u] = g < m ? cand_at<false>(nullptr, gcand, off_sh, nchunks, g) : make_uint2(0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int g = base + u * kSelThreads + tid;
+        if (g < m) cand_sh[g] = v[u];
+      }
+    }
     __syncthreads();
-    select_core<true>(a, qi, m, kprime, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh);
+    select_core<true>(a, qi, m, kprime, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh, red);
   } else {
-    select_core<false>(a, qi, m, kprime, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh);
+    select_core<false>(a, qi, m, kprime, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh, red);
   }
 }
 
@@ -561,7 +649,7 @@ hipError_t launch_index_select(const IndexLaunch& a, int32_t* topk_idx, float* t
   hipLaunchKernelGGL(index_filter, dim3(ws.chunks, a.total_q), dim3(256), 0, stream, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(index_select, dim3(a.total_q), dim3(256), 0, stream, s);
+  hipLaunchKernelGGL(index_select, dim3(a.total_q), dim3(kSelThreads), 0, stream, s);
   return hipGetLastError();
 }
 

@@ -60,6 +60,9 @@ hipError_t launch_index_select(const IndexLaunch& a, int32_t* topk_idx, float* t
                                const IndexWorkspace& ws, hipStream_t stream);
 
 // ---------------------------------------------------------------- attention
+// Rows (top-k list length or visible entries, plus window) one query may attend to.
+constexpr int64_t kAttnMaxRows = 256 * 1024;
+
 struct AttnPlan {
   int splits;          // row splits per (query, head group)
   int rows_per_split;  // multiple of 32

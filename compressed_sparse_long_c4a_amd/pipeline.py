@@ -9,8 +9,10 @@ from __future__ import annotations
 
 import torch
 
-from . import (PagedCache, compress_insert, index_score, index_select, index_workspace_size,
-               sparse_attn_decode, sparse_attn_workspace_size)
+import ctypes
+
+from . import (OK, CsaError, PagedCache, compress_insert, dtype_code, index_score, index_select,
+               index_workspace_size, lib, sparse_attn_decode, sparse_attn_workspace_size)
 
 CACHE_KEYS = ("kv", "swa", "state", "idx", "idx_state")
 
@@ -50,6 +52,8 @@ class Step:
         self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
         self.out = torch.empty((total_q, H, D), dtype=torch.float32, device=dev)
         self.lse = None
+        self.side = None  # second stream for the overlapped schedule (created on first use)
+        self._bound = {}  # id(g) -> pre-marshalled C calls of the step (see fast())
 
     def compress(self, g=None):
         g = g or self.g
@@ -82,6 +86,99 @@ class Step:
                                       with_lse=with_lse, out=self.out, workspace=self.attn_ws)
         self.lse = lse
         return out, lse
+
+    def run_overlapped(self, g=None, with_lse: bool = True):
+        """The whole step with the main-KV compressor (and window-row insert) on a second stream,
+        concurrent with the indexer pipeline (indexer compress, score, top-k) on the current one;
+        attention waits for both.  This is the schedule of the c4a decode path in the pages'
+        multi-stream design; every stream keeps the default priority."""
+        st = self.cfg.stages
+        if "compress" not in st or "index" not in st:
+            return self.run(g, with_lse)
+        main = torch.cuda.current_stream()
+        if self.side is None:
+            self.side = torch.cuda.Stream(device=main.device)
+            self.ev_fork = torch.cuda.Event()
+            self.ev_join = torch.cuda.Event()
+        self.ev_fork.record(main)
+        with torch.cuda.stream(self.side):
+            self.side.wait_event(self.ev_fork)
+            self.compress(g)
+            self.ev_join.record(self.side)
+        if "compress_idx" in st:
+            self.compress_idx(g)
+        self.index_score(g)
+        self.index_select(g)
+        main.wait_event(self.ev_join)
+        if "attn" in st:
+            self.attn(g, with_lse)
+        return self
+
+    def _bind(self, g: dict):
+        """Marshal every C call of the step for input dict g once: (name, function, arguments
+        without the leading stream).  The argument checks of the wrappers ran when the same calls
+        went through them (fast() requires one run() of g first)."""
+        c, L = self.cfg, lib()
+        P = ctypes.c_void_p
+        calls = []
+        refs = []  # keep the ctypes structs alive
+
+        def cache(x):
+            r = ctypes.pointer(x.c())
+            refs.append(r)
+            return r
+        B = g["ctx_lens"].shape[0] if "ctx_lens" in g else g["cu_q"].shape[0] - 1
+        if "compress" in c.stages:
+            calls.append(("compress", L.csa_compress_insert, (
+                c.ratio, B, g["ctx_lens"].data_ptr(), g["cu_new"].data_ptr(), g["new_raw"].shape[0],
+                g["new_raw"].data_ptr(), dtype_code(g["new_raw"].dtype), g["cu_entries"].data_ptr(),
+                g["logits"].shape[0], g["logits"].data_ptr(),
+                None if g.get("gamma") is None else g["gamma"].data_ptr(), c.eps, c.rope_base, 64,
+                cache(g["state"]), cache(g["kv"]), cache(g["swa"]))))
+        if "compress_idx" in c.stages:
+            calls.append(("compress_idx", L.csa_compress_insert, (
+                4, B, g["ctx_lens"].data_ptr(), g["cu_new"].data_ptr(), g["new_idx_raw"].shape[0],
+                g["new_idx_raw"].data_ptr(), dtype_code(g["new_idx_raw"].dtype), g["cu_entries"].data_ptr(),
+                g["idx_logits"].shape[0], g["idx_logits"].data_ptr(), None, c.eps, c.rope_base, 64,
+                cache(g["idx_state"]), cache(g["idx"]), None)))
+        total_q = g["q_pos"].shape[0]
+        if "index" in c.stages:
+            calls.append(("index_score", L.csa_index_score, (
+                B, g["cu_q"].data_ptr(), g["q_pos"].data_ptr(), total_q, c.max_context, g["q_idx"].data_ptr(),
+                dtype_code(g["q_idx"].dtype), g["q_idx"].shape[1], g["head_w"].data_ptr(), cache(g["idx"]),
+                c.k, self.idx_ws.data_ptr(), self.idx_ws.numel())))
+            calls.append(("index_select", L.csa_index_select, (
+                B, g["cu_q"].data_ptr(), g["q_pos"].data_ptr(), total_q, c.max_context, c.k,
+                self.topk.data_ptr(), None if self.topk_score is None else self.topk_score.data_ptr(),
+                self.idx_ws.data_ptr(), self.idx_ws.numel())))
+        if "attn" in c.stages:
+            topk = self.topk if "index" in c.stages else g.get("topk")
+            calls.append(("attn", L.csa_sparse_attn_decode, (
+                B, g["cu_q"].data_ptr(), g["q_pos"].data_ptr(), total_q, c.max_context, g["q"].data_ptr(),
+                dtype_code(g["q"].dtype), g["q"].shape[1], cache(g["kv"]), c.ratio,
+                None if topk is None else topk.data_ptr(), 0 if topk is None else topk.shape[1],
+                cache(g["swa"]), c.window, c.softmax_scale, c.rope_base, 64, self.out.data_ptr(), None,
+                self.attn_ws.data_ptr(), self.attn_ws.numel())))
+        return calls, refs
+
+    def fast(self, g=None, score_events=None):
+        """The whole step (no lse) through pre-marshalled C calls, on the current stream: the same
+        calls as run(), with the host-side Python work done once per input dict.  score_events:
+        optional (before, after) torch events recorded around the index-score launch."""
+        g = g or self.g
+        key = id(g)
+        if key not in self._bound:
+            self._bound[key] = self._bind(g)
+        stream = torch.cuda.current_stream().cuda_stream
+        for name, fn, args in self._bound[key][0]:
+            if score_events is not None and name == "index_score":
+                score_events[0].record()
+            st = fn(stream, *args)
+            if score_events is not None and name == "index_score":
+                score_events[1].record()
+            if st != OK:
+                raise CsaError(name, st)
+        return self
 
     def run(self, g=None, with_lse: bool = True):
         """The whole step, in stage order, on the current stream."""

@@ -211,6 +211,8 @@ int csa_index_select(csa_stream_t stream, int batch, const int32_t* cu_q, const 
  *   kv: rows_per_block 256 / ratio; swa: rows_per_block 256; both with the same
  *       dim (512 or 576) and the same dtype (F32, BF16 or FP8_E4M3).  rope_dims = 64.
  *   1 <= n_heads <= 128.  topk_idx [total_q][k] int32 or NULL (then k is ignored).
+ *   The row count per query, (topk_idx ? k : n(max_context)) + min(window, max_context), must
+ *   not exceed 262144 (CSA_ENOTSUP otherwise; the workspace query then returns 0).
  *   0 <= window <= 4096.  out [total_q][n_heads][dim] float32.  lse [total_q][n_heads] or NULL.
  *   workspace of at least csa_sparse_attn_workspace_size(...) bytes with the same
  *   total_q, n_heads, dim, ratio, topk_idx != NULL, k, max_context and window.

@@ -112,14 +112,16 @@ def compare(cfg, d: dict, step, ores: dict) -> dict:
     return rep
 
 
-def run_step_parity(cfg, queries=None, verbose: bool = False, prep=None) -> dict:
-    """Draw inputs, run the GPU step and the oracle, compare.  Returns the report."""
+def run_step_parity(cfg, queries=None, verbose: bool = False, prep=None, overlap: bool = False) -> dict:
+    """Draw inputs, run the GPU step (optionally with the two-stream schedule) and the oracle,
+    compare.  Returns the report."""
     from compressed_sparse_long_c4a_amd import pipeline
     d = inputs.draw(cfg)
     if prep is not None:
         prep(d)
     g = pipeline.to_device(d)
-    step = pipeline.Step(cfg, g).run()
+    step = pipeline.Step(cfg, g)
+    step.run_overlapped() if overlap else step.run()
     torch.cuda.synchronize()
     ores = O.run_oracle(cfg, d, queries=queries)
     rep = compare(cfg, d, step, ores)

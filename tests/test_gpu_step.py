@@ -25,3 +25,12 @@ def test_step_parity(gpu, name):
     print(f"case {name}: {cfg}", flush=True)
     rep = P.run_step_parity(cfg, verbose=True)
     assert not rep["fail"], rep["fail"][:10]
+
+
+@pytest.mark.gpu
+def test_two_stream_schedule_parity(gpu):
+    """The main-KV compressor on a second stream, concurrent with the indexer pipeline."""
+    cfg = P.SMALL_DECODE
+    print(f"case two-stream: {cfg.name}", flush=True)
+    rep = P.run_step_parity(cfg, verbose=True, overlap=True)
+    assert not rep["fail"], rep["fail"][:10]
