@@ -6,17 +6,26 @@ import glob
 import os
 import shutil
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libcsa.so")
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "-fPIC",
     "--offload-arch=gfx950",
     # no packed-fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+
+# Per-source extra flags.  The attention kernel keeps its MFMA accumulators in ordinary VGPRs:
+# it rescales them with VALU instructions between blocks, and accumulators in AGPRs would be
+# copied out and back for every block.
+FILE_FLAGS = {
+    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def hipcc() -> str:
@@ -26,16 +35,31 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libcsa)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every .hip source of csrc/ into one shared library next to this file."""
-    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+def build(verbose: bool = False, src_dir: str | None = None, out: str | None = None) -> str:
+    """Compile every .hip source of csrc/ (or src_dir) and link one shared library (LIB or out)."""
+    src_dir = src_dir or os.path.join(PKG, "csrc")
+    out = out or LIB
+    srcs = sorted(glob.glob(os.path.join(src_dir, "*.hip")))
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", src_dir]
+    with tempfile.TemporaryDirectory(prefix="csa_build_") as tmpdir:
+        def compile_one(src: str) -> str:
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *inc, "-c", src,
+                   "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+            return obj
+
+        with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+            objs = list(ex.map(compile_one, srcs))
+        tmp = out + ".tmp"
+        cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

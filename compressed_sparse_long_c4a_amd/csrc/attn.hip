@@ -284,7 +284,9 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
     const float m_new = fmaxf(m_run, mloc);
     if (m_new == -INFINITY) return;  // every row so far is padding (uniform per wave)
-    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    // v_exp_f32 directly: arguments are <= 0, and 2^-inf = 0 covers an empty running max and
+    // padding rows
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float pv[8];
     float psum = 0.f;
@@ -292,7 +294,7 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
     for (int T = 0; T < 2; ++T) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const float p = (z[T][jj] == -INFINITY) ? 0.f : exp2f(z[T][jj] - m_new);
+        const float p = __builtin_amdgcn_exp2f(z[T][jj] - m_new);
         psum += p;
         pv[4 * T + jj] = p * sc[T][jj];
       }
@@ -434,84 +436,91 @@ struct MergeArgs {
 };
 
 // One wave per (query, head): split weights from the partial statistics, weighted sum of the
-// partial outputs, normalisation and R_t^{-1} on the last rope_dims dims.  The partial rows of
-// the head are first streamed into LDS with every load of a lane in flight at once.
-constexpr int kMergeStage = 8 * 576;  // floats of staged partial rows per wave (8 splits of 576)
+// partial outputs, normalisation and R_t^{-1} on the last rope_dims dims.  Each lane owns the
+// float4 columns lane, lane + 64, lane + 128 of the row; the partial rows of a round of splits
+// are loaded before the statistics are read, so both memory trips overlap.  No LDS, no
+// workgroup barrier.
+constexpr int kMergeCols = 3;   // float4 columns per lane: rows of up to 768 dims
+constexpr int kMergeRound = 8;  // splits whose partial rows are loaded together
 
 __global__ __launch_bounds__(256) void attn_merge(MergeArgs a) {
-  __shared__ float wgt[4][kMaxSplits];
-  __shared__ float cs[4][64], sn[4][64];
-  __shared__ float4 stage[4][kMergeStage / 4];
-  const int qi = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int h = 4 * blockIdx.x + wv;
-  const bool on = h < a.n_heads;  // whole waves only
-  const int t = a.q_pos[qi];
-  const int64_t qbase = (int64_t)qi * a.splits;
-  float M = -INFINITY, L = 0.f;
-  if (on) {
-    if (lane < a.rope_dims / 2) rope_cos_sin(-(double)t, a.rope.theta[lane], cs[wv][lane], sn[wv][lane]);
-    for (int s = lane; s < a.splits; s += 64) M = fmaxf(M, a.part_ml[((qbase + s) * a.hgp + h) * 2]);
-    M = wave_max(M);
-    for (int s = lane; s < a.splits; s += 64) {
-      const float m = a.part_ml[((qbase + s) * a.hgp + h) * 2];
-      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-      wgt[wv][s] = w;
-      L += w * a.part_ml[((qbase + s) * a.hgp + h) * 2 + 1];
-    }
-    L = wave_sum(L);
-    if (a.lse && lane == 0) a.lse[(int64_t)qi * a.n_heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
-  if (!on) return;
-  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const int qi = blockIdx.y, lane = threadIdx.x & 63;
+  const int h = 4 * blockIdx.x + (threadIdx.x >> 6);
+  if (h >= a.n_heads) return;  // whole waves
   const int dim4 = a.dim / 4;
-  const int64_t stride4 = (int64_t)a.hgp * dim4;
+  const int64_t stride4 = (int64_t)a.hgp * dim4;  // float4s between splits of one head
+  const int64_t qbase = (int64_t)qi * a.splits;
   const float4* src = (const float4*)a.part_o + (qbase * a.hgp + h) * dim4;
-  const int half = a.dim / 2;
-  const int rope0 = (a.dim - a.rope_dims) / 2;
-  float acc[6][2];  // this lane's pairs: pp = lane + 64 u (up to 288 pairs)
+  const float* ml = a.part_ml + (qbase * a.hgp + h) * 2;  // split s at ml[s * hgp * 2]
+  const int64_t mls = (int64_t)a.hgp * 2;
+  int col[kMergeCols];
 #pragma unroll
-  for (int u = 0; u < 6; ++u) acc[u][0] = acc[u][1] = 0.f;
-  const int per = kMergeStage / a.dim;  // splits staged at a time
-  constexpr int LPL = kMergeStage / 4 / 64;  // float4 loads per lane per staging round
-  for (int s0 = 0; s0 < a.splits; s0 += per) {
-    const int ns = min(per, a.splits - s0);
-    const int n4 = ns * dim4;
-    float4 v[LPL];
+  for (int j = 0; j < kMergeCols; ++j) col[j] = min(lane + 64 * j, dim4 - 1);
+  float4 v[kMergeRound][kMergeCols];
+  auto load_round = [&](int s0) {  // clamped, unconditional: every load of the round in flight
 #pragma unroll
-    for (int u = 0; u < LPL; ++u) {  // clamped, unconditional: all loads in flight together
-      const int i = min(lane + 64 * u, n4 - 1);
-      const int s = i / dim4, c = i - s * dim4;
-      v[u] = src[(s0 + s) * stride4 + c];
+    for (int u = 0; u < kMergeRound; ++u) {
+      const int64_t sb = (int64_t)min(s0 + u, a.splits - 1) * stride4;
+#pragma unroll
+      for (int j = 0; j < kMergeCols; ++j) v[u][j] = src[sb + col[j]];
+    }
+  };
+  load_round(0);
+  const int t = a.q_pos[qi];
+
+  // M = max_s m_s (log2 units), L = sum_s 2^(m_s - M) l_s
+  float M = -INFINITY;
+  for (int s = lane; s < a.splits; s += 64) M = fmaxf(M, ml[s * mls]);
+  M = wave_max(M);
+  float L = 0.f;
+  for (int s = lane; s < a.splits; s += 64) {
+    const float m = ml[s * mls];
+    L += (m == -INFINITY) ? 0.f : exp2f(m - M) * ml[s * mls + 1];
+  }
+  L = wave_sum(L);
+  if (a.lse && lane == 0) a.lse[(int64_t)qi * a.n_heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+
+  float4 acc[kMergeCols];
+#pragma unroll
+  for (int j = 0; j < kMergeCols; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wl = 0.f;  // weight of split 64 g + lane for the current group g
+  for (int s0 = 0; s0 < a.splits; s0 += kMergeRound) {
+    if (s0 > 0) load_round(s0);
+    if ((s0 & 63) == 0) {
+      const int s = s0 + lane;
+      const float m = s < a.splits ? ml[s * mls] : -INFINITY;
+      wl = (m == -INFINITY) ? 0.f : exp2f(m - M);
     }
 #pragma unroll
-    for (int u = 0; u < LPL; ++u)
-      if (lane + 64 * u < n4) stage[wv][lane + 64 * u] = v[u];
-    const float* st = (const float*)stage[wv];
+    for (int u = 0; u < kMergeRound; ++u) {
+      const float w = s0 + u < a.splits
+          ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), (s0 & 63) + u))
+          : 0.f;
 #pragma unroll
-    for (int u = 0; u < 6; ++u) {
-      const int pp = lane + 64 * u;
-      if (pp < half) {
-        for (int s = 0; s < ns; ++s) {
-          const float w = wgt[wv][s0 + s];
-          acc[u][0] = fmaf(w, st[s * a.dim + 2 * pp], acc[u][0]);
-          acc[u][1] = fmaf(w, st[s * a.dim + 2 * pp + 1], acc[u][1]);
-        }
+      for (int j = 0; j < kMergeCols; ++j) {
+        acc[j].x = fmaf(w, v[u][j].x, acc[j].x);
+        acc[j].y = fmaf(w, v[u][j].y, acc[j].y);
+        acc[j].z = fmaf(w, v[u][j].z, acc[j].z);
+        acc[j].w = fmaf(w, v[u][j].w, acc[j].w);
       }
     }
   }
+
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const int rope0 = a.dim - a.rope_dims;  // first rotated dim
+  float* orow = a.out + ((int64_t)qi * a.n_heads + h) * a.dim;
 #pragma unroll
-  for (int u = 0; u < 6; ++u) {
-    const int pp = lane + 64 * u;
-    if (pp >= half) continue;
-    float v0 = acc[u][0] * inv, v1 = acc[u][1] * inv;
-    if (pp >= rope0) {
-      const float c = cs[wv][pp - rope0], sv = sn[wv][pp - rope0];
-      const float r0 = v0 * c - v1 * sv, r1 = v0 * sv + v1 * c;
-      v0 = r0;
-      v1 = r1;
+  for (int j = 0; j < kMergeCols; ++j) {
+    if (lane + 64 * j >= dim4) continue;
+    const int d = 4 * (lane + 64 * j);
+    float4 r = make_float4(acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv);
+    if (d >= rope0) {  // pairs (d, d+1) and (d+2, d+3) by -t theta_i
+      float c0, s0, c1, s1;
+      rope_cos_sin(-(double)t, a.rope.theta[(d - rope0) / 2], c0, s0);
+      rope_cos_sin(-(double)t, a.rope.theta[(d - rope0) / 2 + 1], c1, s1);
+      r = make_float4(r.x * c0 - r.y * s0, r.x * s0 + r.y * c0, r.z * c1 - r.w * s1, r.z * s1 + r.w * c1);
     }
-    *(float2*)(a.out + ((int64_t)qi * a.n_heads + h) * a.dim + 2 * pp) = make_float2(v0, v1);
+    *(float4*)(orow + d) = r;
   }
 }
 
