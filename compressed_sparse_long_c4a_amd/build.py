@@ -20,12 +20,8 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-# Per-source extra flags.  The attention kernel keeps its MFMA accumulators in ordinary VGPRs:
-# it rescales them with VALU instructions between blocks, and accumulators in AGPRs would be
-# copied out and back for every block.
-FILE_FLAGS = {
-    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-}
+# Per-source extra hipcc flags (none at present).
+FILE_FLAGS: dict[str, list[str]] = {}
 
 
 def hipcc() -> str:

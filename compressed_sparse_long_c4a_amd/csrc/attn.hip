@@ -6,25 +6,27 @@
 // inverse RoPE: with v_n = k_n = R_n k the output must be multiplied by R_m^{-1}, leaving
 // R_{n-m}.  [vLLM-V4] appendix, exact k values: c128a attends to every entry (top-k = 8192).
 //
-// Kernel 1 (attn_partial), grid (row split, 16-head group, query), 4 waves = 2 pairs:
-//   the addresses (and fp8 scales) of the split's rows are resolved once into LDS; each pair
-//   of waves walks its own 32-row blocks (blocks p, p+2, ...) with a private online softmax,
-//   and the two waves of a pair split the row dimensions in halves: each computes the partial
-//   logits over its half, the halves are summed through LDS (one barrier per block, double
-//   buffered), and each wave accumulates the output for its half of the dims.  The two pairs
-//   are merged through LDS at the end; one partial (m, l, O) per head leaves the workgroup.
-//   Per 32-row block (two 16-row tiles T0, T1):
-//     QK : S^T[16 rows x 16 heads] = R_T . Q^T on MFMA 16x16x32 bf16.  Lane (r, g) holds row
-//          r of the tile, 8 dims per k-step, loaded straight from HBM: the row gather and the
-//          MFMA operand layout coincide.
-//     PV : O^T[dims x heads] += R^T . P^T.  The transposed operand R^T is produced on the
-//          matrix cores by a "selection" MFMA, R_T . Sel_h with Sel_h a 0/1 matrix picking 16
-//          of the 32 dims of a k-step: its output layout (4 rows x 1 dim per lane) is exactly
-//          the A layout PV needs, with rows of T0 in slots 0-3 and rows of T1 in slots 4-7.
-//          P^T comes straight from the QK output registers in the same row order.  P is split
-//          into bf16 hi + lo parts (two MFMAs) so PV keeps ~16 significant bits.
+// Kernel 1 (attn_partial), grid (row split, 16-head group, query), four independent waves:
+//   the addresses (and fp8 scales) of the split's rows are resolved once into LDS; wave w then
+//   walks the 16-row blocks w, w + 4, ... of the split with its own online softmax over the
+//   full row width, with no exchange between waves inside the loop.  Per 16-row block:
+//     QK : S^T[16 rows x 16 heads] = R . Q^T on MFMA 16x16x32 bf16.  Lane (r, g) holds row r,
+//          dims 32 ks + 8 g .. +7 of each k-step, loaded straight from HBM (the row gather and
+//          the A-operand layout coincide); Q^T, the B operand, stays in registers.
+//     softmax on the accumulators: lane (h, g) holds rows 4 g .. 4 g + 3 of head h, which is
+//          exactly the B-operand layout of P^T for MFMA 16x16x16, so P needs no data movement.
+//     PV : O^T[16 dims x 16 heads] += V^T . P^T per 16-dim tile.  The block's bf16 rows,
+//          written to the wave's LDS tile during QK, are read back transposed with
+//          ds_read_b64_tr_b16 (4 rows x 1 dim per lane).  P is split into bf16 hi + lo parts,
+//          which fill the two halves of the K = 32 slots of one MFMA 16x16x32 with V^T
+//          repeated in both halves: one MFMA per tile computes V^T (P_hi + P_lo), so PV keeps
+//          ~16 significant bits of P at the cost of a plain bf16 product.
+//   The softmax keeps a per-head reference exponent that moves only when a block's maximum
+//   exceeds it by more than kSlack (2^kSlack bounds P), so the output rescale is rare.
 //   fp8 rows (code * per-row scale): codes widen exactly to bf16; the scale multiplies the
-//   logit and P.  float32 rows / queries are split hi + lo as well.
+//   logit and P.  float32 rows / queries are split hi + lo as well (a second PV pass over the
+//   rows' lo parts).  The four waves' (m, l, O) are merged through LDS at the end, and one
+//   partial (m, l, O) per head leaves the workgroup.
 // Kernel 2 (attn_merge), grid (4-head group, query), one wave per head: combines the splits
 //   by their softmax statistics, normalises, applies R_t^{-1} to the last rope_dims dims
 //   (angles formed and reduced in float64) and writes out / lse.
@@ -40,6 +42,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSplits = 256;
 constexpr int kRowsPerSplit = 1024;  // most rows a workgroup handles (addresses staged in LDS)
+constexpr float kSlack = 8.0f;       // log2 headroom of P above the softmax reference
 
 struct Args {
   int batch, n_heads, ratio, k, has_topk, window, n_max, rows_per_split, splits, hgp;
@@ -61,38 +64,38 @@ __device__ __forceinline__ bf16x8 f32x8_to_bf16(const float* x) {
 }
 
 
-// Half a row (HKS k-steps of 32 dims) of one 16-row tile as seen by lane (r, g): the 8 dims
-// 32 ks + 8 g .. +7 of row r for each of its k-steps.
-template <int DT, int HKS>
-struct HalfTile {
-  static constexpr int NREG = DT == CSA_FP8_E4M3 ? HKS : (DT == CSA_BF16 ? HKS : 1);
+// One 16-row block as lane (r, g) holds it: dims 32 ks + 8 g .. +7 of row r for each of the
+// NKS k-steps.
+template <int DT, int NKS>
+struct RowTile {
+  static constexpr int NREG = DT == CSA_F32 ? 1 : NKS;
   typedef typename std::conditional<DT == CSA_FP8_E4M3, uint2, uint4>::type Word;
   Word d[NREG];
   const float* f32row;  // float32 rows are re-read per k-step instead of held in registers
 
   // `row` is always a loadable row (padding rows point at a safe row and are masked later).
-  __device__ __forceinline__ void load(const char* row, int ks0, int g) {
+  __device__ __forceinline__ void load(const char* row, int g) {
     if constexpr (DT == CSA_F32) {
-      f32row = (const float*)row + 32 * ks0 + 8 * g;
+      f32row = (const float*)row + 8 * g;
     } else {
       constexpr int ESZ = DT == CSA_BF16 ? 2 : 1;
-      const char* base = row + (32 * ks0 + 8 * g) * ESZ;
+      const char* base = row + 8 * g * ESZ;
 #pragma unroll
-      for (int kk = 0; kk < HKS; ++kk) d[kk] = *(const Word*)(base + 32 * kk * ESZ);
+      for (int ks = 0; ks < NKS; ++ks) d[ks] = *(const Word*)(base + 32 * ks * ESZ);
     }
   }
 
-  // bf16 operand for local k-step kk (exact for bf16 and fp8 rows); lo = residual of float32 rows.
-  __device__ __forceinline__ void frag(int kk, bf16x8& hi, bf16x8& lo) const {
+  // bf16 operand for k-step ks (exact for bf16 and fp8 rows); lo = residual of float32 rows.
+  __device__ __forceinline__ void frag(int ks, bf16x8& hi, bf16x8& lo) const {
     if constexpr (DT == CSA_BF16) {
-      hi = __builtin_bit_cast(bf16x8, d[kk]);
+      hi = __builtin_bit_cast(bf16x8, d[ks]);
     } else if constexpr (DT == CSA_FP8_E4M3) {
-      hi = fp8x8_to_bf16x8(d[kk].x, d[kk].y);
+      hi = fp8x8_to_bf16x8(d[ks].x, d[ks].y);
     } else {
       float x[8];
       {
-        const float4 a = *(const float4*)(f32row + 32 * kk);
-        const float4 b = *(const float4*)(f32row + 32 * kk + 4);
+        const float4 a = *(const float4*)(f32row + 32 * ks);
+        const float4 b = *(const float4*)(f32row + 32 * ks + 4);
         x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
         x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
       }
@@ -105,30 +108,31 @@ struct HalfTile {
   }
 };
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
 template <int DT, int QDT, int DIM>
 __global__ __launch_bounds__(256) void attn_partial(Args a) {
-  constexpr int NKS = DIM / 32;
-  constexpr int HKS = NKS / 2;  // k-steps per wave of a pair
+  constexpr int NKS = DIM / 32;  // QK k-steps
+  constexpr int NDT = DIM / 16;  // PV dim tiles
   constexpr bool ROW_LO = DT == CSA_F32;
   constexpr bool Q_LO = QDT == CSA_F32;
+  constexpr int ESZ = DT == CSA_F32 ? 4 : (DT == CSA_BF16 ? 2 : 1);
   // byte offset of each row from the main cache's row base (window rows included), so every
   // row address is derived from a kernel argument and the loads are known to be global
   __shared__ int64_t off_sh[kRowsPerSplit];
   __shared__ float scale_sh[kRowsPerSplit];  // row scale (1 for bf16/f32 rows); 0 marks padding
-  __shared__ float xs[2][4][64][8];  // partial logits, [buffer][wave][lane][T*4 + jj]
-  // bf16 / fp8 rows: each wave's bf16 half-rows of the current block (row stride padded by 16 B),
-  // read back transposed for PV; the merge at the end reuses the space.  float32 rows use the
-  // selection MFMA instead and need only the merge buffer.
-  constexpr int TROW = (DIM / 2) * 2 + 16;          // bytes per half-row in LDS
-  constexpr int TILE_BYTES = ROW_LO ? 0 : 4 * 32 * TROW;
-  constexpr int MERGE_BYTES = 16 * (DIM + 4) * 4;
+  // each wave's bf16 rows of its current block (row stride padded by 16 B: the 16 rows of a
+  // b128 write then start in distinct bank quads); the final merge reuses the space as two
+  // float32 [16][DIM + 4] buffers
+  constexpr int TROW = DIM * 2 + 16;
+  constexpr int TILE_BYTES = 4 * 16 * TROW;
+  constexpr int MERGE_BYTES = 2 * 16 * (DIM + 4) * 4;
   __shared__ __attribute__((aligned(16))) char tile_sh[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
-  float (*o_sh)[DIM + 4] = reinterpret_cast<float (*)[DIM + 4]>(tile_sh);
-  __shared__ float ml_sh[2][16][2];
+  __shared__ float ml_sh[4][16][2];
 
   const int s = blockIdx.x, hg = blockIdx.y, qi = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int pair = wv >> 1, half = wv & 1;
   const int ln = lane & 15, lg = lane >> 4;
   const int b = seq_of_wave(a.cu_q, a.batch, qi);
   const int t = a.q_pos[qi];
@@ -139,21 +143,21 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
   const int r_begin = s * a.rows_per_split;
   // a query without any visible row (no window and no entry yet) attends to nothing
   const int nrows = (n_w > 0 || n_vis > 0) ? max(0, min(a.rows_per_split, n_rows - r_begin)) : 0;
+  const int nrows16 = (nrows + 15) & ~15;  // rows_per_split is a multiple of 32
   const int H = a.n_heads;
-  const int ks0 = half * HKS;
-  constexpr int ESZ = DT == CSA_F32 ? 4 : (DT == CSA_BF16 ? 2 : 1);
+  const char* kvbase = (const char*)a.kv.rows;
 
   // Q^T as the B operand: lane (head ln, group lg) holds q[h][32 ks + 8 lg + 0..7].
-  bf16x8 qb[HKS], qb_lo[Q_LO ? HKS : 1];
+  bf16x8 qb[NKS], qb_lo[Q_LO ? NKS : 1];
   {
     const int h = 16 * hg + ln;
 #pragma unroll
-    for (int kk = 0; kk < HKS; ++kk) {
-      const int d0 = 32 * (ks0 + kk) + 8 * lg;
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int d0 = 32 * ks + 8 * lg;
       if constexpr (QDT == CSA_BF16) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (h < H) v = *(const uint4*)((const uint16_t*)a.q + ((int64_t)qi * H + h) * DIM + d0);
-        qb[kk] = __builtin_bit_cast(bf16x8, v);
+        qb[ks] = __builtin_bit_cast(bf16x8, v);
       } else {
         float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (h < H) {
@@ -161,17 +165,18 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) x[i] = src[i];
         }
-        qb[kk] = f32x8_to_bf16(x);
+        qb[ks] = f32x8_to_bf16(x);
         float r[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r[i] = x[i] - (float)qb[kk][i];
-        if constexpr (Q_LO) qb_lo[kk] = f32x8_to_bf16(r);
+        for (int i = 0; i < 8; ++i) r[i] = x[i] - (float)qb[ks][i];
+        if constexpr (Q_LO) qb_lo[ks] = f32x8_to_bf16(r);
       }
     }
   }
-  // ---- resolve the split's rows once: address and scale, padding rows -> a safe row.
-  // Each thread owns up to kRowsPerSplit / 256 rows; the list reads, then the block-table
-  // reads, then the scale reads of all its rows are issued together.
+  // ---- resolve the split's rows once: offset and scale; padding rows (up to the next multiple
+  // of 16) -> a safe row with scale 0.  Each thread owns up to kRowsPerSplit / 256 rows; the
+  // list reads, then the block-table reads, then the scale reads of all its rows are issued
+  // together.
   if (nrows > 0) {  // (all staged positions are then rows of this query)
     constexpr int RPT = kRowsPerSplit / 256;
     const int64_t swa_off = (int64_t)((uintptr_t)a.swa.rows - (uintptr_t)a.kv.rows);
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
       const int i = tid + 256 * u;
-      if (i < nrows) {
+      if (i < nrows16) {
         const int64_t base = is_kv[u] ? 0 : swa_off;
         float sc = 0.f;
         if (ok[u]) {
@@ -211,198 +216,149 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
     }
   }
 
-  // Sel_h as the B operand (float32 rows only): slot (lg, j) -> output column 8 (lg - 2h) + j
-  // for lg in {2h, 2h+1}.
-  bf16x8 sel[2];
+  f32x4 o[NDT];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      sel[hh][j] = (__bf16)((lg == 2 * hh + (ln >> 3) && j == (ln & 7)) ? 1.0f : 0.0f);
-  }
-
-  f32x4 o[HKS][2];
-#pragma unroll
-  for (int kk = 0; kk < HKS; ++kk) {
-    o[kk][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    o[kk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_run = 0.f;  // per head: reference exponent (log2 units), sum of P
   __syncthreads();
 
-  const int nblocks = (nrows + 31) >> 5;
-  const int iters = (nblocks + 1) >> 1;
-  // Row loads are unconditional (clamped to the split's last row, which is always loadable):
-  // the wait counters then keep the next block in flight while this one is computed.
-  auto load_block = [&](int it, HalfTile<DT, HKS>* tl) {
-    const int bi = 2 * min(it, iters - 1) + pair;
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-      tl[T].load((const char*)a.kv.rows + off_sh[min(32 * bi + 16 * T + ln, nrows - 1)], ks0, lg);
+  const int nblk = nrows16 >> 4;
+  const int my_n = nblk > wv ? (nblk - wv + 3) >> 2 : 0;  // this wave's blocks: wv, wv + 4, ...
+  char* wtile = tile_sh + wv * 16 * TROW;
+  lds_char* wtile3 = (lds_char*)wtile;
+  // Row loads are unconditional (clamped to the wave's last block, always loadable): the wait
+  // counters then keep the next block in flight while this one is computed.
+  auto load_block = [&](int i, RowTile<DT, NKS>& tl) {
+    const int bi = wv + 4 * min(i, my_n - 1);
+    tl.load(kvbase + off_sh[16 * bi + ln], lg);
+  };
+  // V^T fragment of dim tile dt from the wave's LDS tile: lane (ln, lg) of a 16-lane group
+  // supplies row 4 lg + ln / 4, dims 16 dt + 4 (ln % 4) .. +3; the transposing read returns
+  // rows 4 lg .. 4 lg + 3 of dim 16 dt + ln.
+  auto vt_frag = [&](int dt) -> s16x4 {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(wtile3 + (4 * lg + (ln >> 2)) * TROW +
+                                                   2 * (16 * dt + 4 * (ln & 3))));
   };
 
-  auto process_block = [&](int it, const HalfTile<DT, HKS>* tile, int buf) {
-    const int bi = 2 * it + pair;
-    const bool active = bi < nblocks;
-    const int row0 = 32 * bi;
-    // partial S^T = R_half . Q_half^T
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  auto process_block = [&](int i, const RowTile<DT, NKS>& tile) {
+    const int row0 = 16 * (wv + 4 * i);
+    // S^T = R . Q^T; the bf16 rows also go to the wave's LDS tile for PV
+    f32x4 sacc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // two chains (even / odd ks)
 #pragma unroll
-    for (int kk = 0; kk < HKS; ++kk) {
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        bf16x8 rh, rl;
-        tile[T].frag(kk, rh, rl);
-        if constexpr (!ROW_LO)
-          *(bf16x8*)(tile_sh + wv * 32 * TROW + (16 * T + ln) * TROW + 2 * (32 * kk + 8 * lg)) = rh;
-        sacc[T] = mfma16x16x32(rh, qb[kk], sacc[T]);
-        if constexpr (Q_LO) sacc[T] = mfma16x16x32(rh, qb_lo[kk], sacc[T]);
-        if constexpr (ROW_LO) sacc[T] = mfma16x16x32(rl, qb[kk], sacc[T]);
-      }
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 rh, rl;
+      tile.frag(ks, rh, rl);
+      *(bf16x8*)(wtile + ln * TROW + 2 * (32 * ks + 8 * lg)) = rh;
+      f32x4& acc = sacc2[ks & 1];
+      acc = mfma16x16x32(rh, qb[ks], acc);
+      if constexpr (Q_LO) acc = mfma16x16x32(rh, qb_lo[ks], acc);
+      if constexpr (ROW_LO) acc = mfma16x16x32(rl, qb[ks], acc);
     }
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) xs[buf][wv][lane][4 * T + jj] = sacc[T][jj];
-    barrier_lds();  // the next block's row loads stay in flight
-    float z[2][4], sc[2][4];
+    const f32x4 sacc = sacc2[0] + sacc2[1];
+    // online softmax over the block's rows 4 lg + j (scale 0 marks padding)
+    const float4 rs4 = *(const float4*)&scale_sh[row0 + 4 * lg];
+    const float rs[4] = {rs4.x, rs4.y, rs4.z, rs4.w};
+    float z[4];
     float mloc = -INFINITY;
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float sum = xs[buf][2 * pair][lane][4 * T + jj] + xs[buf][2 * pair + 1][lane][4 * T + jj];
-        const int r = row0 + 16 * T + 4 * lg + jj;
-        const float rs = (active && r < nrows) ? scale_sh[r] : 0.f;
-        sc[T][jj] = rs;
-        z[T][jj] = rs != 0.f ? sum * rs * a.sm_scale2 : -INFINITY;
-        mloc = fmaxf(mloc, z[T][jj]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      z[j] = rs[j] != 0.f ? sacc[j] * rs[j] * a.sm_scale2 : -INFINITY;
+      mloc = fmaxf(mloc, z[j]);
     }
-    if (!active) return;
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-    const float m_new = fmaxf(m_run, mloc);
-    if (m_new == -INFINITY) return;  // every row so far is padding (uniform per wave)
-    // v_exp_f32 directly: arguments are <= 0, and 2^-inf = 0 covers an empty running max and
-    // padding rows
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float pv[8];
-    float psum = 0.f;
+    // move a head's reference only when this block's maximum exceeds it by more than kSlack
+    // (always when it has none yet); P = 2^(z - m_ref) <= 2^kSlack stays far from overflow
+    const bool move = mloc > m_ref + kSlack;
+    if (__ballot(move)) {
+      const float m_new = move ? mloc : m_ref;
+      // v_exp_f32 directly: the argument is <= 0, and 2^-inf = 0 covers an empty reference
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float p = __builtin_amdgcn_exp2f(z[T][jj] - m_new);
-        psum += p;
-        pv[4 * T + jj] = p * sc[T][jj];
-      }
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
     }
-    l_run = l_run * alpha + psum;
-    if (__ballot(alpha != 1.0f)) {  // rescale only when some head's running max moved
+    if (m_ref == -INFINITY) return;  // every row so far is padding (uniform per wave)
+    float pv[4], psum = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < HKS; ++kk) {
-        o[kk][0] *= alpha;
-        o[kk][1] *= alpha;
-      }
+    for (int j = 0; j < 4; ++j) {
+      const float p = __builtin_amdgcn_exp2f(z[j] - m_ref);  // padding rows: 2^-inf = 0
+      psum += p;
+      pv[j] = p * rs[j];
     }
-    bf16x8 p_hi = f32x8_to_bf16(pv), p_lo;
-    {
-      float r[8];
+    l_run += psum;
+    // B operand of PV: k-slots 0-3 of each lane group hold P_hi of its rows 4 lg + j, slots 4-7
+    // hold P_lo of the same rows
+    bf16x8 pb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) r[i] = pv[i] - (float)p_hi[i];
-      p_lo = f32x8_to_bf16(r);
+    for (int j = 0; j < 4; ++j) {
+      const __bf16 hi = (__bf16)pv[j];
+      pb[j] = hi;
+      pb[4 + j] = (__bf16)(pv[j] - (float)hi);
     }
-    if constexpr (!ROW_LO) {
-      // O^T += R^T . P^T over this wave's half of the dims.  The A operand (16 dims x 8 rows per
-      // lane) is read transposed from the wave's LDS tile: two ds_read_b64_tr_b16 per fragment,
-      // the first over rows 4 lg .. 4 lg + 3 of T0 and the second over the same rows of T1,
-      // which is the row order of P^T in the softmax registers.
-      __attribute__((address_space(3))) char* tbase =
-          (__attribute__((address_space(3))) char*)(tile_sh + wv * 32 * TROW);
-      typedef short s16x4 __attribute__((ext_vector_type(4)));
+    // O^T += [V^T | V^T] . [P_hi ; P_lo]
 #pragma unroll
-      for (int kk = 0; kk < HKS; ++kk) {
+    for (int dt = 0; dt < NDT; ++dt) {
+      const s16x4 at = vt_frag(dt);
+      o[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(at, at, 0, 1, 2, 3, 0, 1, 2, 3)), pb, o[dt]);
+    }
+    if constexpr (ROW_LO) {  // float32 rows: V_lo P_hi through the same tile
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int col = 2 * (32 * kk + 16 * hh + 4 * (ln & 3));
-          const int r0 = 4 * lg + (ln >> 2);
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(tbase + r0 * TROW + col));
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(tbase + (16 + r0) * TROW + col));
-          const bf16x8 at = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[kk][hh] = mfma16x16x32(at, p_hi, o[kk][hh]);
-          o[kk][hh] = mfma16x16x32(at, p_lo, o[kk][hh]);
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        bf16x8 rh, rl;
+        tile.frag(ks, rh, rl);
+        *(bf16x8*)(wtile + ln * TROW + 2 * (32 * ks + 8 * lg)) = rl;
       }
-    } else {
-      // float32 rows: R^T made by the selection MFMA from the register tiles (hi and lo parts)
+      bf16x8 ph = pb;
 #pragma unroll
-      for (int kk = 0; kk < HKS; ++kk) {
-        bf16x8 r0h, r0l, r1h, r1l;
-        tile[0].frag(kk, r0h, r0l);
-        tile[1].frag(kk, r1h, r1l);
+      for (int j = 0; j < 4; ++j) ph[4 + j] = (__bf16)0.0f;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-          const f32x4 c0 = mfma16x16x32(r0h, sel[hh], zero);
-          const f32x4 c1 = mfma16x16x32(r1h, sel[hh], zero);
-          const f32x4 d0 = mfma16x16x32(r0l, sel[hh], zero);
-          const f32x4 d1 = mfma16x16x32(r1l, sel[hh], zero);
-          bf16x8 at, al;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            at[jj] = (__bf16)c0[jj];
-            at[4 + jj] = (__bf16)c1[jj];
-            al[jj] = (__bf16)d0[jj];
-            al[4 + jj] = (__bf16)d1[jj];
-          }
-          o[kk][hh] = mfma16x16x32(at, p_hi, o[kk][hh]);
-          o[kk][hh] = mfma16x16x32(at, p_lo, o[kk][hh]);
-          o[kk][hh] = mfma16x16x32(al, p_hi, o[kk][hh]);
-        }
+      for (int dt = 0; dt < NDT; ++dt) {
+        const s16x4 at = vt_frag(dt);
+        o[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(at, at, 0, 1, 2, 3, 0, 1, 2, 3)), ph, o[dt]);
       }
     }
   };
 
-  if (iters > 0) {
-    HalfTile<DT, HKS> ta[2], tb[2];
+  if (my_n > 0) {
+    RowTile<DT, NKS> ta, tb;
     load_block(0, ta);
-    for (int it = 0; it < iters; it += 2) {
-      load_block(it + 1, tb);
-      process_block(it, ta, 0);
-      load_block(it + 2, ta);
-      if (it + 1 < iters) process_block(it + 1, tb, 1);
+    int i = 0;
+    for (; i + 1 < my_n; i += 2) {  // no branch inside: the accumulators stay in place
+      load_block(i + 1, tb);
+      process_block(i, ta);
+      load_block(i + 2, ta);
+      process_block(i + 1, tb);
     }
+    if (i < my_n) process_block(i, ta);
   }
 
-  // ---- merge the two pairs through LDS (the two waves of a pair hold identical m and l)
-  __syncthreads();  // the merge buffer reuses the row tiles
+  // ---- merge the four waves through LDS: per head M = max_w m_w, f_w = 2^(m_w - M)
   float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
-  if (half == 0 && lg == 0) {
-    ml_sh[pair][ln][0] = m_run;
-    ml_sh[pair][ln][1] = l_tot;
+  if (lg == 0) {
+    ml_sh[wv][ln][0] = m_ref;
+    ml_sh[wv][ln][1] = l_tot;
   }
-  __syncthreads();
-  const float M = fmaxf(ml_sh[0][ln][0], ml_sh[1][ln][0]);
-  const float f = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);
-  for (int p = 1; p >= 0; --p) {
-    if (pair == p) {
+  __syncthreads();  // also: every wave is done with its tile (the merge buffers alias them)
+  const float M = fmaxf(fmaxf(ml_sh[0][ln][0], ml_sh[1][ln][0]), fmaxf(ml_sh[2][ln][0], ml_sh[3][ln][0]));
+  const float f = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - M);
+  float (*mb)[16][DIM + 4] = reinterpret_cast<float (*)[16][DIM + 4]>(tile_sh);
+  // waves 0 and 1 store f O into buffers 0 and 1, then waves 2 and 3 add theirs
 #pragma unroll
-      for (int kk = 0; kk < HKS; ++kk) {
+  for (int round = 0; round < 2; ++round) {
+    if ((wv >> 1) == round) {
+      float* dst = &mb[wv & 1][ln][4 * lg];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            // output column m of the selection is dim 32 ks + 16 hh + m
-            const int d = 32 * (ks0 + kk) + 16 * hh + 4 * lg + jj;
-            const float v = f * o[kk][hh][jj];
-            if (p == 1) o_sh[ln][d] = v; else o_sh[ln][d] += v;
-          }
+      for (int dt = 0; dt < NDT; ++dt) {
+        float4 v = make_float4(f * o[dt][0], f * o[dt][1], f * o[dt][2], f * o[dt][3]);
+        if (round == 1) {
+          const float4 w = *(const float4*)(dst + 16 * dt);
+          v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
         }
+        *(float4*)(dst + 16 * dt) = v;
       }
     }
     __syncthreads();
@@ -410,16 +366,18 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
   const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg;
   for (int i = tid; i < 16 * DIM / 4; i += 256) {
     const int h = i / (DIM / 4), d = 4 * (i - h * (DIM / 4));
-    *(float4*)(a.part_o + (pbase + h) * DIM + d) =
-        make_float4(o_sh[h][d], o_sh[h][d + 1], o_sh[h][d + 2], o_sh[h][d + 3]);
+    const float4 x = *(const float4*)&mb[0][h][d], y = *(const float4*)&mb[1][h][d];
+    *(float4*)(a.part_o + (pbase + h) * DIM + d) = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
   }
   if (tid < 16) {
     const int h = tid;
-    const float m0 = ml_sh[0][h][0], m1 = ml_sh[1][h][0];
-    const float Mh = fmaxf(m0, m1);
+    float Mh = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) Mh = fmaxf(Mh, ml_sh[w][h][0]);
     float L = 0.f;
-    if (m0 != -INFINITY) L += exp2f(m0 - Mh) * ml_sh[0][h][1];
-    if (m1 != -INFINITY) L += exp2f(m1 - Mh) * ml_sh[1][h][1];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (ml_sh[w][h][0] != -INFINITY) L += exp2f(ml_sh[w][h][0] - Mh) * ml_sh[w][h][1];
     a.part_ml[(pbase + h) * 2 + 0] = Mh;
     a.part_ml[(pbase + h) * 2 + 1] = L;
   }
