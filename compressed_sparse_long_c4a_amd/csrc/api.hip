@@ -78,7 +78,8 @@ size_t csa_index_workspace_size(int total_q, int max_context, int k) {
 
 static int index_check(int batch, const int32_t* cu_q, const int32_t* q_pos, int total_q,
                        int max_context, int k, size_t ws_bytes, const void* ws) {
-  if (batch <= 0 || total_q < 0 || !cu_q || !q_pos) return CSA_EINVAL;
+  if (batch <= 0 || total_q < 0 || !cu_q) return CSA_EINVAL;
+  if (total_q > 0 && !q_pos) return CSA_EINVAL;
   if (max_context <= 0 || max_context > kMaxContextIndex) return CSA_EINVAL;
   if (k <= 0 || k > 65536) return CSA_EINVAL;
   if (total_q > 0 && (!ws || ws_bytes < csa::index_workspace_bytes(total_q, max_context, k)))
@@ -86,9 +87,10 @@ static int index_check(int batch, const int32_t* cu_q, const int32_t* q_pos, int
   return CSA_OK;
 }
 
-static int score_check(const void* q_idx, int q_dtype, int n_heads_idx, const float* head_w,
-                       const csa_cache* idx_cache) {
-  if (!q_idx || !head_w) return CSA_EINVAL;
+// (q_idx and head_w may be NULL when total_q = 0: zero-length arrays are never read)
+static int score_check(int total_q, const void* q_idx, int q_dtype, int n_heads_idx,
+                       const float* head_w, const csa_cache* idx_cache) {
+  if (total_q > 0 && (!q_idx || !head_w)) return CSA_EINVAL;
   if (!cache_ok(idx_cache, 64, 128)) return CSA_EINVAL;
   if (q_dtype == CSA_BF16) {
     if (n_heads_idx < 1 || n_heads_idx > 64) return CSA_ENOTSUP;
@@ -107,7 +109,7 @@ int csa_index_score(csa_stream_t stream, int batch, const int32_t* cu_q, const i
                     size_t workspace_bytes) {
   int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace);
   if (st != CSA_OK) return st;
-  st = score_check(q_idx, q_dtype, n_heads_idx, head_w, idx_cache);
+  st = score_check(total_q, q_idx, q_dtype, n_heads_idx, head_w, idx_cache);
   if (st != CSA_OK || total_q == 0) return st;
   csa::IndexLaunch L{batch, cu_q, q_pos, total_q, max_context, q_idx, q_dtype, n_heads_idx,
                      head_w, idx_cache, k};
@@ -120,8 +122,8 @@ int csa_index_select(csa_stream_t stream, int batch, const int32_t* cu_q, const 
                      void* workspace, size_t workspace_bytes) {
   int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace);
   if (st != CSA_OK) return st;
-  if (!topk_idx) return CSA_EINVAL;
   if (total_q == 0) return CSA_OK;
+  if (!topk_idx) return CSA_EINVAL;
   csa::IndexLaunch L{batch, cu_q, q_pos, total_q, max_context, nullptr, 0, 0, nullptr, nullptr, k};
   const csa::IndexWorkspace ws = csa::index_workspace_carve(workspace, total_q, max_context, k);
   return hip_status(csa::launch_index_select(L, topk_idx, topk_score, ws, (hipStream_t)stream));
@@ -133,10 +135,10 @@ int csa_index_topk(csa_stream_t stream, int batch, const int32_t* cu_q, const in
                    float* topk_score, void* workspace, size_t workspace_bytes) {
   int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace);
   if (st != CSA_OK) return st;
-  st = score_check(q_idx, q_dtype, n_heads_idx, head_w, idx_cache);
+  st = score_check(total_q, q_idx, q_dtype, n_heads_idx, head_w, idx_cache);
   if (st != CSA_OK) return st;
-  if (!topk_idx) return CSA_EINVAL;
   if (total_q == 0) return CSA_OK;
+  if (!topk_idx) return CSA_EINVAL;
   csa::IndexLaunch L{batch, cu_q, q_pos, total_q, max_context, q_idx, q_dtype, n_heads_idx,
                      head_w, idx_cache, k};
   const csa::IndexWorkspace ws = csa::index_workspace_carve(workspace, total_q, max_context, k);
@@ -162,7 +164,8 @@ int csa_sparse_attn_decode(csa_stream_t stream, int batch, const int32_t* cu_q,
                            float softmax_scale, float rope_base, int rope_dims, float* out,
                            float* lse, void* workspace, size_t workspace_bytes) {
   if (ratio != 4 && ratio != 128) return CSA_EINVAL;
-  if (batch <= 0 || total_q < 0 || !cu_q || !q_pos || !q || !out) return CSA_EINVAL;
+  if (batch <= 0 || total_q < 0 || !cu_q) return CSA_EINVAL;
+  if (total_q > 0 && (!q_pos || !q || !out)) return CSA_EINVAL;  // zero-length arrays may be NULL
   if (max_context <= 0 || window < 0 || window > 4096) return CSA_EINVAL;
   if (topk_idx && (k <= 0 || k > 65536)) return CSA_EINVAL;
   if (!cache_ok(kv, 256 / ratio, -1) || !cache_ok(swa, 256, kv->dim)) return CSA_EINVAL;

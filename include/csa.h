@@ -29,6 +29,8 @@
  *     behaviour, except where a call states how it treats them.
  *   - The functions keep no state between calls and may be called from
  *     several threads on different streams.
+ *   - An array of length zero (total_q = 0, total_new = 0, ...) may be passed
+ *     as NULL; a call with no work returns CSA_OK without launching.
  */
 #ifndef CSA_H
 #define CSA_H

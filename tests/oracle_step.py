@@ -85,12 +85,22 @@ def run_oracle(cfg, d: dict, queries=None, topk_override=None, caches: dict | No
             ids = res["topk"][i]
         else:
             ids = None if "topk" not in d else d["topk"][i].numpy()
-        b, t = int(seq[i]), q_pos[i]
-        rows = attention.gather_rows(kv, swa, b, t, cfg.ratio, ids, cfg.window)
-        o, l = attention.attend(q[i], rows, cfg.softmax_scale)
-        res["out"][i] = inverse_rope(o, t, cfg.rope_base, 64)
-        res["lse"][i] = l
+        res["out"][i], res["lse"][i] = _attend(cfg, d, kv, swa, int(seq[i]), q_pos[i], q[i], ids)
     return res
+
+
+def _attend(cfg, d, kv, swa, b, t, q_i, ids):
+    rows = attention.gather_rows(kv, swa, b, t, cfg.ratio, ids, cfg.window)
+    o, l = attention.attend(q_i, rows, cfg.softmax_scale)
+    return inverse_rope(o, t, cfg.rope_base, 64), l
+
+
+def attend_query(cfg, d: dict, res: dict, i: int, ids):
+    """Oracle attention of query i over the entry list ``ids`` (caches as left by run_oracle)."""
+    cu_q = d["cu_q"].tolist()
+    b = int(np.searchsorted(np.array(cu_q), i, side="right") - 1)
+    q = formats.decode_stored(np_rows(d["q"][i]), DT[d["q"].dtype])
+    return _attend(cfg, d, res["kv"], res["swa"], b, int(d["q_pos"][i]), q, ids)
 
 
 # ------------------------------------------------------------------ comparisons
@@ -154,9 +164,16 @@ def topk_acceptable(gpu_ids: np.ndarray, scores: np.ndarray, k: int, rel: float 
 
 
 def allclose_out(gpu: np.ndarray, ref: np.ndarray, atol: float = 1e-5, rtol: float = 2e-3):
-    err = np.abs(gpu - ref)
-    tol = atol + rtol * np.abs(ref)
-    return bool(np.all(err <= tol)), float(np.max(err / tol))
+    """|gpu - ref| <= atol + rtol |ref| elementwise; equal values (e.g. both -inf for the lse of a
+    query without rows) pass, an infinity on one side only fails."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    same = gpu == ref
+    with np.errstate(invalid="ignore"):
+        err = np.where(same, 0.0, np.abs(gpu - ref))
+        tol = atol + rtol * np.where(np.isfinite(ref), np.abs(ref), 0.0)
+    ratio = np.where(np.isnan(err), np.inf, err / tol)
+    return bool(np.all(ratio <= 1.0)), float(np.max(ratio)) if ratio.size else 0.0
 
 
 def decode_gpu_rows(rows: torch.Tensor, scales, blocks_slots):

@@ -101,27 +101,39 @@ def compare(cfg, d: dict, step, ores: dict) -> dict:
     if "attn" in cfg.stages:
         out = step.out.cpu().numpy()
         lse = None if step.lse is None else step.lse.cpu().numpy()
+        topk_gpu = step.topk.cpu().numpy() if "index" in cfg.stages else None
         for i in ores["queries"]:
+            ref_o, ref_l = ores["out"][i], ores["lse"][i]
             if same_set.get(i, True) is False:
-                continue
-            ok, r = O.allclose_out(out[i], ores["out"][i])
+                # a near tie (accepted above): the oracle attends over the GPU's own selection
+                ref_o, ref_l = O.attend_query(cfg, d, ores, i, topk_gpu[i])
+            ok, r = O.allclose_out(out[i], ref_o)
             note("out", ok, r, i)
             if lse is not None:
-                ok, r = O.allclose_out(lse[i], ores["lse"][i], 1e-5, 2e-3)
+                ok, r = O.allclose_out(lse[i], ref_l, 1e-5, 2e-3)
                 note("lse", ok, r, i)
     return rep
 
 
-def run_step_parity(cfg, queries=None, verbose: bool = False, prep=None, overlap: bool = False) -> dict:
-    """Draw inputs, run the GPU step (optionally with the two-stream schedule) and the oracle,
-    compare.  Returns the report."""
+def run_step_parity(cfg, queries=None, verbose: bool = False, prep=None, overlap: bool = False,
+                    fast: bool = False, with_scores: bool = True) -> dict:
+    """Draw inputs, run the GPU step and the oracle, compare.  Returns the report.
+
+    overlap: the two-stream schedule.  fast: the launch sequence the benchmark times (one
+    run(), then the step again through the pre-marshalled calls; a step is idempotent because
+    every cache row it writes is a function of rows it does not write).  with_scores: also
+    request the top-k scores (the benchmark does not).  prep(d) may edit the drawn inputs."""
     from compressed_sparse_long_c4a_amd import pipeline
     d = inputs.draw(cfg)
     if prep is not None:
         prep(d)
     g = pipeline.to_device(d)
-    step = pipeline.Step(cfg, g)
+    step = pipeline.Step(cfg, g, with_scores=with_scores)
     step.run_overlapped() if overlap else step.run()
+    if fast:
+        torch.cuda.synchronize()
+        step.lse = None
+        step.fast(g)
     torch.cuda.synchronize()
     ores = O.run_oracle(cfg, d, queries=queries)
     rep = compare(cfg, d, step, ores)

@@ -1,0 +1,135 @@
+"""Edge cases of the HIP path against the oracle: empty calls, the first positions of a sequence
+(no entries yet, zero-padded entry 0, a one-row window), ragged batches, a zero window, exact
+score ties, selections too large for the select kernel's LDS, and the largest k the ABI accepts.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from tests import pipeline_check as P
+from workloads import configs as C, inputs
+
+D = dataclasses.replace
+
+# c4a decode of 8 sequences at the very start of their context: t = 0..4, 7, 8, 129 gives
+# 0, 0, 0, 1, 1, 2, 2 and 32 visible entries (no entry, entry 0 with its zero-padded slots, k >= n
+# and k < n); the window holds t + 1 rows.
+EARLY_C4A = D(C.C4A_1M_B4_FP8, name="c4a_early_positions", ctx_after=(1, 2, 3, 4, 5, 8, 9, 130),
+              n_heads=16, k=8)
+# c128a: entries complete at positions 127 and 255 only.
+EARLY_C128A = D(C.C128A_1M_B8, name="c128a_early_positions", ctx_after=(1, 127, 128, 129, 256, 300),
+                n_heads=16)
+# a ragged prefill batch: a sequence starting at position 0, one with three new tokens, one
+# without queries, one whose chunk spans a block edge; every query sees its own chunk causally.
+RAGGED = D(C.C4A_PREFILL_64K, name="c4a_ragged_prefill", ctx_after=(700, 1500, 300, 290),
+           new_tokens=(300, 3, 300, 40), q_per_seq=(5, 3, 0, 40), k=64, n_heads=32)
+# attention over top-k entries only (window 0); t = 2 has no row at all (out 0, lse -inf).
+NO_WINDOW = D(C.C4A_1M_B4_FP8, name="c4a_window0", ctx_after=(3, 4097, 9000), n_heads=16, k=256,
+              window=0, stages=("index", "attn"))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("cfg", [EARLY_C4A, EARLY_C128A, RAGGED, NO_WINDOW], ids=lambda c: c.name)
+def test_edge_step_parity(gpu, cfg):
+    print(f"case {cfg.name}: {cfg}", flush=True)
+    rep = P.run_step_parity(cfg, verbose=True)
+    assert not rep["fail"], rep["fail"][:10]
+
+
+def _zero_index_keys(d):
+    rows, scales, bt = d["idx"]
+    rows.zero_()
+    if scales is not None:
+        scales.fill_(1.0)
+
+
+@pytest.mark.gpu
+def test_all_scores_tied(gpu):
+    """Every indexer key is zero, so every score is exactly 0: the selection must be the k'
+    lowest entry ids (ties go to lower ids), with scores 0."""
+    cfg = D(C.C4A_1M_B4_FP8, name="c4a_all_ties", ctx_after=(20000, 9000, 5), n_heads=16, k=700,
+            stages=("index", "attn"))
+    print(f"case {cfg.name}", flush=True)
+    from compressed_sparse_long_c4a_amd import pipeline
+    d = inputs.draw(cfg)
+    _zero_index_keys(d)
+    g = pipeline.to_device(d)
+    step = pipeline.Step(cfg, g)
+    step.run()
+    torch.cuda.synchronize()
+    topk = step.topk.cpu().numpy()
+    sc = step.topk_score.cpu().numpy()
+    for i, t in enumerate(d["q_pos"].tolist()):
+        n = (t + 1) // 4
+        kk = min(cfg.k, n)
+        assert np.array_equal(topk[i, :kk], np.arange(kk)), i
+        assert np.all(topk[i, kk:] == -1)
+        assert np.all(sc[i] == 0.0)
+    rep = P.run_step_parity(cfg, verbose=True, prep=_zero_index_keys)
+    assert not rep["fail"], rep["fail"][:10]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("ctx,k", [(80000, 12000), (20000, 4500)], ids=["cand-beyond-lds", "bound-disabled"])
+def test_large_selections(gpu, ctx, k):
+    """More candidates than the select kernel holds in LDS (the global-memory path), and a k so
+    large relative to n that the per-chunk bounds cannot filter (every entry is a candidate)."""
+    cfg = D(C.C4A_128K_B32, name=f"c4a_large_k_{k}", ctx_after=(ctx, ctx - 3), n_heads=16, k=k)
+    print(f"case {cfg.name}", flush=True)
+    rep = P.run_step_parity(cfg, verbose=True)
+    assert not rep["fail"], rep["fail"][:10]
+
+
+@pytest.mark.gpu
+def test_max_k(gpu):
+    """k = 65536, the largest the ABI accepts, over a 300K-token context (75,000 entries): the
+    index selection and an attention over 65,536 + 128 rows."""
+    cfg = D(C.C4A_128K_B32, name="c4a_max_k", ctx_after=(300000,), n_heads=16, k=65536)
+    print(f"case {cfg.name}", flush=True)
+    rep = P.run_step_parity(cfg, verbose=True)
+    assert not rep["fail"], rep["fail"][:10]
+
+
+@pytest.mark.gpu
+def test_attention_list_padding_and_out_of_range_ids(gpu):
+    """Attention-only with caller lists: -1 padding, ids past the causal limit and negative ids
+    are skipped; repeated calls reuse one workspace."""
+    cfg = D(C.C4A_128K_B32, name="c4a_attn_lists", ctx_after=(5000, 700, 64), n_heads=16, k=300,
+            stages=("attn",))
+
+    def prep(d):
+        top = inputs.random_topk(cfg, d, fill=0.6)
+        top[0, -5:] = torch.tensor([5000, 1 << 30, -7, 1249, 1250], dtype=torch.int32)  # n = 1250
+        top[2, :] = -1                                                            # window only
+        d["topk"] = top
+
+    print(f"case {cfg.name}", flush=True)
+    rep = P.run_step_parity(cfg, verbose=True, prep=prep)
+    assert not rep["fail"], rep["fail"][:10]
+
+
+@pytest.mark.gpu
+def test_empty_calls_launch_nothing(gpu):
+    """total_q = 0 and total_new = total_entries = 0 are valid and return without launching."""
+    import compressed_sparse_long_c4a_amd as csa
+    dev = "cuda"
+    i32 = dict(dtype=torch.int32, device=dev)
+    kv = csa.PagedCache(torch.zeros((2, 64, 576), dtype=torch.bfloat16, device=dev), torch.zeros((1, 1), **i32))
+    sw = csa.PagedCache(torch.zeros((2, 256, 576), dtype=torch.bfloat16, device=dev), torch.zeros((1, 1), **i32))
+    st = csa.PagedCache(torch.zeros((2, 256, 576), dtype=torch.bfloat16, device=dev), torch.zeros((1, 1), **i32))
+    csa.compress_insert(4, torch.zeros(1, **i32), torch.zeros(2, **i32),
+                        torch.zeros((0, 576), dtype=torch.bfloat16, device=dev), torch.zeros(2, **i32),
+                        torch.zeros((0, 8), dtype=torch.float32, device=dev), st, kv, sw)
+    q = torch.zeros((0, 16, 576), dtype=torch.bfloat16, device=dev)
+    out, _ = csa.sparse_attn_decode(torch.zeros(2, **i32), torch.zeros(0, **i32), q, kv, 4,
+                                    torch.zeros((0, 8), **i32), sw, 128, 0.04, 256)
+    assert out.shape == (0, 16, 576)
+    ic = csa.PagedCache(torch.zeros((2, 64, 128), dtype=torch.bfloat16, device=dev), torch.zeros((1, 1), **i32))
+    topk, _ = csa.index_topk(torch.zeros(2, **i32), torch.zeros(0, **i32),
+                             torch.zeros((0, 64, 128), dtype=torch.bfloat16, device=dev),
+                             torch.zeros((0, 64), dtype=torch.float32, device=dev), ic, 8, 256)
+    assert topk.shape == (0, 8)
+    torch.cuda.synchronize()

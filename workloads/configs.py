@@ -1,7 +1,8 @@
 """Workload shapes: the five configurations of the benchmark plus reduced variants for tests.
 
 A step appends ``new_tokens`` raw tokens to each sequence (ending at ctx_after[b]) and runs
-queries at the last ``q_per_seq`` new positions of each sequence.  ``stages`` lists what the
+queries at the last ``q_per_seq`` new positions of each sequence.  Either may be one count for
+every sequence or a tuple with one count per sequence (ragged batches).  ``stages`` lists what the
 timed step runs: "compress" (main KV, plus window rows), "compress_idx" (indexer keys),
 "index" (scores and top-k) and "attn" (sparse attention and inverse RoPE).
 """
@@ -16,8 +17,8 @@ class StepConfig:
     name: str
     ratio: int                       # 4 (c4a) or 128 (c128a)
     ctx_after: tuple[int, ...]       # raw tokens per sequence after the step
-    new_tokens: int                  # raw tokens appended per sequence by the step
-    q_per_seq: int                   # queries per sequence (the last q_per_seq new positions)
+    new_tokens: int | tuple[int, ...]  # raw tokens appended per sequence by the step
+    q_per_seq: int | tuple[int, ...]   # queries per sequence (at its last new positions)
     n_heads: int
     kv_dtype: str                    # "f32" | "bf16" | "fp8" (main and window caches)
     q_dtype: str                     # "f32" | "bf16"
@@ -38,6 +39,12 @@ class StepConfig:
     @property
     def batch(self) -> int:
         return len(self.ctx_after)
+
+    def new_of(self, b: int) -> int:
+        return self.new_tokens[b] if isinstance(self.new_tokens, tuple) else self.new_tokens
+
+    def q_of(self, b: int) -> int:
+        return self.q_per_seq[b] if isinstance(self.q_per_seq, tuple) else self.q_per_seq
 
     @property
     def max_context(self) -> int:

@@ -23,17 +23,20 @@ def draw(cfg: StepConfig) -> dict:
     B, R, D = cfg.batch, cfg.ratio, cfg.dim
     Wc = LOGITS_PER_ENTRY[R]
     L1 = list(cfg.ctx_after)
-    L0 = [l - cfg.new_tokens for l in L1]
+    new = [cfg.new_of(b) for b in range(B)]
+    nq = [cfg.q_of(b) for b in range(B)]
+    L0 = [l - m for l, m in zip(L1, new)]
+    assert all(0 <= q <= m for q, m in zip(nq, new)), "queries sit at new positions"
     assert min(L0) >= 0
     n0 = [l // R for l in L0]
     n1 = [l // R for l in L1]
     e = [b - a for a, b in zip(n0, n1)]
     d: dict = {"L0": L0, "L1": L1}
     d["ctx_lens"] = torch.tensor(L0, dtype=torch.int32)
-    d["cu_new"] = torch.arange(B + 1, dtype=torch.int32) * cfg.new_tokens
+    d["cu_new"] = torch.tensor([0] + list(torch.tensor(new).cumsum(0).tolist()), dtype=torch.int32)
     d["cu_entries"] = torch.tensor([0] + list(torch.tensor(e).cumsum(0).tolist()), dtype=torch.int32)
     raw_t = TORCH_DTYPE[cfg.raw_dtype]
-    d["new_raw"] = g.normal("new_raw", (B * cfg.new_tokens, D), raw_t)
+    d["new_raw"] = g.normal("new_raw", (sum(new), D), raw_t)
     d["logits"] = g.normal("logits", (sum(e), Wc))
     d["gamma"] = g.uniform("gamma", (D,), 0.5, 1.5) if cfg.gamma else None
 
@@ -45,10 +48,9 @@ def draw(cfg: StepConfig) -> dict:
                        [(max(0, a - Wc), b) for a, b in zip(L0, L1)])
     d["kv"], d["swa"], d["state"] = kv, swa, state
 
-    q_first = [b - cfg.q_per_seq for b in L1]
-    d["q_pos"] = torch.tensor([q + i for q in q_first for i in range(cfg.q_per_seq)], dtype=torch.int32)
-    d["cu_q"] = torch.arange(B + 1, dtype=torch.int32) * cfg.q_per_seq
-    total_q = B * cfg.q_per_seq
+    d["q_pos"] = torch.tensor([l - c + i for l, c in zip(L1, nq) for i in range(c)], dtype=torch.int32)
+    d["cu_q"] = torch.tensor([0] + list(torch.tensor(nq).cumsum(0).tolist()), dtype=torch.int32)
+    total_q = sum(nq)
     d["q"] = g.normal("q", (total_q, cfg.n_heads, D), TORCH_DTYPE[cfg.q_dtype])
 
     if cfg.has_indexer:
@@ -56,7 +58,7 @@ def draw(cfg: StepConfig) -> dict:
         d["q_idx"] = g.normal("q_idx", (total_q, cfg.idx_heads, 128), TORCH_DTYPE[cfg.idx_q_dtype])
         d["head_w"] = g.uniform("head_w", (total_q, cfg.idx_heads))
         if "compress_idx" in cfg.stages:
-            d["new_idx_raw"] = g.normal("new_idx_raw", (B * cfg.new_tokens, 128), raw_t)
+            d["new_idx_raw"] = g.normal("new_idx_raw", (sum(new), 128), raw_t)
             d["idx_logits"] = g.normal("idx_logits", (sum(e), Wc))
             d["idx_state"] = paged_rows(g, "idx_state", B, 256, 128, cfg.raw_dtype, maxL,
                                         [(max(0, a - Wc), b) for a, b in zip(L0, L1)])
