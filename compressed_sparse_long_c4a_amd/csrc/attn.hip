@@ -6,26 +6,32 @@
 // inverse RoPE: with v_n = k_n = R_n k the output must be multiplied by R_m^{-1}, leaving
 // R_{n-m}.  [vLLM-V4] appendix, exact k values: c128a attends to every entry (top-k = 8192).
 //
-// Kernel 1 (attn_partial), grid (row split, 16-head group, query), four independent waves:
-//   the addresses (and fp8 scales) of the split's rows are resolved once into LDS; wave w then
-//   walks the 16-row blocks w, w + 4, ... of the split with its own online softmax over the
-//   full row width, with no exchange between waves inside the loop.  Per 16-row block:
-//     QK : S^T[16 rows x 16 heads] = R . Q^T on MFMA 16x16x32 bf16.  Lane (r, g) holds row r,
-//          dims 32 ks + 8 g .. +7 of each k-step, loaded straight from HBM (the row gather and
-//          the A-operand layout coincide); Q^T, the B operand, stays in registers.
-//     softmax on the accumulators: lane (h, g) holds rows 4 g .. 4 g + 3 of head h, which is
-//          exactly the B-operand layout of P^T for MFMA 16x16x16, so P needs no data movement.
-//     PV : O^T[16 dims x 16 heads] += V^T . P^T per 16-dim tile.  The block's bf16 rows,
-//          written to the wave's LDS tile during QK, are read back transposed with
+// Kernel 1 (attn_partial), grid (row split, 16-head group, query).  The addresses (and fp8
+//   scales) of the split's rows are resolved once into LDS.  The workgroup's waves are
+//   (dq, ri): dq picks a quarter of the row's dimensions (32-dim k-steps, 5/5/4/4 of 18 for
+//   576), ri a row group; row group ri takes the 16-row blocks ri, ri + kRG, ... of the split,
+//   its four quarter waves in step.  Per block:
+//     QK : each quarter wave computes the partial S^T[16 rows x 16 heads] = R . Q^T over its
+//          dimensions on MFMA 16x16x32 bf16 (lane (r, g) holds row r, dims 32 ks + 8 g .. +7,
+//          loaded straight from HBM; Q^T, the B operand, stays in registers) and publishes it
+//          in LDS; after one barrier each wave adds the row group's four partials in the same
+//          order, so the four hold identical S.
+//     softmax on the accumulators (identical in the four waves): lane (h, g) holds rows
+//          4 g .. 4 g + 3 of head h, the B-operand layout of P^T, so P needs no data movement.
+//     PV : each wave accumulates O^T[its dims x 16 heads] only.  The bf16 quarter-rows it
+//          loaded, written to its LDS tile during QK, are read back transposed with
 //          ds_read_b64_tr_b16 (4 rows x 1 dim per lane).  P is split into bf16 hi + lo parts,
 //          which fill the two halves of the K = 32 slots of one MFMA 16x16x32 with V^T
 //          repeated in both halves: one MFMA per tile computes V^T (P_hi + P_lo), so PV keeps
 //          ~16 significant bits of P at the cost of a plain bf16 product.
+//   Every row is thus read from memory once per head group, and a wave's state (Q^T and O of
+//   its quarter, a ring of prefetched quarter-row tiles) is small enough for two waves per
+//   SIMD, whose memory and LDS latencies overlap.
 //   The softmax keeps a per-head reference exponent that moves only when a block's maximum
 //   exceeds it by more than kSlack (2^kSlack bounds P), so the output rescale is rare.
 //   fp8 rows (code * per-row scale): codes widen exactly to bf16; the scale multiplies the
 //   logit and P.  float32 rows / queries are split hi + lo as well (a second PV pass over the
-//   rows' lo parts).  The four waves' (m, l, O) are merged through LDS at the end, and one
+//   rows' lo parts).  The row groups' (m, l, O) are merged through LDS at the end, and one
 //   partial (m, l, O) per head leaves the workgroup.
 // Kernel 2 (attn_merge), grid (4-head group, query), one wave per head: combines the splits
 //   by their softmax statistics, normalises, applies R_t^{-1} to the last rope_dims dims
@@ -42,6 +48,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSplits = 256;
 constexpr int kRowsPerSplit = 1024;  // most rows a workgroup handles (addresses staged in LDS)
+constexpr int kRG = 2;               // row groups per workgroup (of four quarter waves each)
+constexpr int kWaves = 4 * kRG;
+constexpr int kThreads = 64 * kWaves;
 constexpr float kSlack = 8.0f;       // log2 headroom of P above the softmax reference
 
 struct Args {
@@ -112,9 +121,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 template <int DT, int QDT, int DIM>
-__global__ __launch_bounds__(256) void attn_partial(Args a) {
-  constexpr int NKS = DIM / 32;  // QK k-steps
-  constexpr int NDT = DIM / 16;  // PV dim tiles
+__global__ __launch_bounds__(kThreads) void attn_partial(Args a) {
+  constexpr int NKS = DIM / 32;        // QK k-steps of a full row
+  constexpr int MQ = (NKS + 3) / 4;    // k-steps of the largest quarter
   constexpr bool ROW_LO = DT == CSA_F32;
   constexpr bool Q_LO = QDT == CSA_F32;
   constexpr int ESZ = DT == CSA_F32 ? 4 : (DT == CSA_BF16 ? 2 : 1);
@@ -122,78 +131,88 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
   // row address is derived from a kernel argument and the loads are known to be global
   __shared__ int64_t off_sh[kRowsPerSplit];
   __shared__ float scale_sh[kRowsPerSplit];  // row scale (1 for bf16/f32 rows); 0 marks padding
-  // each wave's bf16 rows of its current block (row stride padded by 16 B: the 16 rows of a
-  // b128 write then start in distinct bank quads); the final merge reuses the space as two
-  // float32 [16][DIM + 4] buffers
-  constexpr int TROW = DIM * 2 + 16;
-  constexpr int TILE_BYTES = 4 * 16 * TROW;
-  constexpr int MERGE_BYTES = 2 * 16 * (DIM + 4) * 4;
+  // each wave's bf16 quarter-rows of its current block (row stride padded by 16 B so the 16
+  // rows of a b128 write start in distinct bank quads); the final merge reuses the space as
+  // one float32 [16][DIM + 4] buffer
+  constexpr int TROW = MQ * 64 + 16;
+  constexpr int TILE_BYTES = kWaves * 16 * TROW;
+  constexpr int MERGE_BYTES = 16 * (DIM + 4) * 4;
   __shared__ __attribute__((aligned(16))) char tile_sh[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
-  __shared__ float ml_sh[4][16][2];
+  __shared__ f32x4 sx_sh[2][kRG][4][64];  // partial S^T of each quarter: [step parity][row group]
+  __shared__ float ml_sh[kRG][16][2];
 
   const int s = blockIdx.x, hg = blockIdx.y, qi = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: scalar branches below)
   const int ln = lane & 15, lg = lane >> 4;
-  const int b = seq_of_wave(a.cu_q, a.batch, qi);
-  const int t = a.q_pos[qi];
-  const int n_vis = min((t + 1) / a.ratio, a.n_max);
-  const int n_c = a.has_topk ? a.k : n_vis;
-  const int n_w = min(a.window, t + 1);
-  const int n_rows = n_c + n_w;
-  const int r_begin = s * a.rows_per_split;
-  // a query without any visible row (no window and no entry yet) attends to nothing
-  const int nrows = (n_w > 0 || n_vis > 0) ? max(0, min(a.rows_per_split, n_rows - r_begin)) : 0;
-  const int nrows16 = (nrows + 15) & ~15;  // rows_per_split is a multiple of 32
+  // wave (dq, ri): waves 2 dq + ri share a SIMD pairwise with a wave of another quarter size
+  const int dq = wv / kRG, ri = wv % kRG;
+  const int nkq = NKS / 4 + (dq < NKS % 4 ? 1 : 0);              // k-steps of quarter dq
+  const int k0 = dq * (NKS / 4) + min(dq, NKS % 4);               // its first k-step
   const int H = a.n_heads;
   const char* kvbase = (const char*)a.kv.rows;
+  const int r_begin = s * a.rows_per_split;
 
-  // Q^T as the B operand: lane (head ln, group lg) holds q[h][32 ks + 8 lg + 0..7].
-  bf16x8 qb[NKS], qb_lo[Q_LO ? NKS : 1];
+  // ---- loads that need nothing else: the query position, its sequence, the split's list
+  // entries (list positions are bounded by k, so they are read before t is known), Q^T
+  const int t = a.q_pos[qi];
+  const int b = seq_of_wave(a.cu_q, a.batch, qi);
+  constexpr int RPT = kRowsPerSplit / kThreads;
+  int ent[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int pos = r_begin + min(tid + kThreads * u, a.rows_per_split - 1);
+    ent[u] = a.has_topk ? a.topk[(int64_t)qi * a.k + min(pos, a.k - 1)] : pos;
+  }
+  // Q^T as the B operand of quarter dq: lane (head ln, group lg) holds q[h][32 ks + 8 lg + 0..7]
+  bf16x8 qb[MQ], qb_lo[Q_LO ? MQ : 1];
   {
     const int h = 16 * hg + ln;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int d0 = 32 * ks + 8 * lg;
+    for (int kk = 0; kk < MQ; ++kk) {
+      const int d0 = 32 * min(k0 + kk, NKS - 1) + 8 * lg;
+      const bool use = h < H && kk < nkq;  // a short quarter's missing k-step stays zero
       if constexpr (QDT == CSA_BF16) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (h < H) v = *(const uint4*)((const uint16_t*)a.q + ((int64_t)qi * H + h) * DIM + d0);
-        qb[ks] = __builtin_bit_cast(bf16x8, v);
+        if (use) v = *(const uint4*)((const uint16_t*)a.q + ((int64_t)qi * H + h) * DIM + d0);
+        qb[kk] = __builtin_bit_cast(bf16x8, v);
       } else {
         float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (h < H) {
+        if (use) {
           const float* src = (const float*)a.q + ((int64_t)qi * H + h) * DIM + d0;
 #pragma unroll
           for (int i = 0; i < 8; ++i) x[i] = src[i];
         }
-        qb[ks] = f32x8_to_bf16(x);
+        qb[kk] = f32x8_to_bf16(x);
         float r[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r[i] = x[i] - (float)qb[ks][i];
-        if constexpr (Q_LO) qb_lo[ks] = f32x8_to_bf16(r);
+        for (int i = 0; i < 8; ++i) r[i] = x[i] - (float)qb[kk][i];
+        if constexpr (Q_LO) qb_lo[kk] = f32x8_to_bf16(r);
       }
     }
   }
-  // ---- resolve the split's rows once: offset and scale; padding rows (up to the next multiple
-  // of 16) -> a safe row with scale 0.  Each thread owns up to kRowsPerSplit / 256 rows; the
-  // list reads, then the block-table reads, then the scale reads of all its rows are issued
-  // together.
+
+  const int n_vis = min((t + 1) / a.ratio, a.n_max);
+  const int n_c = a.has_topk ? a.k : n_vis;
+  const int n_w = min(a.window, t + 1);
+  const int n_rows = n_c + n_w;
+  // a query without any visible row (no window and no entry yet) attends to nothing
+  const int nrows = (n_w > 0 || n_vis > 0) ? max(0, min(a.rows_per_split, n_rows - r_begin)) : 0;
+  // padded to whole steps (16 rows per row group); rows_per_split is a multiple of 16 kRG
+  const int nrows_p = (nrows + 16 * kRG - 1) / (16 * kRG) * (16 * kRG);
+
+  // ---- resolve the split's rows once: offset and scale; padding rows (up to a whole step)
+  // -> a safe row (finite data) with scale 0.  The block-table reads of all of a thread's rows are
+  // issued together, then the scale reads.
   if (nrows > 0) {  // (all staged positions are then rows of this query)
-    constexpr int RPT = kRowsPerSplit / 256;
     const int64_t swa_off = (int64_t)((uintptr_t)a.swa.rows - (uintptr_t)a.kv.rows);
     const int64_t safe = n_w > 0 ? swa_off + phys_row(a.swa, b, t) * (DIM * ESZ)
                                  : phys_row(a.kv, b, max(n_vis - 1, 0)) * (DIM * ESZ);
-    int ent[RPT];
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-      const int i = tid + 256 * u;
-      const int pos = r_begin + min(i, nrows - 1);
-      ent[u] = pos < n_c ? (a.has_topk ? a.topk[(int64_t)qi * a.k + pos] : pos) : -1;
-    }
     int64_t prow[RPT];
     bool is_kv[RPT], ok[RPT];
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
-      const int i = tid + 256 * u;
+      const int i = tid + kThreads * u;
       const int pos = r_begin + min(i, nrows - 1);
       is_kv[u] = pos < n_c;
       ok[u] = i < nrows && (!is_kv[u] || (ent[u] >= 0 && ent[u] < n_vis));
@@ -202,8 +221,8 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
     }
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
-      const int i = tid + 256 * u;
-      if (i < nrows16) {
+      const int i = tid + kThreads * u;
+      if (i < nrows_p) {
         const int64_t base = is_kv[u] ? 0 : swa_off;
         float sc = 0.f;
         if (ok[u]) {
@@ -216,23 +235,59 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
     }
   }
 
-  f32x4 o[NDT];
+  f32x4 o[2 * MQ];  // O^T of quarter dq: dim tile 16 d' .. +15 (d' < 2 nkq) x 16 heads
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 2 * MQ; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_run = 0.f;  // per head: reference exponent (log2 units), sum of P
   __syncthreads();
 
-  const int nblk = nrows16 >> 4;
-  const int my_n = nblk > wv ? (nblk - wv + 3) >> 2 : 0;  // this wave's blocks: wv, wv + 4, ...
+  const int steps = nrows_p / (16 * kRG);  // blocks of every row group
   char* wtile = tile_sh + wv * 16 * TROW;
   lds_char* wtile3 = (lds_char*)wtile;
-  // Row loads are unconditional (clamped to the wave's last block, always loadable): the wait
-  // counters then keep the next block in flight while this one is computed.
-  auto load_block = [&](int i, RowTile<DT, NKS>& tl) {
-    const int bi = wv + 4 * min(i, my_n - 1);
-    tl.load(kvbase + off_sh[16 * bi + ln], lg);
+  // lane (row ln, group lg): dims 32 (k0 + kk) + 8 lg .. +7 of its row for each kk < nkq
+  typedef typename std::conditional<DT == CSA_FP8_E4M3, uint2, uint4>::type Word;
+  struct Tile {
+    Word d[DT == CSA_F32 ? 1 : MQ];
+    const float* f32row;  // float32 rows are re-read per k-step instead of held in registers
   };
-  // V^T fragment of dim tile dt from the wave's LDS tile: lane (ln, lg) of a 16-lane group
+  // Row loads are unconditional (clamped to the last step; with no step at all, row 0 of the
+  // cache): the wait counters then keep the next blocks in flight while one is computed.
+  auto load_block = [&](int i, Tile& tl) {
+    const int bi = ri + kRG * max(0, min(i, steps - 1));
+    const int64_t off = steps > 0 ? off_sh[16 * bi + ln] : 0;
+    const char* row = kvbase + off + (32 * k0 + 8 * lg) * ESZ;
+    if constexpr (DT == CSA_F32) {
+      tl.f32row = (const float*)row;
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < MQ; ++kk) {
+        // (a missing last k-step of a short quarter reloads the previous one)
+        const int kc = kk < nkq ? kk : nkq - 1;
+        tl.d[kk] = *(const Word*)(row + 32 * kc * ESZ);
+      }
+    }
+  };
+  // bf16 operand of local k-step kk (exact for bf16 and fp8 rows); lo = float32 residual
+  auto frag = [&](const Tile& tl, int kk, bf16x8& hi, bf16x8& lo) {
+    if constexpr (DT == CSA_BF16) {
+      hi = __builtin_bit_cast(bf16x8, tl.d[kk]);
+    } else if constexpr (DT == CSA_FP8_E4M3) {
+      hi = fp8x8_to_bf16x8(tl.d[kk].x, tl.d[kk].y);
+    } else {
+      float x[8];
+      const int kc = kk < nkq ? kk : nkq - 1;  // (stays inside the row)
+      const float4 u0 = *(const float4*)(tl.f32row + 32 * kc);
+      const float4 u1 = *(const float4*)(tl.f32row + 32 * kc + 4);
+      x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+      x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+      hi = f32x8_to_bf16(x);
+      float r[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[i] = x[i] - (float)hi[i];
+      lo = f32x8_to_bf16(r);
+    }
+  };
+  // V^T fragment of local dim tile dt from the wave's tile: lane (ln, lg) of a 16-lane group
   // supplies row 4 lg + ln / 4, dims 16 dt + 4 (ln % 4) .. +3; the transposing read returns
   // rows 4 lg .. 4 lg + 3 of dim 16 dt + ln.
   auto vt_frag = [&](int dt) -> s16x4 {
@@ -240,23 +295,41 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
         (__attribute__((address_space(3))) s16x4*)(wtile3 + (4 * lg + (ln >> 2)) * TROW +
                                                    2 * (16 * dt + 4 * (ln & 3))));
   };
-
-  auto process_block = [&](int i, const RowTile<DT, NKS>& tile) {
-    const int row0 = 16 * (wv + 4 * i);
-    // S^T = R . Q^T; the bf16 rows also go to the wave's LDS tile for PV
-    f32x4 sacc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // two chains (even / odd ks)
+  // (a short quarter also runs its missing last k-step: a zero Q^T fragment adds nothing to S,
+  // and the two extra dim tiles accumulate the repeated k-step into O^T tiles never written
+  // out; no branch separates a tile's loads from their use)
+  auto pv = [&](const bf16x8& pb) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 rh, rl;
-      tile.frag(ks, rh, rl);
-      *(bf16x8*)(wtile + ln * TROW + 2 * (32 * ks + 8 * lg)) = rh;
-      f32x4& acc = sacc2[ks & 1];
-      acc = mfma16x16x32(rh, qb[ks], acc);
-      if constexpr (Q_LO) acc = mfma16x16x32(rh, qb_lo[ks], acc);
-      if constexpr (ROW_LO) acc = mfma16x16x32(rl, qb[ks], acc);
+    for (int dt = 0; dt < 2 * MQ; ++dt) {
+      const s16x4 at = vt_frag(dt);
+      o[dt] = mfma16x16x32(
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(at, at, 0, 1, 2, 3, 0, 1, 2, 3)), pb, o[dt]);
     }
-    const f32x4 sacc = sacc2[0] + sacc2[1];
+  };
+
+  // One step: row group ri takes its block i; every wave passes the barrier.
+  auto step = [&](int i, const Tile& tl) {
+    const int par = i & 1;
+    // partial S^T = R . Q^T over this quarter; the bf16 quarter-rows go to the wave's tile
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < MQ; ++kk) {
+      bf16x8 rh, rl;
+      frag(tl, kk, rh, rl);
+      *(bf16x8*)(wtile + ln * TROW + 2 * (32 * kk + 8 * lg)) = rh;
+      acc = mfma16x16x32(rh, qb[kk], acc);
+      if constexpr (Q_LO) acc = mfma16x16x32(rh, qb_lo[kk], acc);
+      if constexpr (ROW_LO) acc = mfma16x16x32(rl, qb[kk], acc);
+    }
+    sx_sh[par][ri][dq][lane] = acc;
+    barrier_lds();  // the partials of block i are visible; parity par is not reused before
+                    // the next barrier, so one barrier per step suffices
+    // the full S^T, summed in quarter order so the four waves hold identical values
+    f32x4 sacc = sx_sh[par][ri][0][lane];
+#pragma unroll
+    for (int d = 1; d < 4; ++d) sacc += sx_sh[par][ri][d][lane];
     // online softmax over the block's rows 4 lg + j (scale 0 marks padding)
+    const int row0 = 16 * (ri + kRG * i);
     const float4 rs4 = *(const float4*)&scale_sh[row0 + 4 * lg];
     const float rs[4] = {rs4.x, rs4.y, rs4.z, rs4.w};
     float z[4];
@@ -278,106 +351,113 @@ __global__ __launch_bounds__(256) void attn_partial(Args a) {
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < 2 * MQ; ++dt) o[dt] *= alpha;
     }
-    if (m_ref == -INFINITY) return;  // every row so far is padding (uniform per wave)
-    float pv[4], psum = 0.f;
+    float pvv[4], psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float p = __builtin_amdgcn_exp2f(z[j] - m_ref);  // padding rows: 2^-inf = 0
+      // padding rows give 0 (also while every row so far is padding and m_ref is -inf)
+      const float p = z[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[j] - m_ref);
       psum += p;
-      pv[j] = p * rs[j];
+      pvv[j] = p * rs[j];
     }
     l_run += psum;
     // B operand of PV: k-slots 0-3 of each lane group hold P_hi of its rows 4 lg + j, slots 4-7
-    // hold P_lo of the same rows
+    // hold P_lo of the same rows; O^T += [V^T | V^T] . [P_hi ; P_lo]
     bf16x8 pb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const __bf16 hi = (__bf16)pv[j];
+      const __bf16 hi = (__bf16)pvv[j];
       pb[j] = hi;
-      pb[4 + j] = (__bf16)(pv[j] - (float)hi);
+      pb[4 + j] = (__bf16)(pvv[j] - (float)hi);
     }
-    // O^T += [V^T | V^T] . [P_hi ; P_lo]
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const s16x4 at = vt_frag(dt);
-      o[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(at, at, 0, 1, 2, 3, 0, 1, 2, 3)), pb, o[dt]);
-    }
+    pv(pb);
     if constexpr (ROW_LO) {  // float32 rows: V_lo P_hi through the same tile
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int kk = 0; kk < MQ; ++kk) {
         bf16x8 rh, rl;
-        tile.frag(ks, rh, rl);
-        *(bf16x8*)(wtile + ln * TROW + 2 * (32 * ks + 8 * lg)) = rl;
+        frag(tl, kk, rh, rl);
+        *(bf16x8*)(wtile + ln * TROW + 2 * (32 * kk + 8 * lg)) = rl;
       }
       bf16x8 ph = pb;
 #pragma unroll
       for (int j = 0; j < 4; ++j) ph[4 + j] = (__bf16)0.0f;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const s16x4 at = vt_frag(dt);
-        o[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(at, at, 0, 1, 2, 3, 0, 1, 2, 3)), ph, o[dt]);
-      }
+      pv(ph);
     }
   };
 
-  if (my_n > 0) {
-    RowTile<DT, NKS> ta, tb;
-    load_block(0, ta);
+  // A ring of four register tiles: the next three blocks' loads are in flight while one is
+  // computed.  The unrolled loop body has no branch, so the wait counters see every tile's
+  // loads in order; the last steps (fewer than four) run after it on tiles already loaded.
+  // (float32 rows are read inside the step and need no ring.)
+  {
+    Tile t0, t1, t2, t3;
+    load_block(0, t0);
+    load_block(1, t1);
+    load_block(2, t2);
+    load_block(3, t3);
     int i = 0;
-    for (; i + 1 < my_n; i += 2) {  // no branch inside: the accumulators stay in place
-      load_block(i + 1, tb);
-      process_block(i, ta);
-      load_block(i + 2, ta);
-      process_block(i + 1, tb);
+    for (; i + 4 <= steps; i += 4) {
+      step(i, t0);
+      load_block(i + 4, t0);
+      step(i + 1, t1);
+      load_block(i + 5, t1);
+      step(i + 2, t2);
+      load_block(i + 6, t2);
+      step(i + 3, t3);
+      load_block(i + 7, t3);
     }
-    if (i < my_n) process_block(i, ta);
+    if (i < steps) step(i, t0);          // (uniform across the workgroup)
+    if (i + 1 < steps) step(i + 1, t1);
+    if (i + 2 < steps) step(i + 2, t2);
   }
 
-  // ---- merge the four waves through LDS: per head M = max_w m_w, f_w = 2^(m_w - M)
+  // ---- merge the row groups through LDS: per head M = max_g m_g, f_g = 2^(m_g - M)
   float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
-  if (lg == 0) {
-    ml_sh[wv][ln][0] = m_ref;
-    ml_sh[wv][ln][1] = l_tot;
+  if (dq == 0 && lg == 0) {
+    ml_sh[ri][ln][0] = m_ref;
+    ml_sh[ri][ln][1] = l_tot;
   }
-  __syncthreads();  // also: every wave is done with its tile (the merge buffers alias them)
-  const float M = fmaxf(fmaxf(ml_sh[0][ln][0], ml_sh[1][ln][0]), fmaxf(ml_sh[2][ln][0], ml_sh[3][ln][0]));
+  __syncthreads();  // also: every wave is done with its tile (the merge buffer aliases them)
+  float M = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < kRG; ++g) M = fmaxf(M, ml_sh[g][ln][0]);
   const float f = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - M);
-  float (*mb)[16][DIM + 4] = reinterpret_cast<float (*)[16][DIM + 4]>(tile_sh);
-  // waves 0 and 1 store f O into buffers 0 and 1, then waves 2 and 3 add theirs
+  float (*mb)[DIM + 4] = reinterpret_cast<float (*)[DIM + 4]>(tile_sh);
+  // row group 0 stores f O of its quarter, the others add theirs in turn
+  float* dst = &mb[ln][32 * k0 + 4 * lg];
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    if ((wv >> 1) == round) {
-      float* dst = &mb[wv & 1][ln][4 * lg];
+  for (int round = 0; round < kRG; ++round) {
+    if (ri == round) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        float4 v = make_float4(f * o[dt][0], f * o[dt][1], f * o[dt][2], f * o[dt][3]);
-        if (round == 1) {
-          const float4 w = *(const float4*)(dst + 16 * dt);
-          v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+      for (int dt = 0; dt < 2 * MQ; ++dt) {
+        if (dt < 2 * nkq) {
+          float4 v = make_float4(f * o[dt][0], f * o[dt][1], f * o[dt][2], f * o[dt][3]);
+          if (round > 0) {
+            const float4 w = *(const float4*)(dst + 16 * dt);
+            v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+          }
+          *(float4*)(dst + 16 * dt) = v;
         }
-        *(float4*)(dst + 16 * dt) = v;
       }
     }
     __syncthreads();
   }
   const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg;
-  for (int i = tid; i < 16 * DIM / 4; i += 256) {
+  for (int i = tid; i < 16 * DIM / 4; i += kThreads) {
     const int h = i / (DIM / 4), d = 4 * (i - h * (DIM / 4));
-    const float4 x = *(const float4*)&mb[0][h][d], y = *(const float4*)&mb[1][h][d];
-    *(float4*)(a.part_o + (pbase + h) * DIM + d) = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+    *(float4*)(a.part_o + (pbase + h) * DIM + d) = *(const float4*)&mb[h][d];
   }
   if (tid < 16) {
     const int h = tid;
     float Mh = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) Mh = fmaxf(Mh, ml_sh[w][h][0]);
+    for (int g = 0; g < kRG; ++g) Mh = fmaxf(Mh, ml_sh[g][h][0]);
     float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      if (ml_sh[w][h][0] != -INFINITY) L += exp2f(ml_sh[w][h][0] - Mh) * ml_sh[w][h][1];
+    for (int g = 0; g < kRG; ++g)
+      if (ml_sh[g][h][0] != -INFINITY) L += exp2f(ml_sh[g][h][0] - Mh) * ml_sh[g][h][1];
     a.part_ml[(pbase + h) * 2 + 0] = Mh;
     a.part_ml[(pbase + h) * 2 + 1] = L;
   }
@@ -484,7 +564,7 @@ __global__ __launch_bounds__(256) void attn_merge(MergeArgs a) {
 
 template <int DT, int QDT, int DIM>
 void launch_partial(const Args& args, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_partial<DT, QDT, DIM>), grid, dim3(256), 0, stream, args);
+  hipLaunchKernelGGL((attn_partial<DT, QDT, DIM>), grid, dim3(kThreads), 0, stream, args);
 }
 
 template <int DT, int QDT>
