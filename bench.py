@@ -183,15 +183,19 @@ def main() -> int:
 
     # per-stage breakdown (separate pass, events around every stage)
     stages = {}
-    names = [s for s in ("compress", "compress_idx", "index_score", "index_select", "attn")
-             if (s in cfg.stages) or (s.startswith("index") and has_index)]
+    # ("compress" runs every compressor of the step -- main KV and indexer keys -- in one launch)
+    names = [s for s in ("compress", "index_score", "index_select", "attn")
+             if (s in cfg.stages) or (s.startswith("index") and has_index)
+             or (s == "compress" and "compress_idx" in cfg.stages)]
+    run_stage = {"compress": step.compress_all, "index_score": step.index_score,
+                 "index_select": step.index_select, "attn": lambda g: step.attn(g, with_lse=False)}
     evs = {s: [] for s in names}
     for i in range(min(K, 100)):
         g = reps[i % len(reps)]
         for s in names:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            getattr(step, s)(g) if s != "attn" else step.attn(g, with_lse=False)
+            run_stage[s](g)
             b.record()
             evs[s].append((a, b))
     torch.cuda.synchronize()

@@ -8,7 +8,8 @@ the current HIP stream.  There is no fallback: if the library is not built,
 Calls (see include/csa.h for the exact semantics of each):
 
 * ``compress_insert`` -- compress + RMSNorm + RoPE + paged insert, rolling
-  state append and window-row write.
+  state append and window-row write; ``compress_insert_many`` runs several
+  compressors (main KV and indexer keys) in one launch.
 * ``index_topk`` (or ``index_score`` then ``index_select``) -- indexer scores
   and exact top-k over c4a entries.
 * ``sparse_attn_decode`` -- attention with K = V over the selected entries
@@ -43,6 +44,25 @@ class _CCache(ctypes.Structure):
     ]
 
 
+class _CJob(ctypes.Structure):
+    """csa_compress_job (include/csa.h)."""
+    _fields_ = [
+        ("ratio", ctypes.c_int32),
+        ("new_raw", ctypes.c_void_p),
+        ("raw_dtype", ctypes.c_int32),
+        ("cu_entries", ctypes.c_void_p),
+        ("total_entries", ctypes.c_int32),
+        ("gate_logits", ctypes.c_void_p),
+        ("gamma", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+        ("rope_base", ctypes.c_float),
+        ("rope_dims", ctypes.c_int32),
+        ("state", ctypes.POINTER(_CCache)),
+        ("out", ctypes.POINTER(_CCache)),
+        ("swa", ctypes.POINTER(_CCache)),
+    ]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
@@ -55,6 +75,7 @@ _SIGNATURES = {
     "csa_num_entries": (ctypes.c_int64, [_I, ctypes.c_int64]),
     "csa_compress_insert": (_I, [_P, _I, _I, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _F, _I,
                                  _CP, _CP, _CP]),
+    "csa_compress_insert_many": (_I, [_P, _I, _P, _P, _I, _I, ctypes.POINTER(_CJob)]),
     "csa_index_workspace_size": (_SZ, [_I, _I, _I]),
     "csa_index_topk": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _CP, _I, _P, _P, _P, _SZ]),
     "csa_index_score": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _CP, _I, _P, _SZ]),
@@ -193,6 +214,52 @@ def compress_insert(ratio: int, ctx_lens: torch.Tensor, cu_new: torch.Tensor, ne
         _ptr(new_raw), dtype_code(new_raw.dtype), cu_entries.data_ptr(), gate_logits.shape[0],
         _ptr(gate_logits), _ptr(gamma), eps, rope_base, rope_dims, _cref(state), _cref(out), _cref(swa))
     _check(st, "csa_compress_insert")
+
+
+class CompressJob:
+    """One compressor instance of compress_insert_many (the arguments of compress_insert that
+    are not shared by the call)."""
+
+    def __init__(self, ratio: int, new_raw: torch.Tensor, cu_entries: torch.Tensor,
+                 gate_logits: torch.Tensor, state: PagedCache, out: PagedCache,
+                 swa: PagedCache | None = None, gamma: torch.Tensor | None = None,
+                 eps: float = 1e-6, rope_base: float = 10000.0, rope_dims: int = 64):
+        _dev(cu_entries, "cu_entries", torch.int32, 1)
+        _dev(new_raw, "new_raw", (torch.float32, torch.bfloat16), 2)
+        _dev(gate_logits, "gate_logits", torch.float32, 2)
+        if gamma is not None:
+            _dev(gamma, "gamma", torch.float32, 1)
+        self.args = (ratio, new_raw, cu_entries, gate_logits, state, out, swa, gamma, eps, rope_base,
+                     rope_dims)
+        self._refs = [_cref(state), _cref(out), _cref(swa)]
+        self.c = _CJob(ratio, _ptr(new_raw), dtype_code(new_raw.dtype), cu_entries.data_ptr(),
+                       gate_logits.shape[0], _ptr(gate_logits), _ptr(gamma), eps, rope_base, rope_dims,
+                       *self._refs)
+
+
+def compress_jobs_array(jobs: list[CompressJob]):
+    """A ctypes array of csa_compress_job for compress_insert_many (kept alive by the caller)."""
+    arr = (_CJob * len(jobs))(*[j.c for j in jobs])
+    return arr
+
+
+def compress_insert_many(ctx_lens: torch.Tensor, cu_new: torch.Tensor, total_new: int,
+                         jobs: list[CompressJob]) -> None:
+    """Several compressors (e.g. main KV and indexer keys) over the same new tokens, one launch."""
+    _dev(ctx_lens, "ctx_lens", torch.int32, 1)
+    _dev(cu_new, "cu_new", torch.int32, 1)
+    batch = ctx_lens.shape[0]
+    if cu_new.shape[0] != batch + 1:
+        raise ValueError("cu_new needs batch + 1 entries")
+    for j in jobs:
+        if j.args[2].shape[0] != batch + 1:
+            raise ValueError("cu_entries needs batch + 1 entries")
+        if j.args[1].shape[0] != total_new:
+            raise ValueError("new_raw must have total_new rows")
+    arr = compress_jobs_array(jobs)
+    st = lib().csa_compress_insert_many(_stream(), batch, ctx_lens.data_ptr(), cu_new.data_ptr(), total_new,
+                                        len(jobs), arr)
+    _check(st, "csa_compress_insert_many")
 
 
 def index_workspace_size(total_q: int, max_context: int, k: int) -> int:

@@ -45,30 +45,60 @@ int64_t csa_num_entries(int ratio, int64_t num_tokens) {
   return num_tokens / ratio;
 }
 
+// Validates one compressor instance against the call's shared token layout and fills `job`.
+static int compress_job_check(const csa_compress_job& j, int batch, int total_new,
+                              csa::CompressJob* job) {
+  if (j.ratio != 4 && j.ratio != 128) return CSA_EINVAL;
+  if (j.total_entries < 0 || !j.cu_entries || !j.state || !j.out) return CSA_EINVAL;
+  if (total_new > 0 && !j.new_raw) return CSA_EINVAL;
+  if (j.total_entries > 0 && !j.gate_logits) return CSA_EINVAL;
+  if (j.raw_dtype != CSA_F32 && j.raw_dtype != CSA_BF16) return CSA_ENOTSUP;
+  if (!(j.eps >= 0.f) || !(j.rope_base > 0.f)) return CSA_EINVAL;
+  if (!cache_ok(j.state, 256, -1)) return CSA_EINVAL;
+  const int dim = j.state->dim;
+  if (j.state->dtype != j.raw_dtype) return CSA_EINVAL;
+  if (!cache_ok(j.out, 256 / j.ratio, dim)) return CSA_EINVAL;
+  if (j.swa && !cache_ok(j.swa, 256, dim)) return CSA_EINVAL;
+  if (dim < 2 || dim > 1024 || (dim & 1)) return CSA_ENOTSUP;
+  if (j.rope_dims < 2 || (j.rope_dims & 1) || j.rope_dims > dim || j.rope_dims > 128) return CSA_EINVAL;
+  (void)batch;
+  *job = csa::CompressJob{j.ratio, j.new_raw, j.raw_dtype, j.cu_entries, j.total_entries,
+                          j.gate_logits, j.gamma, j.eps, j.rope_base, j.rope_dims, j.state,
+                          j.out, j.swa};
+  return CSA_OK;
+}
+
+int csa_compress_insert_many(csa_stream_t stream, int batch, const int32_t* ctx_lens,
+                             const int32_t* cu_new, int total_new, int num_jobs,
+                             const csa_compress_job* jobs) {
+  if (batch <= 0 || total_new < 0 || !ctx_lens || !cu_new) return CSA_EINVAL;
+  if (num_jobs < 1 || num_jobs > csa::kMaxCompressJobs || !jobs) return CSA_EINVAL;
+  csa::CompressLaunch L{};
+  L.batch = batch;
+  L.ctx_lens = ctx_lens;
+  L.cu_new = cu_new;
+  L.total_new = total_new;
+  L.num_jobs = num_jobs;
+  int64_t work = 0;
+  for (int i = 0; i < num_jobs; ++i) {
+    const int st = compress_job_check(jobs[i], batch, total_new, &L.jobs[i]);
+    if (st != CSA_OK) return st;
+    work += (int64_t)jobs[i].total_entries + total_new;
+  }
+  if (work == 0) return CSA_OK;
+  if (work > 0x7FFFFFFF) return CSA_ENOTSUP;
+  return hip_status(csa::launch_compress(L, (hipStream_t)stream));
+}
+
 int csa_compress_insert(csa_stream_t stream, int ratio, int batch, const int32_t* ctx_lens,
                         const int32_t* cu_new, int total_new, const void* new_raw, int raw_dtype,
                         const int32_t* cu_entries, int total_entries, const float* gate_logits,
                         const float* gamma, float eps, float rope_base, int rope_dims,
                         const csa_cache* state, const csa_cache* out, const csa_cache* swa) {
-  if (ratio != 4 && ratio != 128) return CSA_EINVAL;
-  if (batch <= 0 || total_new < 0 || total_entries < 0) return CSA_EINVAL;
-  if (!ctx_lens || !cu_new || !cu_entries || !state || !out) return CSA_EINVAL;
-  if (total_new > 0 && !new_raw) return CSA_EINVAL;
-  if (total_entries > 0 && !gate_logits) return CSA_EINVAL;
-  if (raw_dtype != CSA_F32 && raw_dtype != CSA_BF16) return CSA_ENOTSUP;
-  if (!(eps >= 0.f) || !(rope_base > 0.f)) return CSA_EINVAL;
-  if (!cache_ok(state, 256, -1)) return CSA_EINVAL;
-  const int dim = state->dim;
-  if (state->dtype != raw_dtype) return CSA_EINVAL;
-  if (!cache_ok(out, 256 / ratio, dim)) return CSA_EINVAL;
-  if (swa && !cache_ok(swa, 256, dim)) return CSA_EINVAL;
-  if (dim < 2 || dim > 1024 || (dim & 1)) return CSA_ENOTSUP;
-  if (rope_dims < 2 || (rope_dims & 1) || rope_dims > dim || rope_dims > 128) return CSA_EINVAL;
-  if (total_new == 0 && total_entries == 0) return CSA_OK;
-  csa::CompressLaunch L{ratio, batch, ctx_lens, cu_new, total_new, new_raw, raw_dtype, cu_entries,
-                        total_entries, gate_logits, gamma, eps, rope_base, rope_dims, state, out,
-                        swa};
-  return hip_status(csa::launch_compress(L, (hipStream_t)stream));
+  const csa_compress_job job{ratio,      new_raw, raw_dtype, cu_entries, total_entries, gate_logits,
+                             gamma,      eps,     rope_base, rope_dims,  state,         out,
+                             swa};
+  return csa_compress_insert_many(stream, batch, ctx_lens, cu_new, total_new, 1, &job);
 }
 
 size_t csa_index_workspace_size(int total_q, int max_context, int k) {

@@ -9,9 +9,13 @@
 // [vLLM-V4] section 3 part 1: the compressor keeps the last coff*ratio raw rows per request as
 // sliding-window state.
 //
-// Launch shape: one 256-thread workgroup per emitted entry, then one per new raw row.  Both
-// kinds are latency-bound (a decode step emits at most one entry per sequence), so the kernel
-// favours few passes over the row: each thread owns the dimensions tid, tid+256, ... and the
+// Launch shape: one launch runs any number (<= kMaxCompressJobs) of compressor instances ("jobs") over
+// the same new tokens -- a c4a layer's main-KV and indexer-key compressors together, say --
+// with one 256-thread workgroup per emitted entry, then one per new raw row, job after job.
+// Every task is latency-bound (a decode step emits at most one entry per sequence and job), so
+// the kernel minimises dependent memory trips: the sequence tables (entry and token offsets,
+// context lengths) are read in one trip alongside the inputs that need no lookup, then the
+// block-table reads, then the rows.  Each thread owns the dimensions tid, tid+256, ... and the
 // row is staged once in LDS for the pairwise rotation and the fp8 amax.
 #include <type_traits>
 
@@ -23,13 +27,11 @@ namespace {
 
 constexpr int kMaxDim = 1024;
 constexpr int kPerThread = kMaxDim / 256;
-constexpr int kLdsBatch = 1024;  // sequences whose offsets are staged in LDS in one load
 constexpr int64_t kNoRow = INT64_MIN;  // window slot at a negative position
 
-struct Args {
-  int ratio, batch, W, coff, dim, rope_dims, total_entries, has_swa, raw_dtype;
-  const int32_t* ctx_lens;
-  const int32_t* cu_new;
+struct Job {
+  int ratio, W, coff, dim, rope_dims, total_entries, has_swa, raw_dtype;
+  int wg_begin;  // first workgroup of this job
   const void* new_raw;
   const int32_t* cu_entries;
   const float* logits;
@@ -37,6 +39,13 @@ struct Args {
   float eps;
   DevCache state, out, swa;
   RopeTable rope;
+};
+
+struct Args {
+  int batch, total_new, num_jobs;
+  const int32_t* ctx_lens;
+  const int32_t* cu_new;
+  Job job[kMaxCompressJobs];
 };
 
 // Rotate the last rope_dims entries of v_sh (consecutive pairs) by `position`.
@@ -74,74 +83,77 @@ __device__ void store_row(const DevCache& c, int64_t prow, const float* v_sh, in
   }
 }
 
-// Sequence owning flat index i (prefix sums cu[0..batch], staged in LDS when small enough).
-__device__ __forceinline__ int seq_lookup(const int* cu_sh, const int32_t* cu, int batch, int i) {
-  if (batch > kLdsBatch) return seq_of(cu, batch, i);
+// Sequence tables staged in LDS: the prefix sums `cu` (entries or new tokens), the context
+// lengths and the new-token offsets; for batch <= 256 one trip loads them all, larger batches
+// look entries up in global memory.
+struct SeqTables {
+  int cu[257];
+  int ctx[256];
+  int nw[256];
+};
+
+// Sequence owning flat index i of the prefix sums cu[0..batch] (empty sequences allowed).
+__device__ __forceinline__ int seq_lookup(const SeqTables& t, const int32_t* cu, int batch, int i) {
+  if (batch > 256) return seq_of(cu, batch, i);
   int lo = 0, hi = batch - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (cu_sh[mid] <= i) lo = mid; else hi = mid - 1;
+    if (t.cu[mid] <= i) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
 
-// RAW: dtype of the raw rows (CSA_BF16 or CSA_F32).  Every workgroup issues the loads that do
-// not depend on its sequence before the sequence lookup, and all rows of a window at once, so
-// a task costs about four dependent memory round trips: offsets, sequence length, block
-// table, rows.
 template <int RAW>
-__global__ __launch_bounds__(256) void compress_kernel(Args a) {
+__device__ void compress_task(const Args& a, const Job& J, int local, SeqTables& tab, float* v_sh,
+                              float* w_sh, int64_t* off_sh, float* red_sh) {
   typedef typename std::conditional<RAW == CSA_BF16, uint16_t, float>::type Elem;
   constexpr int ESZ = sizeof(Elem);
-  __shared__ float v_sh[kMaxDim];
-  __shared__ float w_sh[128];
-  // byte offset of window row r from new_raw (kNoRow: no row; a state row may lie below
-  // new_raw, so offsets take either sign); addresses derived from a kernel argument compile to
-  // global loads, whose waits do not drain LDS traffic
-  __shared__ int64_t off_sh[128];
-  __shared__ float red_sh[8];
-  __shared__ int cu_sh[kLdsBatch + 1];
   const int tid = threadIdx.x;
-  const int dim = a.dim;
+  const int dim = J.dim;
   const int64_t row_bytes = (int64_t)dim * ESZ;
-  const char* raw = (const char*)a.new_raw;
-  const bool entry_task = (int)blockIdx.x < a.total_entries;
+  const char* raw = (const char*)J.new_raw;
   auto to_f32 = [](Elem v) -> float {
     if constexpr (RAW == CSA_BF16) return bf16_bits_to_f32(v);
     else return v;
   };
+  const bool entry_task = local < J.total_entries;
 
   if (entry_task) {
     // ---- one compressed entry
-    const int e = blockIdx.x;
-    const int W = a.W;
-    const float lg = (tid < W) ? a.logits[(int64_t)e * W + tid] : -INFINITY;
+    const int e = local;
+    const int W = J.W;
+    // trip 1: everything that needs no lookup
+    const float lg = (tid < W) ? J.logits[(int64_t)e * W + tid] : -INFINITY;
     float gm[kPerThread];
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k)
-      gm[k] = a.gamma ? a.gamma[min(tid + 256 * k, dim - 1)] : 1.0f;
-    if (a.batch <= kLdsBatch)
-      for (int i = tid; i <= a.batch; i += 256) cu_sh[i] = a.cu_entries[i];
+    for (int k = 0; k < kPerThread; ++k) gm[k] = J.gamma ? J.gamma[min(tid + 256 * k, dim - 1)] : 1.0f;
+    if (a.batch <= 256) {
+      if (tid <= a.batch) tab.cu[tid] = J.cu_entries[tid];
+      if (tid < a.batch) {
+        tab.ctx[tid] = a.ctx_lens[tid];
+        tab.nw[tid] = a.cu_new[tid];
+      }
+    }
     __syncthreads();
-    const int b = seq_lookup(cu_sh, a.cu_entries, a.batch, e);
-    const int64_t L0 = a.ctx_lens[b];
-    const int n0 = a.cu_new[b];
-    const int e0 = a.batch <= kLdsBatch ? cu_sh[b] : a.cu_entries[b];
-    const int64_t j = L0 / a.ratio + (e - e0);
-    const int64_t start = (int64_t)a.ratio * j - (int64_t)(a.coff - 1) * a.ratio;
-    const int64_t anchor = (int64_t)a.ratio * j + a.ratio - 1;
+    const int b = seq_lookup(tab, J.cu_entries, a.batch, e);
+    const int64_t L0 = a.batch <= 256 ? tab.ctx[b] : a.ctx_lens[b];
+    const int n0 = a.batch <= 256 ? tab.nw[b] : a.cu_new[b];
+    const int e0 = a.batch <= 256 ? tab.cu[b] : J.cu_entries[b];
+    const int64_t j = L0 / J.ratio + (e - e0);
+    const int64_t start = (int64_t)J.ratio * j - (int64_t)(J.coff - 1) * J.ratio;
+    const int64_t anchor = (int64_t)J.ratio * j + J.ratio - 1;
 
-    // window rows: positions below 0 hold no row, below L0 come from the state cache, the
-    // rest are new rows of this sequence
+    // trip 2: block tables.  Window rows: positions below 0 hold no row, below L0 come from the
+    // state cache, the rest are new rows of this sequence
     if (tid < W) {
       const int64_t p = start + tid;
-      const int64_t state_off = (int64_t)((uintptr_t)a.state.rows - (uintptr_t)a.new_raw);
+      const int64_t state_off = (int64_t)((uintptr_t)J.state.rows - (uintptr_t)J.new_raw);
       int64_t off = kNoRow;
       if (p >= L0) off = (n0 + (p - L0)) * row_bytes;
-      else if (p >= 0) off = state_off + phys_row(a.state, b, p) * row_bytes;
+      else if (p >= 0) off = state_off + phys_row(J.state, b, p) * row_bytes;
       off_sh[tid] = off;
     }
-    const int64_t orow = phys_row(a.out, b, j);
+    const int64_t orow = phys_row(J.out, b, j);
     // w = softmax(logits of this entry)
     const float mx = block_max256(lg, red_sh);
     const float ex = (tid < W) ? expf(lg - mx) : 0.f;
@@ -149,8 +161,8 @@ __global__ __launch_bounds__(256) void compress_kernel(Args a) {
     if (tid < W) w_sh[tid] = ex / den;
     __syncthreads();
 
-    // y = sum_r w_r x_r, eight rows' loads in flight together (a missing row loads the first
-    // new row, which exists whenever an entry is emitted, and is then discarded)
+    // trip 3: y = sum_r w_r x_r, eight rows' loads in flight together (a missing row loads the
+    // first new row, which exists whenever an entry is emitted, and is then discarded)
     float y[kPerThread] = {0.f, 0.f, 0.f, 0.f};
     for (int r0 = 0; r0 < W; r0 += 8) {
       Elem x[8][kPerThread];
@@ -175,83 +187,111 @@ __global__ __launch_bounds__(256) void compress_kernel(Args a) {
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) ss = tid + 256 * k < dim ? fmaf(y[k], y[k], ss) : ss;
     ss = block_sum256(ss, red_sh);
-    const float inv = 1.0f / sqrtf(ss / (float)dim + a.eps);
+    const float inv = 1.0f / sqrtf(ss / (float)dim + J.eps);
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
       const int d = tid + 256 * k;
       if (d < dim) v_sh[d] = y[k] * inv * gm[k];
     }
     __syncthreads();
-    rope_lds(v_sh, dim, a.rope_dims, (double)anchor, a.rope);
+    rope_lds(v_sh, dim, J.rope_dims, (double)anchor, J.rope);
     __syncthreads();
-    store_row(a.out, orow, v_sh, dim, red_sh);
+    store_row(J.out, orow, v_sh, dim, red_sh);
   } else {
     // ---- one new raw row: state append (last W positions) and window row RoPE_p(x_p)
-    const int r = blockIdx.x - a.total_entries;
+    const int r = local - J.total_entries;
+    // trip 1: the row and the sequence tables
     Elem x[kPerThread];
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k)
-      x[k] = ((const Elem*)a.new_raw)[(int64_t)r * dim + min(tid + 256 * k, dim - 1)];
-    if (a.batch <= kLdsBatch)
-      for (int i = tid; i <= a.batch; i += 256) cu_sh[i] = a.cu_new[i];
+    for (int k = 0; k < kPerThread; ++k) x[k] = ((const Elem*)raw)[(int64_t)r * dim + min(tid + 256 * k, dim - 1)];
+    if (a.batch <= 256) {
+      if (tid <= a.batch) tab.cu[tid] = a.cu_new[tid];
+      if (tid < a.batch) tab.ctx[tid] = a.ctx_lens[tid];
+    }
     __syncthreads();
-    const int b = seq_lookup(cu_sh, a.cu_new, a.batch, r);
-    const int64_t L0 = a.ctx_lens[b];
-    const int n0 = a.batch <= kLdsBatch ? cu_sh[b] : a.cu_new[b];
-    const int n1 = a.batch <= kLdsBatch ? cu_sh[b + 1] : a.cu_new[b + 1];
+    const int b = seq_lookup(tab, a.cu_new, a.batch, r);
+    const int64_t L0 = a.batch <= 256 ? tab.ctx[b] : a.ctx_lens[b];
+    const int n0 = a.batch <= 256 ? tab.cu[b] : a.cu_new[b];
+    const int n1 = a.batch <= 256 ? tab.cu[b + 1] : a.cu_new[b + 1];
     const int64_t p = L0 + (r - n0);
     const int64_t L1 = L0 + (n1 - n0);
-    const bool append = p >= L1 - a.W;
-    const int64_t srow = append ? phys_row(a.state, b, p) : 0;
-    const int64_t wrow = a.has_swa ? phys_row(a.swa, b, p) : 0;
+    const bool append = p >= L1 - J.W;
+    // trip 2: block tables, then the stores
+    const int64_t srow = append ? phys_row(J.state, b, p) : 0;
+    const int64_t wrow = J.has_swa ? phys_row(J.swa, b, p) : 0;
     if (append) {
-      Elem* dst = (Elem*)a.state.rows + srow * dim;
+      Elem* dst = (Elem*)J.state.rows + srow * dim;
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k)
         if (tid + 256 * k < dim) dst[tid + 256 * k] = x[k];
     }
-    if (a.has_swa) {
+    if (J.has_swa) {
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k)
         if (tid + 256 * k < dim) v_sh[tid + 256 * k] = to_f32(x[k]);
       __syncthreads();
-      rope_lds(v_sh, dim, a.rope_dims, (double)p, a.rope);
+      rope_lds(v_sh, dim, J.rope_dims, (double)p, J.rope);
       __syncthreads();
-      store_row(a.swa, wrow, v_sh, dim, red_sh);
+      store_row(J.swa, wrow, v_sh, dim, red_sh);
     }
   }
+}
+
+__global__ __launch_bounds__(256) void compress_kernel(Args a) {
+  __shared__ float v_sh[kMaxDim];
+  __shared__ float w_sh[128];
+  // byte offset of window row r from new_raw (kNoRow: no row; a state row may lie below
+  // new_raw, so offsets take either sign); addresses derived from a kernel argument compile to
+  // global loads, whose waits do not drain LDS traffic
+  __shared__ int64_t off_sh[128];
+  __shared__ float red_sh[8];
+  __shared__ SeqTables tab;
+  int jb = 0;  // the job of this workgroup (uniform)
+  for (int i = 1; i < a.num_jobs; ++i)
+    if ((int)blockIdx.x >= a.job[i].wg_begin) jb = i;
+  const Job& J = a.job[jb];
+  const int local = blockIdx.x - J.wg_begin;
+  if (J.raw_dtype == CSA_BF16)
+    compress_task<CSA_BF16>(a, J, local, tab, v_sh, w_sh, off_sh, red_sh);
+  else
+    compress_task<CSA_F32>(a, J, local, tab, v_sh, w_sh, off_sh, red_sh);
 }
 
 }  // namespace
 
 hipError_t launch_compress(const CompressLaunch& c, hipStream_t stream) {
   Args a{};
-  a.ratio = c.ratio;
   a.batch = c.batch;
-  a.coff = c.ratio == 4 ? 2 : 1;
-  a.W = a.coff * c.ratio;
-  a.dim = c.state->dim;
-  a.rope_dims = c.rope_dims;
-  a.total_entries = c.total_entries;
-  a.has_swa = c.swa != nullptr;
-  a.raw_dtype = c.raw_dtype;
+  a.total_new = c.total_new;
+  a.num_jobs = c.num_jobs;
   a.ctx_lens = c.ctx_lens;
   a.cu_new = c.cu_new;
-  a.new_raw = c.new_raw;
-  a.cu_entries = c.cu_entries;
-  a.logits = c.logits;
-  a.gamma = c.gamma;
-  a.eps = c.eps;
-  a.rope = make_rope_table(c.rope_base, c.rope_dims);
-  a.state = to_dev(c.state);
-  a.out = to_dev(c.out);
-  a.swa = to_dev(c.swa);
-  const int blocks = c.total_entries + c.total_new;
+  int blocks = 0;
+  for (int i = 0; i < c.num_jobs; ++i) {
+    const CompressJob& s = c.jobs[i];
+    Job& J = a.job[i];
+    J.ratio = s.ratio;
+    J.coff = s.ratio == 4 ? 2 : 1;
+    J.W = J.coff * s.ratio;
+    J.dim = s.state->dim;
+    J.rope_dims = s.rope_dims;
+    J.total_entries = s.total_entries;
+    J.has_swa = s.swa != nullptr;
+    J.raw_dtype = s.raw_dtype;
+    J.wg_begin = blocks;
+    J.new_raw = s.new_raw;
+    J.cu_entries = s.cu_entries;
+    J.logits = s.logits;
+    J.gamma = s.gamma;
+    J.eps = s.eps;
+    J.rope = make_rope_table(s.rope_base, s.rope_dims);
+    J.state = to_dev(s.state);
+    J.out = to_dev(s.out);
+    J.swa = to_dev(s.swa);
+    blocks += s.total_entries + c.total_new;
+  }
   if (blocks == 0) return hipSuccess;
-  if (c.raw_dtype == CSA_BF16)
-    hipLaunchKernelGGL(compress_kernel<CSA_BF16>, dim3(blocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(compress_kernel<CSA_F32>, dim3(blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(compress_kernel, dim3(blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

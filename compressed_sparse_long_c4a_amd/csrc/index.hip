@@ -16,9 +16,10 @@
 //     lower bound on the k-th largest score (each full chunk holds kc keys above its bound,
 //     and chunks * kc >= k), so every selected entry has score >= tau_lo.  Survivors are
 //     compacted, in entry order, into a chunk-sparse candidate list.
-//  3. select -- one workgroup per query: gathers the candidates into LDS and finds the exact
-//     k-th largest key by four 8-bit radix passes, then writes the winners in ascending
-//     entry order, resolving exact ties towards lower entry ids.
+//  3. select -- one workgroup per query: gathers the candidate lists densely into LDS (one
+//     coalesced piece per chunk), finds the exact k-th largest key by 11-bit radix passes over
+//     the candidates' own key range, then writes the winners in ascending entry order with one
+//     prefix scan, resolving exact ties towards lower entry ids.
 #include "common.h"
 #include "launch.h"
 
@@ -390,42 +391,37 @@ __global__ __launch_bounds__(256) void index_filter(SelArgs a) {
 // ---- select: exact k-th largest among the candidates, winners in ascending entry order.
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kDigitBits = 11;              // radix digit: 2048 bins, two per thread
+constexpr int kBins = 1 << kDigitBits;
 
-template <typename T, typename Op>
-__device__ __forceinline__ T sel_block_reduce(T v, T* red, Op op) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = op(v, (T)__shfl_xor(v, o, kWave));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  T r = red[0];
-#pragma unroll
-  for (int i = 1; i < kSelWaves; ++i) r = op(r, red[i]);
-  return r;
-}
-
-// Exclusive prefix sum over the select block; total in *total.  sh holds kSelWaves ints.
-__device__ __forceinline__ int sel_exscan(int v, int* sh, int* total) {
+// Exclusive prefix sums of two values over the select block at once; totals in tot[0..1].
+// sh holds 2 kSelWaves ints.
+__device__ __forceinline__ int2 sel_exscan2(int v0, int v1, int* sh, int* tot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = v;
+  int i0 = v0, i1 = v1;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
+    const int y0 = __shfl_up(i0, o, kWave), y1 = __shfl_up(i1, o, kWave);
+    if (lane >= o) { i0 += y0; i1 += y1; }
   }
   __syncthreads();
-  if (lane == 63) sh[w] = incl;
+  if (lane == 63) { sh[w] = i0; sh[kSelWaves + w] = i1; }
   __syncthreads();
-  int base = 0, tot = 0;
+  int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
 #pragma unroll
   for (int i = 0; i < kSelWaves; ++i) {
-    base += i < w ? sh[i] : 0;
-    tot += sh[i];
+    const int x0 = sh[i], x1 = sh[kSelWaves + i];
+    b0 += i < w ? x0 : 0;
+    b1 += i < w ? x1 : 0;
+    t0 += x0;
+    t1 += x1;
   }
-  *total = tot;
-  return base + incl - v;
+  tot[0] = t0;
+  tot[1] = t1;
+  return make_int2(b0 + i0 - v0, b1 + i1 - v1);
 }
 
+// Candidate g of the query (dense index over the chunk-sparse list).
 template <bool IN_LDS>
 __device__ __forceinline__ uint2 cand_at(const uint2* cand_sh, const uint2* gcand, const int* off_sh,
                                          int nchunks, int g) {
@@ -438,65 +434,90 @@ __device__ __forceinline__ uint2 cand_at(const uint2* cand_sh, const uint2* gcan
   return gcand[(int64_t)lo * C + (g - off_sh[lo])];
 }
 
+// The kprime-th largest key among the m candidates and how many keys equal to it are
+// selected: a most-significant-digit radix select on d = key - lo over the candidates' own
+// range, 11 bits per pass (keys decided by a higher digit drop out of later passes).
 template <bool IN_LDS>
-__device__ void select_core(const SelArgs& a, int qi, int m, int kprime, const uint2* cand_sh,
-                            const uint2* gcand, const int* off_sh, int nchunks, uint32_t* hist,
-                            int* misc, int* scan_sh, uint32_t* red) {
-  const int tid = threadIdx.x;
-  // radix select on d = key - lo over the candidates' own range, 8 bits per pass from the top
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+__device__ void radix_select(int m, int kprime, const uint2* cand_sh, const uint2* gcand,
+                             const int* off_sh, int nchunks, uint32_t* hist, int* misc,
+                             int* scan_sh, uint32_t* red, uint32_t& tau, int& ties_needed) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t lo = 0xFFFFFFFFu, nhi = 0xFFFFFFFFu;  // min key, min of ~key
   for (int g = tid; g < m; g += kSelThreads) {
     const uint32_t key = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x;
     lo = min(lo, key);
-    hi = max(hi, key);
+    nhi = min(nhi, ~key);
   }
-  lo = sel_block_reduce(lo, red, [](uint32_t x, uint32_t y) { return min(x, y); });
-  hi = sel_block_reduce(hi, red, [](uint32_t x, uint32_t y) { return max(x, y); });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, kWave));
+    nhi = min(nhi, (uint32_t)__shfl_xor((int)nhi, o, kWave));
+  }
+  if (lane == 0) { red[w] = lo; red[kSelWaves + w] = nhi; }
+  __syncthreads();
+  lo = red[0];
+  nhi = red[kSelWaves];
+#pragma unroll
+  for (int i = 1; i < kSelWaves; ++i) { lo = min(lo, red[i]); nhi = min(nhi, red[kSelWaves + i]); }
+  const uint32_t range = ~nhi - lo;
   uint32_t prefix = 0;  // decided high digits of d
   int need = kprime;
-  for (int top = bit_len(hi - lo); top > 0; top -= 8) {
-    const int shift = max(0, top - 8);
-    if (tid < 256) hist[tid] = 0;
+  for (int top = bit_len(range); top > 0; top -= kDigitBits) {
+    const int shift = max(0, top - kDigitBits);
+    hist[tid] = 0;
+    hist[tid + kSelThreads] = 0;
     __syncthreads();
     for (int g = tid; g < m; g += kSelThreads) {
       const uint32_t d = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x - lo;
-      if (top >= 32 || (d >> top) == (prefix >> top)) atomicAdd(&hist[(d >> shift) & 255u], 1u);
+      if (top >= 32 || (d >> top) == (prefix >> top)) atomicAdd(&hist[(d >> shift) & (kBins - 1)], 1u);
     }
     __syncthreads();
-    if (tid < kWave) pick_bin_wave0(hist, need, misc);
+    // thread t owns bins 2047 - 2t and 2046 - 2t (descending); the thread whose running count
+    // from the top crosses `need` holds the bin of the kprime-th largest key
+    const uint32_t h0 = hist[kBins - 1 - 2 * tid], h1 = hist[kBins - 2 - 2 * tid];
+    int tot2[2];
+    const int before = sel_exscan2((int)(h0 + h1), 0, scan_sh, tot2).x;
+    if (before < need && before + (int)(h0 + h1) >= need) {
+      const bool first = before + (int)h0 >= need;
+      misc[0] = first ? kBins - 1 - 2 * tid : kBins - 2 - 2 * tid;
+      misc[1] = first ? before : before + (int)h0;
+    }
     __syncthreads();
     prefix |= (uint32_t)misc[0] << shift;
     need -= misc[1];
     __syncthreads();
   }
-  const uint32_t tau = prefix + lo;  // the kprime-th largest key
-  const int ties_needed = need;      // how many keys equal to tau are selected
-  // contiguous ranges per thread keep entry order through both scans
+  tau = prefix + lo;  // the kprime-th largest key
+  ties_needed = need; // how many keys equal to tau are selected
+}
+
+// Winners in ascending entry order: the candidates are stored in entry order, so one scan of
+// (keys above tau, keys equal to tau) per thread-contiguous range places every winner; ties
+// go to the lowest entries.
+template <bool IN_LDS>
+__device__ void write_winners(const SelArgs& a, int qi, int m, uint32_t tau, int ties_needed,
+                              const uint2* cand_sh, const uint2* gcand, const int* off_sh,
+                              int nchunks, int* scan_sh) {
+  const int tid = threadIdx.x;
   const int per = (m + kSelThreads - 1) / kSelThreads;
   const int g0 = min(m, tid * per), g1 = min(m, g0 + per);
-  int eq = 0;
-  for (int g = g0; g < g1; ++g) eq += cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x == tau;
-  int tot;
-  const int tie_rank = sel_exscan(eq, scan_sh, &tot);
-  int sel = 0;
-  {
-    int tr = tie_rank;
-    for (int g = g0; g < g1; ++g) {
-      const uint32_t key = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x;
-      if (key > tau) ++sel;
-      else if (key == tau) { sel += tr < ties_needed; ++tr; }
-    }
+  int gt = 0, eq = 0;
+  for (int g = g0; g < g1; ++g) {
+    const uint32_t key = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x;
+    gt += key > tau;
+    eq += key == tau;
   }
-  int pos = sel_exscan(sel, scan_sh + kSelWaves, &tot);
+  int tot2[2];
+  const int2 ex = sel_exscan2(gt, eq, scan_sh, tot2);
+  int tr = ex.y;                                 // ties before this range
+  int pos = ex.x + min(ex.y, ties_needed);       // winners before this range
   int32_t* out = a.topk_idx + (int64_t)qi * a.k;
   float* outs = a.topk_score ? a.topk_score + (int64_t)qi * a.k : nullptr;
-  int tr = tie_rank;
   for (int g = g0; g < g1; ++g) {
     const uint2 c = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g);
-    bool take = false;
-    if (c.x > tau) take = true;
-    else if (c.x == tau) { take = tr < ties_needed; ++tr; }
-    if (take && pos < a.k) {
+    bool take = c.x > tau;
+    if (c.x == tau) { take = tr < ties_needed; ++tr; }
+    if (take) {
       out[pos] = (int32_t)c.y;
       if (outs) outs[pos] = key2f(c.x);
       ++pos;
@@ -507,11 +528,12 @@ __device__ void select_core(const SelArgs& a, int qi, int m, int kprime, const u
 __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
   __shared__ uint2 cand_sh[kSelCap];
   __shared__ int off_sh[kMaxChunks + 1];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kBins];
   __shared__ int misc[4];
   __shared__ int scan_sh[2 * kSelWaves];
-  __shared__ uint32_t red[kSelWaves];
+  __shared__ uint32_t red[2 * kSelWaves];
   const int qi = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int n = query_entries(a.q_pos, qi, a.n_max);
   const int kprime = min(a.k, n);
   int32_t* out = a.topk_idx + (int64_t)qi * a.k;
@@ -529,33 +551,49 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
     }
     return;
   }
-  // prefix sums of the per-chunk candidate counts (one chunk per thread)
+  // offsets of the per-chunk candidate lists (one chunk per thread)
   const int nchunks = (n + C - 1) / C;
   const int cnt = tid < nchunks ? a.cand_cnt[(int64_t)qi * a.chunks + tid] : 0;
-  int m;
-  off_sh[tid] = sel_exscan(cnt, scan_sh, &m);
-  if (tid == 0) off_sh[kMaxChunks] = m;
+  int tot2[2];
+  off_sh[tid] = sel_exscan2(cnt, 0, scan_sh, tot2).x;
+  const int m = tot2[0];
+  if (tid == 0) off_sh[nchunks] = m;
   __syncthreads();
   const uint2* gcand = a.cand + (int64_t)qi * a.n_cap;
+  uint32_t tau;
+  int ties_needed;
   if (m <= kSelCap) {
-    // gather the chunk-sparse candidates densely, eight independent loads in flight per thread
-    for (int base = 0; base < m; base += 8 * kSelThreads) {
+    // gather the lists densely into LDS: wave w copies chunks w, w + 16, ...; up to eight
+    // 64-candidate pieces per wave are loaded before any is stored
+    for (int c0 = w; c0 < nchunks; c0 += 8 * kSelWaves) {
       uint2 v[8];
+      int dst[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int g = base + u * kSelThreads + tid;
-        v[u] = g < m ? cand_at<false>(nullptr, gcand, off_sh, nchunks, g) : make_uint2(0, 0);
+        const int c = c0 + u * kSelWaves;
+        const int len = c < nchunks ? off_sh[c + 1] - off_sh[c] : 0;
+        dst[u] = lane < len ? off_sh[c] + lane : -1;
+        v[u] = lane < len ? gcand[(int64_t)c * C + lane] : make_uint2(0, 0);
       }
 #pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (dst[u] >= 0) cand_sh[dst[u]] = v[u];
+      // lists longer than one piece
+#pragma unroll 1
       for (int u = 0; u < 8; ++u) {
-        const int g = base + u * kSelThreads + tid;
-        if (g < m) cand_sh[g] = v[u];
+        const int c = c0 + u * kSelWaves;
+        const int len = c < nchunks ? off_sh[c + 1] - off_sh[c] : 0;
+        for (int j = 64 + lane; j < len; j += 64) cand_sh[off_sh[c] + j] = gcand[(int64_t)c * C + j];
       }
     }
     __syncthreads();
-    select_core<true>(a, qi, m, kprime, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh, red);
+    radix_select<true>(m, kprime, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh, red, tau,
+                       ties_needed);
+    write_winners<true>(a, qi, m, tau, ties_needed, cand_sh, gcand, off_sh, nchunks, scan_sh);
   } else {
-    select_core<false>(a, qi, m, kprime, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh, red);
+    radix_select<false>(m, kprime, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh, red, tau,
+                        ties_needed);
+    write_winners<false>(a, qi, m, tau, ties_needed, cand_sh, gcand, off_sh, nchunks, scan_sh);
   }
 }
 

@@ -10,11 +10,10 @@
 namespace csa {
 
 // ---------------------------------------------------------------- compress
-struct CompressLaunch {
-  int ratio, batch;
-  const int32_t* ctx_lens;
-  const int32_t* cu_new;
-  int total_new;
+constexpr int kMaxCompressJobs = 4;  // compressor instances one launch can run
+
+struct CompressJob {
+  int ratio;
   const void* new_raw;
   int raw_dtype;
   const int32_t* cu_entries;
@@ -26,6 +25,15 @@ struct CompressLaunch {
   const csa_cache* state;
   const csa_cache* out;
   const csa_cache* swa;
+};
+
+struct CompressLaunch {
+  int batch;
+  const int32_t* ctx_lens;
+  const int32_t* cu_new;
+  int total_new;
+  int num_jobs;
+  CompressJob jobs[kMaxCompressJobs];
 };
 hipError_t launch_compress(const CompressLaunch& a, hipStream_t stream);
 

@@ -11,8 +11,9 @@ import torch
 
 import ctypes
 
-from . import (OK, CsaError, PagedCache, compress_insert, dtype_code, index_score, index_select,
-               index_workspace_size, lib, sparse_attn_decode, sparse_attn_workspace_size)
+from . import (OK, CompressJob, CsaError, PagedCache, compress_insert, compress_insert_many,
+               compress_jobs_array, dtype_code, index_score, index_select, index_workspace_size, lib,
+               sparse_attn_decode, sparse_attn_workspace_size)
 
 CACHE_KEYS = ("kv", "swa", "state", "idx", "idx_state")
 
@@ -60,6 +61,24 @@ class Step:
         c = self.cfg
         compress_insert(c.ratio, g["ctx_lens"], g["cu_new"], g["new_raw"], g["cu_entries"], g["logits"],
                         g["state"], g["kv"], g["swa"], g.get("gamma"), c.eps, c.rope_base, 64)
+
+    def _jobs(self, g) -> list:
+        c = self.cfg
+        jobs = []
+        if "compress" in c.stages:
+            jobs.append(CompressJob(c.ratio, g["new_raw"], g["cu_entries"], g["logits"], g["state"], g["kv"],
+                                    g["swa"], g.get("gamma"), c.eps, c.rope_base, 64))
+        if "compress_idx" in c.stages:
+            jobs.append(CompressJob(4, g["new_idx_raw"], g["cu_entries"], g["idx_logits"], g["idx_state"],
+                                    g["idx"], None, None, c.eps, c.rope_base, 64))
+        return jobs
+
+    def compress_all(self, g=None):
+        """Every compressor of the step (main KV with window rows, indexer keys) in one launch."""
+        g = g or self.g
+        jobs = self._jobs(g)
+        if jobs:
+            compress_insert_many(g["ctx_lens"], g["cu_new"], g["new_raw"].shape[0], jobs)
 
     def compress_idx(self, g=None):
         g = g or self.g
@@ -128,19 +147,12 @@ class Step:
             refs.append(r)
             return r
         B = g["ctx_lens"].shape[0] if "ctx_lens" in g else g["cu_q"].shape[0] - 1
-        if "compress" in c.stages:
-            calls.append(("compress", L.csa_compress_insert, (
-                c.ratio, B, g["ctx_lens"].data_ptr(), g["cu_new"].data_ptr(), g["new_raw"].shape[0],
-                g["new_raw"].data_ptr(), dtype_code(g["new_raw"].dtype), g["cu_entries"].data_ptr(),
-                g["logits"].shape[0], g["logits"].data_ptr(),
-                None if g.get("gamma") is None else g["gamma"].data_ptr(), c.eps, c.rope_base, 64,
-                cache(g["state"]), cache(g["kv"]), cache(g["swa"]))))
-        if "compress_idx" in c.stages:
-            calls.append(("compress_idx", L.csa_compress_insert, (
-                4, B, g["ctx_lens"].data_ptr(), g["cu_new"].data_ptr(), g["new_idx_raw"].shape[0],
-                g["new_idx_raw"].data_ptr(), dtype_code(g["new_idx_raw"].dtype), g["cu_entries"].data_ptr(),
-                g["idx_logits"].shape[0], g["idx_logits"].data_ptr(), None, c.eps, c.rope_base, 64,
-                cache(g["idx_state"]), cache(g["idx"]), None)))
+        jobs = self._jobs(g)
+        if jobs:  # every compressor of the step in one launch
+            arr = compress_jobs_array(jobs)
+            refs.extend([jobs, arr])
+            calls.append(("compress", L.csa_compress_insert_many, (
+                B, g["ctx_lens"].data_ptr(), g["cu_new"].data_ptr(), g["new_raw"].shape[0], len(jobs), arr)))
         total_q = g["q_pos"].shape[0]
         if "index" in c.stages:
             calls.append(("index_score", L.csa_index_score, (
@@ -183,10 +195,7 @@ class Step:
     def run(self, g=None, with_lse: bool = True):
         """The whole step, in stage order, on the current stream."""
         st = self.cfg.stages
-        if "compress" in st:
-            self.compress(g)
-        if "compress_idx" in st:
-            self.compress_idx(g)
+        self.compress_all(g)
         if "index" in st:
             self.index_score(g)
             self.index_select(g)

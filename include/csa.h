@@ -146,6 +146,35 @@ int csa_compress_insert(csa_stream_t stream, int ratio, int batch,
                         const csa_cache* state, const csa_cache* out, const csa_cache* swa);
 
 /*
+ * csa_compress_insert_many -- several compressor instances over the same new tokens in one
+ * launch: for example a c4a layer's main-KV compressor (d = 576, with window rows) and its
+ * indexer-key compressor (d = 128), which [vLLM-V4] section 3 part 2 runs as separate
+ * instances per head dimension.  Every job computes exactly what csa_compress_insert computes
+ * with the call's ctx_lens / cu_new / total_new and the job's own arguments (its own ratio,
+ * entry offsets, logits, caches, dtype and RoPE settings).  1 <= num_jobs <= 4; `jobs` is a
+ * host array.  The jobs must not write the same cache rows.  Returns the first job's error if
+ * any job is rejected (nothing is launched then).
+ */
+typedef struct csa_compress_job {
+  int32_t            ratio;          /* 4 or 128 */
+  const void*        new_raw;        /* [total_new][dim] of raw_dtype */
+  int32_t            raw_dtype;      /* CSA_F32 or CSA_BF16 */
+  const int32_t*     cu_entries;     /* [batch+1] prefix sums of this job's emitted entries */
+  int32_t            total_entries;  /* cu_entries[batch] (host) */
+  const float*       gate_logits;    /* [total_entries][coff * ratio] */
+  const float*       gamma;          /* [dim] or NULL (= 1) */
+  float              eps, rope_base;
+  int32_t            rope_dims;
+  const csa_cache*   state;          /* host descriptors, as in csa_compress_insert */
+  const csa_cache*   out;
+  const csa_cache*   swa;            /* or NULL */
+} csa_compress_job;
+
+int csa_compress_insert_many(csa_stream_t stream, int batch, const int32_t* ctx_lens,
+                             const int32_t* cu_new, int total_new, int num_jobs,
+                             const csa_compress_job* jobs);
+
+/*
  * csa_index_topk -- indexer score and top-k over c4a entries ([vLLM-V4]
  * section 2: DeepSeek Sparse Attention, the query attends to the top-k
  * compressed tokens; appendix: causality 4j + 3 <= t and default k).

@@ -95,3 +95,20 @@ def test_validation_rejects_before_launch(csa):
     bad = list(args)
     bad[21] = 8
     assert L.csa_sparse_attn_decode(*bad) == csa.EWORKSPACE
+
+
+def test_compress_many_validation(csa):
+    """csa_compress_insert_many rejects an empty or oversized job list and a bad job before
+    launching (fake, never dereferenced pointers)."""
+    L = csa.lib()
+    st = csa._CCache(1, None, csa.BF16, 576, 256, 10, 1, 8)
+    out = csa._CCache(1, None, csa.BF16, 576, 64, 10, 1, 8)
+    P = ctypes.pointer
+    job = csa._CJob(4, 1, csa.BF16, 1, 1, 1, None, 1e-6, 1e4, 64, P(st), P(out), None)
+    arr = (csa._CJob * 5)(*([job] * 5))
+    assert L.csa_compress_insert_many(None, 1, 1, 1, 1, 0, arr) == csa.EINVAL
+    assert L.csa_compress_insert_many(None, 1, 1, 1, 1, 5, arr) == csa.EINVAL
+    bad = (csa._CJob * 2)(job, csa._CJob(5, 1, csa.BF16, 1, 1, 1, None, 1e-6, 1e4, 64, P(st), P(out), None))
+    assert L.csa_compress_insert_many(None, 1, 1, 1, 1, 2, bad) == csa.EINVAL
+    mismatch = (csa._CJob * 1)(csa._CJob(4, 1, csa.F32, 1, 1, 1, None, 1e-6, 1e4, 64, P(st), P(out), None))
+    assert L.csa_compress_insert_many(None, 1, 1, 1, 1, 1, mismatch) == csa.EINVAL
