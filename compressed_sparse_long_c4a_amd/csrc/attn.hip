@@ -339,8 +339,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial(Args a) {
       z[j] = rs[j] != 0.f ? sacc[j] * rs[j] * a.sm_scale2 : -INFINITY;
       mloc = fmaxf(mloc, z[j]);
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+    mloc = rows_reduce(mloc, [](float x, float y) { return fmaxf(x, y); });
     // move a head's reference only when this block's maximum exceeds it by more than kSlack
     // (always when it has none yet); P = 2^(z - m_ref) <= 2^kSlack stays far from overflow
     const bool move = mloc > m_ref + kSlack;
@@ -413,8 +412,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial(Args a) {
   }
 
   // ---- merge the row groups through LDS: per head M = max_g m_g, f_g = 2^(m_g - M)
-  float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
-  l_tot += __shfl_xor(l_tot, 32, kWave);
+  const float l_tot = rows_reduce(l_run, [](float x, float y) { return x + y; });
   if (dq == 0 && lg == 0) {
     ml_sh[ri][ln][0] = m_ref;
     ml_sh[ri][ln][1] = l_tot;

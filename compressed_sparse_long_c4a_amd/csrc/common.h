@@ -139,17 +139,73 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// ---------------------------------------------------------------- reductions
+// ---------------------------------------------------------------- cross-lane operations
+// Reductions and scans inside a wave use DPP lane moves and the gfx950 permlane swaps (VALU
+// instructions), not ds_bpermute: a wave-wide sum costs a few cycles per step instead of an LDS
+// round trip.  Every lane of the wave must be active.
+
+__device__ __forceinline__ uint32_t as_u32(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ uint32_t as_u32(uint32_t v) { return v; }
+__device__ __forceinline__ uint32_t as_u32(int v) { return (uint32_t)v; }
+template <typename T> __device__ __forceinline__ T from_u32(uint32_t v) { return __builtin_bit_cast(T, v); }
+
+// Value of lane (l xor 16) and of lane (l xor 32) combined by op over the four 16-lane rows:
+// every lane gets op over lanes {l mod 16 + 16 r}.  (permlane16_swap pairs rows 0-1 and 2-3,
+// permlane32_swap the halves; with both operands equal, op of the two results is the pairwise
+// combination in every lane.)
+template <typename T, typename Op>
+__device__ __forceinline__ T rows_reduce(T v, Op op) {
+  const auto a = __builtin_amdgcn_permlane16_swap(as_u32(v), as_u32(v), false, false);
+  v = op(from_u32<T>(a[0]), from_u32<T>(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
+  return op(from_u32<T>(b[0]), from_u32<T>(b[1]));
+}
+
+// DPP move of src within 16-lane rows (lanes without a source read 0).
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp(T v) {
+  return from_u32<T>(__builtin_amdgcn_update_dpp(0u, as_u32(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8
+constexpr int kDppRowMirror = 0x140;   // lane i <-> 15 - i within 16
+template <int N> constexpr int kDppRowShr = 0x110 + N;
+
+// op over the whole wave; every lane gets the result.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, dpp<kDppQuadXor1>(v));
+  v = op(v, dpp<kDppQuadXor2>(v));
+  v = op(v, dpp<kDppHalfMirror>(v));
+  v = op(v, dpp<kDppRowMirror>(v));
+  return rows_reduce(v, op);
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](float x, float y) { return x + y; });
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce(v, [](uint32_t x, uint32_t y) { return min(x, y); });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce(v, [](uint32_t x, uint32_t y) { return max(x, y); });
+}
+
+// Inclusive prefix sum over the wave (lane order).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp<kDppRowShr<1>>(x);
+  x += dpp<kDppRowShr<2>>(x);
+  x += dpp<kDppRowShr<4>>(x);
+  x += dpp<kDppRowShr<8>>(x);
+  const int t0 = __builtin_amdgcn_readlane(x, 15);
+  const int t1 = __builtin_amdgcn_readlane(x, 31);
+  const int t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? t0 : 0) + (row > 1 ? t1 : 0) + (row > 2 ? t2 : 0);
 }
 
 // Sum / max over a 256-thread block; every thread gets the result.  `sh` holds >= 4 floats.
@@ -174,12 +230,7 @@ __device__ __forceinline__ float block_max256(float v, float* sh) {
 // `sh` holds >= 5 ints.
 __device__ __forceinline__ int block_exscan256(int v, int* sh, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x / kWave;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_incl_scan(v);
   __syncthreads();
   if (lane == 63) sh[w] = incl;
   __syncthreads();

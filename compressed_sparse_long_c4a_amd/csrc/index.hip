@@ -59,12 +59,7 @@ __device__ void pick_bin_wave0(const uint32_t* hist, int need, int* out) {
     hb[i] = hist[255 - 4 * lane - i];
     local += hb[i];
   }
-  uint32_t incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = (uint32_t)wave_incl_scan((int)local);
   const unsigned long long hit = __ballot(incl >= (uint32_t)need);
   const int first = hit ? __ffsll(hit) - 1 : 63;
   if (lane == first) {
@@ -83,16 +78,14 @@ __device__ void pick_bin_wave0(const uint32_t* hist, int need, int* out) {
 }
 
 __device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  v = wave_min_u32(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   return min(min(red[0], red[1]), min(red[2], red[3]));
 }
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  v = wave_max_u32(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -229,8 +222,7 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
       for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) sacc = fmaf(wt[mt][jj], fmaxf(acc[mt][jj], 0.f), sacc);
-      sacc += __shfl_xor(sacc, 16, kWave);
-      sacc += __shfl_xor(sacc, 32, kWave);
+      sacc = rows_reduce(sacc, [](float x, float y) { return x + y; });
       sacc *= kg.scale[u];
       // tile < C / 16 always, so every lane's slot is inside this chunk's workspace slice
       const int eloc = tile * 16 + ln;
@@ -343,8 +335,7 @@ __device__ uint32_t query_tau_lo(const SelArgs& a, int qi, int n, uint32_t* red)
   if (kc > C) return 0u;
   uint32_t mn = 0xFFFFFFFFu;
   for (int c = threadIdx.x; c < m_full; c += 256) mn = min(mn, a.bounds[(int64_t)qi * a.chunks + c]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+  mn = wave_min_u32(mn);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mn;
   __syncthreads();
@@ -360,12 +351,12 @@ __global__ __launch_bounds__(256) void index_filter(SelArgs a) {
   if (j0 >= n) return;
   const int kprime = min(a.k, n);
   if (kprime == n) return;  // select takes every candidate directly
-  const uint32_t tau = query_tau_lo(a, qi, n, red);
   const int nloc = (int)min((int64_t)C, n - j0);
   static_assert(C == 256 * 8, "the filter gives each of its 256 threads 8 entries of a chunk");
   const int base = threadIdx.x * 8;
   uint32_t key[8];
   int cnt = 0;
+  // the chunk's scores are loaded before the bounds: both trips overlap
   const float* sc = a.scores + (int64_t)qi * a.n_cap + j0;
   if (base + 8 <= nloc) {
     const float4 v0 = *(const float4*)(sc + base), v1 = *(const float4*)(sc + base + 4);
@@ -376,6 +367,7 @@ __global__ __launch_bounds__(256) void index_filter(SelArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) key[i] = (base + i < nloc) ? f2key(sc[base + i]) : 0u;
   }
+  const uint32_t tau = query_tau_lo(a, qi, n, red);
 #pragma unroll
   for (int i = 0; i < 8; ++i) cnt += (base + i < nloc && key[i] >= tau) ? 1 : 0;
   int total;
@@ -398,12 +390,7 @@ constexpr int kBins = 1 << kDigitBits;
 // sh holds 2 kSelWaves ints.
 __device__ __forceinline__ int2 sel_exscan2(int v0, int v1, int* sh, int* tot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int i0 = v0, i1 = v1;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y0 = __shfl_up(i0, o, kWave), y1 = __shfl_up(i1, o, kWave);
-    if (lane >= o) { i0 += y0; i1 += y1; }
-  }
+  const int i0 = wave_incl_scan(v0), i1 = wave_incl_scan(v1);
   __syncthreads();
   if (lane == 63) { sh[w] = i0; sh[kSelWaves + w] = i1; }
   __syncthreads();
@@ -434,38 +421,48 @@ __device__ __forceinline__ uint2 cand_at(const uint2* cand_sh, const uint2* gcan
   return gcand[(int64_t)lo * C + (g - off_sh[lo])];
 }
 
-// The kprime-th largest key among the m candidates and how many keys equal to it are
-// selected: a most-significant-digit radix select on d = key - lo over the candidates' own
-// range, 11 bits per pass (keys decided by a higher digit drop out of later passes).
+// Min and max key over the candidates (block-wide).
 template <bool IN_LDS>
-__device__ void radix_select(int m, int kprime, const uint2* cand_sh, const uint2* gcand,
-                             const int* off_sh, int nchunks, uint32_t* hist, int* misc,
-                             int* scan_sh, uint32_t* red, uint32_t& tau, int& ties_needed) {
+__device__ void cand_range(int m, const uint2* cand_sh, const uint2* gcand, const int* off_sh,
+                           int nchunks, uint32_t* red, uint32_t& lo, uint32_t& hi) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  uint32_t lo = 0xFFFFFFFFu, nhi = 0xFFFFFFFFu;  // min key, min of ~key
+  lo = 0xFFFFFFFFu;
+  uint32_t nhi = 0xFFFFFFFFu;  // min of ~key
   for (int g = tid; g < m; g += kSelThreads) {
     const uint32_t key = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x;
     lo = min(lo, key);
     nhi = min(nhi, ~key);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, kWave));
-    nhi = min(nhi, (uint32_t)__shfl_xor((int)nhi, o, kWave));
-  }
+  lo = wave_min_u32(lo);
+  nhi = wave_min_u32(nhi);
   if (lane == 0) { red[w] = lo; red[kSelWaves + w] = nhi; }
   __syncthreads();
   lo = red[0];
   nhi = red[kSelWaves];
 #pragma unroll
   for (int i = 1; i < kSelWaves; ++i) { lo = min(lo, red[i]); nhi = min(nhi, red[kSelWaves + i]); }
-  const uint32_t range = ~nhi - lo;
+  hi = ~nhi;
+  __syncthreads();  // red is reused
+}
+
+// The kprime-th largest key among the m candidates (all in [lo, hi]) and how many keys equal to
+// it are selected: a most-significant-digit radix select on d = key - lo, 11 bits per pass (keys
+// decided by a higher digit drop out of later passes).  Once the bin that holds the answer has
+// at most 64 keys, one wave ranks them directly instead of further passes.
+template <bool IN_LDS>
+__device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, const uint2* cand_sh,
+                             const uint2* gcand, const int* off_sh, int nchunks, uint32_t* hist,
+                             int* misc, int* scan_sh, uint32_t* small_sh, uint32_t& tau,
+                             int& ties_needed) {
+  const int tid = threadIdx.x, lane = tid & 63;
   uint32_t prefix = 0;  // decided high digits of d
   int need = kprime;
-  for (int top = bit_len(range); top > 0; top -= kDigitBits) {
+  int top = bit_len(hi - lo);
+  while (top > 0) {
     const int shift = max(0, top - kDigitBits);
     hist[tid] = 0;
     hist[tid + kSelThreads] = 0;
+    if (tid == 0) misc[2] = 0;
     __syncthreads();
     for (int g = tid; g < m; g += kSelThreads) {
       const uint32_t d = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x - lo;
@@ -481,14 +478,44 @@ __device__ void radix_select(int m, int kprime, const uint2* cand_sh, const uint
       const bool first = before + (int)h0 >= need;
       misc[0] = first ? kBins - 1 - 2 * tid : kBins - 2 - 2 * tid;
       misc[1] = first ? before : before + (int)h0;
+      misc[3] = (int)(first ? h0 : h1);  // keys in that bin
     }
     __syncthreads();
     prefix |= (uint32_t)misc[0] << shift;
     need -= misc[1];
+    const int in_bin = misc[3];
+    top = shift;
+    if (top > 0 && in_bin <= 64) {
+      // collect the bin's keys (any order) and rank them in one wave
+      for (int g = tid; g < m; g += kSelThreads) {
+        const uint32_t key = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x;
+        if (((key - lo) >> top) == (prefix >> top)) small_sh[atomicAdd(&misc[2], 1)] = key;
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        const uint32_t mine = lane < in_bin ? small_sh[lane] : 0u;
+        int greater = 0, equal = 0;
+        for (int i = 0; i < in_bin; ++i) {
+          const uint32_t other = (uint32_t)__builtin_amdgcn_readlane((int)mine, i);
+          greater += other > mine;
+          equal += other == mine;
+        }
+        // the need-th largest: greater < need <= greater + equal (any holder of it may write)
+        if (lane < in_bin && greater < need && need <= greater + equal) {
+          misc[0] = (int)(mine - lo);
+          misc[1] = need - greater;
+        }
+      }
+      __syncthreads();
+      tau = (uint32_t)misc[0] + lo;
+      ties_needed = misc[1];
+      __syncthreads();
+      return;
+    }
     __syncthreads();
   }
-  tau = prefix + lo;  // the kprime-th largest key
-  ties_needed = need; // how many keys equal to tau are selected
+  tau = prefix + lo;   // the kprime-th largest key
+  ties_needed = need;  // how many keys equal to tau are selected
 }
 
 // Winners in ascending entry order: the candidates are stored in entry order, so one scan of
@@ -529,6 +556,7 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
   __shared__ uint2 cand_sh[kSelCap];
   __shared__ int off_sh[kMaxChunks + 1];
   __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t small_sh[64];
   __shared__ int misc[4];
   __shared__ int scan_sh[2 * kSelWaves];
   __shared__ uint32_t red[2 * kSelWaves];
@@ -551,48 +579,48 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
     }
     return;
   }
-  // offsets of the per-chunk candidate lists (one chunk per thread)
   const int nchunks = (n + C - 1) / C;
+  const uint2* gcand = a.cand + (int64_t)qi * a.n_cap;
+  // one trip: the per-chunk candidate counts (one chunk per thread) and, speculatively, the
+  // first 64 slots of every chunk's list (wave w reads chunks w, w + 16, ..., up to 8 of them;
+  // slots past a list's end hold stale data of this query's slice and are discarded)
+  constexpr int kPieces = 8;
+  uint2 v[kPieces];
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u) {
+    const int c = min(w + u * kSelWaves, nchunks - 1);
+    v[u] = gcand[(int64_t)c * C + lane];
+  }
   const int cnt = tid < nchunks ? a.cand_cnt[(int64_t)qi * a.chunks + tid] : 0;
   int tot2[2];
   off_sh[tid] = sel_exscan2(cnt, 0, scan_sh, tot2).x;
   const int m = tot2[0];
   if (tid == 0) off_sh[nchunks] = m;
   __syncthreads();
-  const uint2* gcand = a.cand + (int64_t)qi * a.n_cap;
-  uint32_t tau;
+  uint32_t tau, lo, hi;
   int ties_needed;
   if (m <= kSelCap) {
-    // gather the lists densely into LDS: wave w copies chunks w, w + 16, ...; up to eight
-    // 64-candidate pieces per wave are loaded before any is stored
-    for (int c0 = w; c0 < nchunks; c0 += 8 * kSelWaves) {
-      uint2 v[8];
-      int dst[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = c0 + u * kSelWaves;
-        const int len = c < nchunks ? off_sh[c + 1] - off_sh[c] : 0;
-        dst[u] = lane < len ? off_sh[c] + lane : -1;
-        v[u] = lane < len ? gcand[(int64_t)c * C + lane] : make_uint2(0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (dst[u] >= 0) cand_sh[dst[u]] = v[u];
-      // lists longer than one piece
-#pragma unroll 1
-      for (int u = 0; u < 8; ++u) {
-        const int c = c0 + u * kSelWaves;
-        const int len = c < nchunks ? off_sh[c + 1] - off_sh[c] : 0;
-        for (int j = 64 + lane; j < len; j += 64) cand_sh[off_sh[c] + j] = gcand[(int64_t)c * C + j];
-      }
+    for (int u = 0; u < kPieces; ++u) {
+      const int c = w + u * kSelWaves;
+      const int len = c < nchunks ? off_sh[c + 1] - off_sh[c] : 0;
+      if (lane < len) cand_sh[off_sh[c] + lane] = v[u];
+    }
+    // the rest: chunks beyond the first 8 per wave, and lists longer than 64
+    for (int c = w; c < nchunks; c += kSelWaves) {
+      const int len = off_sh[c + 1] - off_sh[c];
+      const int j0 = c < w + kPieces * kSelWaves ? 64 : 0;
+      for (int j = j0 + lane; j < len; j += 64) cand_sh[off_sh[c] + j] = gcand[(int64_t)c * C + j];
     }
     __syncthreads();
-    radix_select<true>(m, kprime, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh, red, tau,
-                       ties_needed);
+    cand_range<true>(m, cand_sh, gcand, off_sh, nchunks, red, lo, hi);
+    radix_select<true>(m, kprime, lo, hi, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh,
+                       small_sh, tau, ties_needed);
     write_winners<true>(a, qi, m, tau, ties_needed, cand_sh, gcand, off_sh, nchunks, scan_sh);
   } else {
-    radix_select<false>(m, kprime, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh, red, tau,
-                        ties_needed);
+    cand_range<false>(m, cand_sh, gcand, off_sh, nchunks, red, lo, hi);
+    radix_select<false>(m, kprime, lo, hi, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh,
+                        small_sh, tau, ties_needed);
     write_winners<false>(a, qi, m, tau, ties_needed, cand_sh, gcand, off_sh, nchunks, scan_sh);
   }
 }
