@@ -461,6 +461,271 @@ __global__ __launch_bounds__(kThreads) void attn_partial(Args a) {
   }
 }
 
+// ---- fp8 rows with bf16 queries.  A row group's four waves take one 64-row chunk per step:
+// wave dq computes S^T for one 16-row tile over the full row width (no partial sums to
+// exchange), the per-head block maximum and then P are exchanged through LDS, and every wave
+// accumulates O^T over all 64 rows for its own quarter of the dimensions.  The waves stage the
+// fp8 codes they loaded in LDS; PV reads them back transposed with ds_read_b64_tr_b8 (a 16-lane
+// group reads an 8-row x 16-byte block and lane l receives column l of the 8 rows), which is
+// exactly the A operand of V^T with K = 32 rows: the MFMA rows of the two QK tiles of a 32-row
+// half are interleaved (tile h holds rows 8 (r / 4) + 4 h + r % 4) so that after the softmax
+// lane (head j, group g) holds P of rows 8 g .. 8 g + 7 -- the B operand -- with no movement.
+// P is applied as bf16 hi and lo parts in two MFMAs.
+constexpr int kChunk = 64;  // rows of a row group per step (four 16-row QK tiles)
+template <int DIM>
+__global__ __launch_bounds__(kThreads) void attn_partial_fp8(Args a) {
+  constexpr int NKS = DIM / 32;        // k-steps of a full row
+  constexpr int MQ = (NKS + 3) / 4;    // k-steps of the largest quarter
+  constexpr int VROW = DIM + 16;       // LDS bytes per staged row
+  __shared__ int64_t off_sh[kRowsPerSplit];
+  __shared__ float scale_sh[kRowsPerSplit];  // row scale; 0 marks padding
+  constexpr int V_BYTES = kRG * kChunk * VROW;
+  constexpr int MERGE_BYTES = 16 * (DIM + 4) * 4;
+  __shared__ __attribute__((aligned(16))) char v_sh[V_BYTES > MERGE_BYTES ? V_BYTES : MERGE_BYTES];
+  __shared__ uint4 p_sh[kRG][4][64];         // P of each QK tile, lane-major {4 hi, 4 lo} bf16
+  __shared__ float mx_sh[kRG][4][16];        // per-head maximum logit of each QK tile
+  __shared__ float ml_sh[kRG][4][16][2];     // (m, l) of every wave, for the final merge
+
+  const int s = blockIdx.x, hg = blockIdx.y, qi = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15, lg = lane >> 4;
+  // wave (dq, rg): waves 2 dq + rg, so a SIMD holds waves of a long and a short quarter
+  const int dq = wv >> 1, rg = wv & 1;
+  const int nkq = NKS / 4 + (dq < NKS % 4 ? 1 : 0);   // k-steps of quarter dq
+  const int k0 = dq * (NKS / 4) + min(dq, NKS % 4);    // its first k-step
+  const int H = a.n_heads;
+  const char* kvbase = (const char*)a.kv.rows;
+  const int r_begin = s * a.rows_per_split;
+
+  // ---- loads that need nothing else: query position, sequence, list entries, Q^T
+  const int t = a.q_pos[qi];
+  const int b = seq_of_wave(a.cu_q, a.batch, qi);
+  constexpr int RPT = kRowsPerSplit / kThreads;
+  int ent[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int pos = r_begin + min(tid + kThreads * u, a.rows_per_split - 1);
+    ent[u] = a.has_topk ? a.topk[(int64_t)qi * a.k + min(pos, a.k - 1)] : pos;
+  }
+  // QK runs over the dimensions in the order the rows are loaded: lane group lg of 64-byte
+  // segment m holds dims 64 m + 16 lg .. +15 (one 16-byte load), k-step 2 m + e takes the half
+  // e of them.  Q^T, the B operand, follows the same order: lane (head ln, group lg) holds
+  // q[h][64 m + 16 lg + 8 e + 0..7] for k-step 2 m + e.
+  bf16x8 qb[NKS];
+  {
+    const int h = 16 * hg + ln;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      const int d0 = 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1);
+      if (h < H) v = *(const uint4*)((const uint16_t*)a.q + ((int64_t)qi * H + h) * DIM + d0);
+      qb[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  const int n_vis = min((t + 1) / a.ratio, a.n_max);
+  const int n_c = a.has_topk ? a.k : n_vis;
+  const int n_w = min(a.window, t + 1);
+  const int n_rows = n_c + n_w;
+  const int nrows = (n_w > 0 || n_vis > 0) ? max(0, min(a.rows_per_split, n_rows - r_begin)) : 0;
+  // padded to whole steps; rows_per_split is a multiple of kRG * kChunk
+  const int nrows_p = (nrows + kRG * kChunk - 1) / (kRG * kChunk) * (kRG * kChunk);
+
+  // ---- resolve the split's rows once: offset and scale; padding rows -> a safe row with
+  // scale 0
+  if (nrows > 0) {
+    const int64_t swa_off = (int64_t)((uintptr_t)a.swa.rows - (uintptr_t)a.kv.rows);
+    const int64_t safe = n_w > 0 ? swa_off + phys_row(a.swa, b, t) * DIM
+                                 : phys_row(a.kv, b, max(n_vis - 1, 0)) * DIM;
+    int64_t prow[RPT];
+    bool is_kv[RPT], ok[RPT];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int i = tid + kThreads * u;
+      const int pos = r_begin + min(i, nrows - 1);
+      is_kv[u] = pos < n_c;
+      ok[u] = i < nrows && (!is_kv[u] || (ent[u] >= 0 && ent[u] < n_vis));
+      prow[u] = is_kv[u] ? (ok[u] ? phys_row(a.kv, b, ent[u]) : 0)
+                         : phys_row(a.swa, b, t - n_w + 1 + (pos - n_c));
+    }
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int i = tid + kThreads * u;
+      if (i < nrows_p) {
+        const int64_t base = is_kv[u] ? 0 : swa_off;
+        const float sc = ok[u] ? (is_kv[u] ? a.kv.scales : a.swa.scales)[prow[u]] : 0.f;
+        off_sh[i] = ok[u] ? base + prow[u] * DIM : safe;
+        scale_sh[i] = sc;
+      }
+    }
+  }
+
+  f32x4 o[2 * MQ];  // O^T of quarter dq (dim tile 16 d .. +15 x 16 heads), over the group's rows
+#pragma unroll
+  for (int dt = 0; dt < 2 * MQ; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_run = 0.f;  // per head: reference exponent (log2 units), this
+                                         // wave's share of the sum of P
+  __syncthreads();
+
+  const int steps = nrows_p / (kRG * kChunk);
+  const int kb = dq >> 1, hh = dq & 1;  // this wave's QK tile: half kb, interleave hh
+  const int my_row = 32 * kb + 8 * (ln >> 2) + 4 * hh + (ln & 3);  // chunk row of QK row ln
+  const int srow0 = 32 * kb + 8 * lg + 4 * hh;                       // chunk rows of P lanes
+  char* vrow_w = v_sh + (rg * kChunk + my_row) * VROW + 16 * lg;
+  constexpr int NSEG = DIM / 64;  // 64-byte segments of a row
+  struct Tile { uint4 d[NSEG]; };
+  // Row loads are unconditional (clamped to the last step; with no step at all, row 0 of the
+  // cache).
+  auto load_block = [&](int i, Tile& tl) {
+    const int c = rg + kRG * max(0, min(i, steps - 1));
+    const int64_t off = steps > 0 ? off_sh[kChunk * c + my_row] : 0;
+    const char* row = kvbase + off + 16 * lg;
+#pragma unroll
+    for (int m = 0; m < NSEG; ++m) tl.d[m] = *(const uint4*)(row + 64 * m);
+  };
+
+  auto step = [&](int i, Tile& tl) {
+    const int r0 = kChunk * (rg + kRG * i);
+    // S^T of this wave's 16 rows over the full width, two accumulation chains
+    f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int m = 0; m < NSEG; ++m) {
+      acc2[0] = mfma16x16x32(fp8x8_to_bf16x8(tl.d[m].x, tl.d[m].y), qb[2 * m], acc2[0]);
+      acc2[1] = mfma16x16x32(fp8x8_to_bf16x8(tl.d[m].z, tl.d[m].w), qb[2 * m + 1], acc2[1]);
+    }
+    const f32x4 sacc = acc2[0] + acc2[1];
+    const float4 rs4 = *(const float4*)&scale_sh[r0 + srow0];
+    const float rs[4] = {rs4.x, rs4.y, rs4.z, rs4.w};
+    float z[4];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      z[j] = rs[j] != 0.f ? sacc[j] * rs[j] * a.sm_scale2 : -INFINITY;
+      mloc = fmaxf(mloc, z[j]);
+    }
+    mloc = rows_reduce(mloc, [](float x, float y) { return fmaxf(x, y); });
+    if (lg == 0) mx_sh[rg][dq][ln] = mloc;
+    barrier_lds();  // #1: the four tiles' maxima; every wave is past the previous step's PV
+    // stage this wave's rows (fp8 codes) for PV; the tile is then free for the next chunk,
+    // whose loads overlap this step's softmax and PV
+#pragma unroll
+    for (int m = 0; m < NSEG; ++m) *(uint4*)(vrow_w + 64 * m) = tl.d[m];
+    load_block(i + 1, tl);
+    const float mblk = fmaxf(fmaxf(mx_sh[rg][0][ln], mx_sh[rg][1][ln]), fmaxf(mx_sh[rg][2][ln], mx_sh[rg][3][ln]));
+    // the row group's reference moves only when a block's maximum exceeds it by more than
+    // kSlack (always when it has none yet); the four waves take the same decision
+    const bool move = mblk > m_ref + kSlack;
+    if (__ballot(move)) {
+      const float m_new = move ? mblk : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 2 * MQ; ++dt) o[dt] *= alpha;
+    }
+    uint4 pw;
+    {
+      float pvv[4], psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = z[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[j] - m_ref);
+        psum += p;
+        pvv[j] = p * rs[j];
+      }
+      l_run += psum;
+      bf16x8 hl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const __bf16 hi = (__bf16)pvv[j];
+        hl[j] = hi;
+        hl[4 + j] = (__bf16)(pvv[j] - (float)hi);
+      }
+      pw = __builtin_bit_cast(uint4, hl);
+    }
+    p_sh[rg][dq][lane] = pw;
+    barrier_lds();  // #2: P of the four tiles and the staged rows
+    // O^T += V^T . P^T over the chunk, one 32-row half at a time (P_hi and P_lo MFMAs)
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, p_sh[rg][2 * kh][lane]);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, p_sh[rg][2 * kh + 1][lane]);
+      const bf16x8 phi = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+      const bf16x8 plo = {pa[4], pa[5], pa[6], pa[7], pb[4], pb[5], pb[6], pb[7]};
+      const char* vt = v_sh + (rg * kChunk + 32 * kh + 8 * lg + (ln >> 1)) * VROW + 32 * k0 + 8 * (ln & 1);
+#pragma unroll
+      for (int dt = 0; dt < 2 * MQ; ++dt) {
+        // (a short quarter's two extra tiles re-read its last tile: O^T tiles never written out)
+        const int dtc = dt < 2 * nkq ? dt : 2 * nkq - 1;
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(vt + 16 * dtc));
+        const bf16x8 va = fp8x8_to_bf16x8((uint32_t)raw[0], (uint32_t)raw[1]);
+        o[dt] = mfma16x16x32(va, phi, o[dt]);
+        o[dt] = mfma16x16x32(va, plo, o[dt]);
+      }
+    }
+  };
+
+  {
+    Tile t0;
+    load_block(0, t0);
+    for (int i = 0; i < steps; ++i) step(i, t0);
+  }
+
+  // ---- merge: per head, the row group's l is the sum over its four waves; then the two row
+  // groups are combined with weights 2^(m_g - M)
+  const float l_tot = rows_reduce(l_run, [](float x, float y) { return x + y; });
+  if (lg == 0) {
+    ml_sh[rg][dq][ln][0] = m_ref;
+    ml_sh[rg][dq][ln][1] = l_tot;
+  }
+  __syncthreads();  // also: every wave is done with the staged rows (the merge buffer aliases)
+  float M = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < kRG; ++g) M = fmaxf(M, ml_sh[g][0][ln][0]);
+  const float f = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - M);
+  float (*mb)[DIM + 4] = reinterpret_cast<float (*)[DIM + 4]>(v_sh);
+  float* dst = &mb[ln][32 * k0 + 4 * lg];
+#pragma unroll
+  for (int round = 0; round < kRG; ++round) {
+    if (rg == round) {
+#pragma unroll
+      for (int dt = 0; dt < 2 * MQ; ++dt) {
+        if (dt < 2 * nkq) {
+          float4 v = make_float4(f * o[dt][0], f * o[dt][1], f * o[dt][2], f * o[dt][3]);
+          if (round > 0) {
+            const float4 w = *(const float4*)(dst + 16 * dt);
+            v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+          }
+          *(float4*)(dst + 16 * dt) = v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg;
+  for (int i = tid; i < 16 * DIM / 4; i += kThreads) {
+    const int h = i / (DIM / 4), d = 4 * (i - h * (DIM / 4));
+    *(float4*)(a.part_o + (pbase + h) * DIM + d) = *(const float4*)&mb[h][d];
+  }
+  if (tid < 16) {
+    const int h = tid;
+    float Mh = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < kRG; ++g) Mh = fmaxf(Mh, ml_sh[g][0][h][0]);
+    float L = 0.f;
+#pragma unroll
+    for (int g = 0; g < kRG; ++g) {
+      const float mg = ml_sh[g][0][h][0];
+      if (mg != -INFINITY)
+        L += exp2f(mg - Mh) * (ml_sh[g][0][h][1] + ml_sh[g][1][h][1] + ml_sh[g][2][h][1] + ml_sh[g][3][h][1]);
+    }
+    a.part_ml[(pbase + h) * 2 + 0] = Mh;
+    a.part_ml[(pbase + h) * 2 + 1] = L;
+  }
+}
+
 struct MergeArgs {
   int n_heads, splits, hgp, dim, rope_dims;
   const int32_t* q_pos;
@@ -577,6 +842,16 @@ void launch_q(const Args& args, int qdt, int dim, dim3 grid, hipStream_t stream)
   else launch_dim<DT, CSA_F32>(args, dim, grid, stream);
 }
 
+template <>
+void launch_q<CSA_FP8_E4M3>(const Args& args, int qdt, int dim, dim3 grid, hipStream_t stream) {
+  if (qdt == CSA_BF16) {
+    if (dim == 576) hipLaunchKernelGGL((attn_partial_fp8<576>), grid, dim3(kThreads), 0, stream, args);
+    else hipLaunchKernelGGL((attn_partial_fp8<512>), grid, dim3(kThreads), 0, stream, args);
+  } else {
+    launch_dim<CSA_FP8_E4M3, CSA_F32>(args, dim, grid, stream);
+  }
+}
+
 }  // namespace
 
 AttnPlan attn_plan(int total_q, int n_heads, int ratio, int has_topk, int k, int max_context,
@@ -587,9 +862,10 @@ AttnPlan attn_plan(int total_q, int n_heads, int ratio, int has_topk, int k, int
   p.head_groups = (n_heads + 15) / 16;
   const int64_t blocks32 = std::max<int64_t>(1, (p.max_rows + 31) / 32);
   const int64_t units = (int64_t)total_q * p.head_groups;
-  // aim at one 256-thread workgroup per compute unit (256 CUs), at least 4 blocks per group
+  // aim at one workgroup per compute unit (256 CUs); a split is a whole number of 128-row
+  // steps (the fp8 kernel's step: two row groups of 64 rows)
   int64_t bpw = std::max<int64_t>(4, (blocks32 * units + 255) / 256);
-  bpw = std::min<int64_t>(std::min(bpw, blocks32), kRowsPerSplit / 32);
+  bpw = std::min<int64_t>((std::min(bpw, blocks32) + 3) / 4 * 4, kRowsPerSplit / 32);
   // callers keep max_rows <= kMaxSplits * kRowsPerSplit, so splits <= kMaxSplits
   const int64_t splits = (blocks32 + bpw - 1) / bpw;
   p.splits = (int)splits;
