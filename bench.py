@@ -64,6 +64,15 @@ def algorithmic_bytes(cfg, d) -> dict:
     return out
 
 
+def score_kernel_sha1() -> str:
+    """SHA-1 of the score kernel's source text (from its section comment to the next kernel's),
+    so the counter figures go stale when that kernel changes and only then."""
+    text = open(INDEX_SRC).read()
+    a = text.index("// ---- MFMA score kernel")
+    b = text.index("// ---- float32 queries")
+    return hashlib.sha1(text[a:b].encode()).hexdigest()
+
+
 def counters_traffic():
     """HBM bytes per index-score launch from the committed rocprofv3 counter summary, or None
     when there is none or it was taken from a different version of the kernel source."""
@@ -74,7 +83,7 @@ def counters_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    src_hash = hashlib.sha1(open(INDEX_SRC, "rb").read()).hexdigest()
+    src_hash = score_kernel_sha1()
     if kv.get("source_sha1") != src_hash:
         return None
     try:
