@@ -142,12 +142,15 @@ template <int KEY_DT>
 struct KeyGroup {
   static constexpr int NW = KEY_DT == CSA_FP8_E4M3 ? 2 : 4;  // 16-byte words per lane per tile
   uint4 raw[4][NW];
-  float scale[4];
+  float scale;  // lane (e, g): scale of entry e of the group's tile g
 };
 
 template <int KEY_DT, int HT>
 __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
+  constexpr int QROW = 136;  // bf16 per LDS query row (padded: rows start 16 bytes apart mod 256)
   __shared__ float sc_sh[C];
+  __shared__ __attribute__((aligned(16))) uint16_t q_sh[HT * 16 * QROW];
+  __shared__ __attribute__((aligned(16))) float w_sh[HT * 16];
   __shared__ uint32_t hist[256];
   __shared__ int misc[4];
   __shared__ uint32_t red[4];
@@ -166,6 +169,16 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
   const int nblk = (nloc + 63) >> 6;
   const int32_t* btrow = a.cache.bt + (int64_t)b * a.cache.bt_stride + (j0 >> 6);
   const int32_t my_blk = lane < nblk ? btrow[lane] : 0;
+  // the query (heads x 128 bf16) and head weights are read once per workgroup, 16 bytes per
+  // thread and pass, and shared through LDS
+  uint4 qv[HT];
+  const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)qi * H * 128;
+#pragma unroll
+  for (int p = 0; p < HT; ++p) {
+    const int h = 16 * p + (threadIdx.x >> 4);
+    qv[p] = h < H ? *(const uint4*)(qrow + (int64_t)h * 128 + 8 * (threadIdx.x & 15)) : make_uint4(0, 0, 0, 0);
+  }
+  const float wv_h = threadIdx.x < 16 * HT && threadIdx.x < H ? a.w[(int64_t)qi * H + threadIdx.x] : 0.f;
 
   const int ntiles = (nloc + 15) >> 4;
   bf16x8 qa[HT][4];
@@ -175,30 +188,28 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
   // flight): entries past the chunk's end read the chunk's last row and write their unused
   // scores inside this chunk's own slice of the workspace.
   auto load_group = [&](int gi, KeyGroup<KEY_DT>& kg) {
+    int64_t prow_g = 0;  // row of entry ln of tile lg: one scale load covers the four tiles
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int tile = min(16 * gi + 4 * u + wv, ntiles - 1);
       const int eloc = min(tile * 16 + ln, nloc - 1);
       const int blk = __builtin_amdgcn_readlane(my_blk, min(4 * gi + u, nblk - 1));
       const int64_t prow = ((int64_t)blk << 6) + (eloc & 63);
-      if constexpr (KEY_DT == CSA_FP8_E4M3) {
-        const uint4* src = (const uint4*)((const uint8_t*)a.cache.rows + prow * 128 + 32 * lg);
-        kg.raw[u][0] = src[0];
-        kg.raw[u][1] = src[1];
-        kg.scale[u] = a.cache.scales[prow];
-      } else {
-        const uint4* src = (const uint4*)((const uint16_t*)a.cache.rows + prow * 128 + 32 * lg);
+      prow_g = lg == u ? prow : prow_g;
+      // load i reads one 64-byte half line of each of the tile's 16 rows: lane group lg takes
+      // bytes 64 i + 16 lg .. +15 (the K order of the A operand matches)
+      const uint4* src = (const uint4*)((const uint8_t*)a.cache.rows + prow * (KEY_DT == CSA_FP8_E4M3 ? 128 : 256) + 16 * lg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kg.raw[u][i] = src[i];
-        kg.scale[u] = 1.f;
-      }
+      for (int i = 0; i < NW; ++i) kg.raw[u][i] = src[4 * i];
     }
+    if constexpr (KEY_DT == CSA_FP8_E4M3) kg.scale = a.cache.scales[prow_g];
+    else kg.scale = 1.f;
   };
 
   auto compute_group = [&](int gi, const KeyGroup<KEY_DT>& kg) {
+    float mine = 0.f;  // lane (e, g): score of entry e of tile g
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int tile = 16 * gi + 4 * u + wv;
       bf16x8 kb[4];
       if constexpr (KEY_DT == CSA_FP8_E4M3) {
         const uint32_t wd[8] = {kg.raw[u][0].x, kg.raw[u][0].y, kg.raw[u][0].z, kg.raw[u][0].w,
@@ -223,12 +234,14 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) sacc = fmaf(wt[mt][jj], fmaxf(acc[mt][jj], 0.f), sacc);
       sacc = rows_reduce(sacc, [](float x, float y) { return x + y; });
-      sacc *= kg.scale[u];
-      // tile < C / 16 always, so every lane's slot is inside this chunk's workspace slice
-      const int eloc = tile * 16 + ln;
-      a.scores[(int64_t)qi * a.n_cap + j0 + eloc] = sacc;
-      sc_sh[eloc] = sacc;
+      mine = lg == u ? sacc : mine;
     }
+    mine *= kg.scale;
+    // one store per lane for the four tiles; tile < C / 16 always, so every lane's slot is
+    // inside this chunk's workspace slice
+    const int eloc = (16 * gi + 4 * lg + wv) * 16 + ln;
+    a.scores[(int64_t)qi * a.n_cap + j0 + eloc] = mine;
+    sc_sh[eloc] = mine;
   };
 
   // every chunk runs the same fully unrolled sequence of C / 256 groups with no runtime
@@ -236,23 +249,26 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
   constexpr int NG = C / 256;
   KeyGroup<KEY_DT> kg[2];
   load_group(0, kg[0]);
-  // (issued after the first keys) A operand: lane (head ln of tile mt, group lg) holds
-  // q[h][32 lg + 8 ks + 0..7].
-  const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)qi * H * 128;
+#pragma unroll
+  for (int p = 0; p < HT; ++p)
+    *(uint4*)&q_sh[(16 * p + (threadIdx.x >> 4)) * QROW + 8 * (threadIdx.x & 15)] = qv[p];
+  if (threadIdx.x < 16 * HT) w_sh[threadIdx.x] = wv_h;
+  __syncthreads();
+  // A operand: lane (head ln of tile mt, group lg) holds the dims its key lanes hold for
+  // k-step ks (fp8: 64 (ks / 2) + 16 lg + 8 (ks % 2) + 0..7, the eight codes of half a
+  // 16-byte load; bf16: 32 ks + 8 lg + 0..7, one 16-byte load).
 #pragma unroll
   for (int mt = 0; mt < HT; ++mt) {
-    const int h = 16 * mt + ln;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (h < H) v = *(const uint4*)(qrow + (int64_t)h * 128 + 32 * lg + 8 * ks);
-      qa[mt][ks] = __builtin_bit_cast(bf16x8, v);
+      const int d0 = KEY_DT == CSA_FP8_E4M3 ? 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1) : 32 * ks + 8 * lg;
+      qa[mt][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)&q_sh[(16 * mt + ln) * QROW + d0]);
     }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int hh = 16 * mt + 4 * lg + jj;
-      wt[mt][jj] = hh < H ? a.w[(int64_t)qi * H + hh] : 0.f;
-    }
+    const float4 w4 = *(const float4*)&w_sh[16 * mt + 4 * lg];
+    wt[mt][0] = w4.x;
+    wt[mt][1] = w4.y;
+    wt[mt][2] = w4.z;
+    wt[mt][3] = w4.w;
   }
 
 #pragma unroll
