@@ -508,20 +508,19 @@ __global__ __launch_bounds__(kThreads) void attn_partial_fp8(Args a) {
     const int pos = r_begin + min(tid + kThreads * u, a.rows_per_split - 1);
     ent[u] = a.has_topk ? a.topk[(int64_t)qi * a.k + min(pos, a.k - 1)] : pos;
   }
-  // QK runs over the dimensions in the order the rows are loaded: lane group lg of 64-byte
-  // segment m holds dims 64 m + 16 lg .. +15 (one 16-byte load), k-step 2 m + e takes the half
-  // e of them.  Q^T, the B operand, follows the same order: lane (head ln, group lg) holds
-  // q[h][64 m + 16 lg + 8 e + 0..7] for k-step 2 m + e.
-  bf16x8 qb[NKS];
-  {
-    const int h = 16 * hg + ln;
+  // the workgroup's 16 query heads are read once, 16 bytes per thread and pass, and staged in
+  // LDS (in the row buffer, which the first step fills only after every wave's first QK)
+  constexpr int QS = DIM + 8;                  // bf16 per staged query row (padded)
+  constexpr int QV = 16 * DIM / 8;             // 16-byte pieces of the tile
+  constexpr int QP = (QV + kThreads - 1) / kThreads;
+  static_assert(16 * QS * 2 <= (int)sizeof(v_sh), "query tile fits the row buffer");
+  uint4 qv[QP];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      const int d0 = 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1);
-      if (h < H) v = *(const uint4*)((const uint16_t*)a.q + ((int64_t)qi * H + h) * DIM + d0);
-      qb[ks] = __builtin_bit_cast(bf16x8, v);
-    }
+  for (int p = 0; p < QP; ++p) {
+    const int i = p * kThreads + tid;
+    const int h = i / (DIM / 8), c = i - h * (DIM / 8);
+    qv[p] = i < QV && 16 * hg + h < H ? *(const uint4*)((const uint16_t*)a.q + ((int64_t)qi * H + 16 * hg + h) * DIM + 8 * c)
+                                     : make_uint4(0, 0, 0, 0);
   }
 
   const int n_vis = min((t + 1) / a.ratio, a.n_max);
@@ -561,12 +560,31 @@ __global__ __launch_bounds__(kThreads) void attn_partial_fp8(Args a) {
     }
   }
 
+  {
+    uint16_t* q_sh = (uint16_t*)v_sh;
+#pragma unroll
+    for (int p = 0; p < QP; ++p) {
+      const int i = p * kThreads + tid;
+      const int h = i / (DIM / 8), c = i - h * (DIM / 8);
+      if (i < QV) *(uint4*)&q_sh[h * QS + 8 * c] = qv[p];
+    }
+  }
   f32x4 o[2 * MQ];  // O^T of quarter dq (dim tile 16 d .. +15 x 16 heads), over the group's rows
 #pragma unroll
   for (int dt = 0; dt < 2 * MQ; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_run = 0.f;  // per head: reference exponent (log2 units), this
                                          // wave's share of the sum of P
   __syncthreads();
+  // QK runs over the dimensions in the order the rows are loaded: lane group lg of 64-byte
+  // segment m holds dims 64 m + 16 lg .. +15 (one 16-byte load), k-step 2 m + e takes the half
+  // e of them.  Q^T, the B operand, follows the same order: lane (head ln, group lg) holds
+  // q[h][64 m + 16 lg + 8 e + 0..7] for k-step 2 m + e.
+  bf16x8 qb[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int d0 = 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1);
+    qb[ks] = __builtin_bit_cast(bf16x8, *(const uint4*)((const uint16_t*)v_sh + ln * QS + d0));
+  }
 
   const int steps = nrows_p / (kRG * kChunk);
   const int kb = dq >> 1, hh = dq & 1;  // this wave's QK tile: half kb, interleave hh
