@@ -505,7 +505,10 @@ __device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, const 
       // collect the bin's keys (any order) and rank them in one wave
       for (int g = tid; g < m; g += kSelThreads) {
         const uint32_t key = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x;
-        if (((key - lo) >> top) == (prefix >> top)) small_sh[atomicAdd(&misc[2], 1)] = key;
+        if (((key - lo) >> top) == (prefix >> top)) {
+          const int slot = atomicAdd(&misc[2], 1);
+          if (slot < 64) small_sh[slot] = key;  // (at most in_bin <= 64 keys match)
+        }
       }
       __syncthreads();
       if (tid < kWave) {
@@ -561,8 +564,10 @@ __device__ void write_winners(const SelArgs& a, int qi, int m, uint32_t tau, int
     bool take = c.x > tau;
     if (c.x == tau) { take = tr < ties_needed; ++tr; }
     if (take) {
-      out[pos] = (int32_t)c.y;
-      if (outs) outs[pos] = key2f(c.x);
+      if (pos < a.k) {  // (exactly k' keys are taken: a guard, never a branch taken)
+        out[pos] = (int32_t)c.y;
+        if (outs) outs[pos] = key2f(c.x);
+      }
       ++pos;
     }
   }
