@@ -148,12 +148,12 @@ struct KeyGroup {
 template <int KEY_DT, int HT>
 __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
   constexpr int QROW = 136;  // bf16 per LDS query row (padded: rows start 16 bytes apart mod 256)
-  __shared__ float sc_sh[C];
+  __shared__ __attribute__((aligned(16))) float sc_sh[C];
   __shared__ __attribute__((aligned(16))) uint16_t q_sh[HT * 16 * QROW];
   __shared__ __attribute__((aligned(16))) float w_sh[HT * 16];
   __shared__ uint32_t hist[256];
   __shared__ int misc[4];
-  __shared__ uint32_t red[4];
+  __shared__ uint32_t red[4], red2[4];
   const int chunk = blockIdx.x, qi = blockIdx.y;
   const int b = seq_of_wave(a.cu_q, a.batch, qi);
   const int n = query_entries(a.q_pos, qi, a.n_max);
@@ -179,6 +179,7 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
     qv[p] = h < H ? *(const uint4*)(qrow + (int64_t)h * 128 + 8 * (threadIdx.x & 15)) : make_uint4(0, 0, 0, 0);
   }
   const float wv_h = threadIdx.x < 16 * HT && threadIdx.x < H ? a.w[(int64_t)qi * H + threadIdx.x] : 0.f;
+  hist[threadIdx.x] = 0u;  // (the bound's histogram; ordered by the barrier after the query copy)
 
   const int ntiles = (nloc + 15) >> 4;
   bf16x8 qa[HT][4];
@@ -206,6 +207,7 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
     else kg.scale = 1.f;
   };
 
+  uint32_t lane_keys[C / 256];  // the lane's key of each group: eight distinct entries
   auto compute_group = [&](int gi, const KeyGroup<KEY_DT>& kg) {
     float mine = 0.f;  // lane (e, g): score of entry e of tile g
 #pragma unroll
@@ -237,11 +239,10 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
       mine = lg == u ? sacc : mine;
     }
     mine *= kg.scale;
-    // one store per lane for the four tiles; tile < C / 16 always, so every lane's slot is
-    // inside this chunk's workspace slice
+    // tile < C / 16 always, so every lane's slot is inside this chunk
     const int eloc = (16 * gi + 4 * lg + wv) * 16 + ln;
-    a.scores[(int64_t)qi * a.n_cap + j0 + eloc] = mine;
     sc_sh[eloc] = mine;
+    lane_keys[gi] = f2key(mine);
   };
 
   // every chunk runs the same fully unrolled sequence of C / 256 groups with no runtime
@@ -276,8 +277,51 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
     if (gi + 1 < NG) load_group(gi + 1, kg[(gi + 1) & 1]);
     compute_group(gi, kg[gi & 1]);
   }
+  // Epilogue.  Every lane holds 8 distinct entries' keys (entries past a partial chunk's end
+  // repeat its last entry), so the chunk's key range is reduced from registers, and the same
+  // barrier that completes sc_sh publishes the per-wave ranges.
+  static_assert(C / 256 == 8, "eight groups per chunk");
+  uint32_t klo = lane_keys[0], khi = lane_keys[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    klo = min(klo, lane_keys[i]);
+    khi = max(khi, lane_keys[i]);
+  }
+  klo = wave_min_u32(klo);
+  khi = wave_max_u32(khi);
+  if (lane == 0) {
+    red[wv] = klo;
+    red2[wv] = khi;
+  }
   __syncthreads();
-  finish_chunk(a, qi, chunk, n, nloc, sc_sh, hist, misc, red);
+  // the chunk's scores leave in full lines, 16 bytes per thread and pass
+  {
+    float4* dst = (float4*)(a.scores + (int64_t)qi * a.n_cap + j0);
+#pragma unroll
+    for (int p = 0; p < C / 1024; ++p)
+      dst[p * 256 + threadIdx.x] = *(const float4*)&sc_sh[4 * (p * 256 + threadIdx.x)];
+  }
+  // the bound (full chunks): one 256-bin histogram over the chunk's own key range; the bound
+  // is the lower edge of the bin that holds the kc-th largest key
+  const int kprime = min(a.k, n);
+  const int m_full = n / C;
+  if (nloc == C && kprime < n && m_full > 0) {
+    const int kc = (kprime + m_full - 1) / m_full;
+    if (kc > C) {
+      if (threadIdx.x == 0) a.bounds[(int64_t)qi * a.chunks + chunk] = 0u;
+      return;
+    }
+    const uint32_t lo = min(min(red[0], red[1]), min(red[2], red[3]));
+    const uint32_t hi = max(max(red2[0], red2[1]), max(red2[2], red2[3]));
+    const int shift = max(0, bit_len(hi - lo) - 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) atomicAdd(&hist[((lane_keys[i] - lo) >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wv == 0) {
+      pick_bin_wave0(hist, kc, misc);  // (the crossing lane writes misc[0])
+      if (lane == 0) a.bounds[(int64_t)qi * a.chunks + chunk] = lo + ((uint32_t)misc[0] << shift);
+    }
+  }
 }
 
 // ---- float32 queries (any key dtype): plain per-entry dot products.
