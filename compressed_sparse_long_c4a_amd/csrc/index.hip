@@ -382,7 +382,7 @@ struct SelArgs {
   const float* scores;
   const uint32_t* bounds;
   uint2* cand;
-  int32_t* cand_cnt;
+  int4* cand_info;  // per chunk: candidate count, least and largest candidate key
   int32_t* topk_idx;
   float* topk_score;
 };
@@ -403,7 +403,7 @@ __device__ uint32_t query_tau_lo(const SelArgs& a, int qi, int n, uint32_t* red)
 }
 
 __global__ __launch_bounds__(256) void index_filter(SelArgs a) {
-  __shared__ uint32_t red[4];
+  __shared__ uint32_t red[4], kmin_sh[4], kmax_sh[4];
   __shared__ int scan_sh[8];
   const int chunk = blockIdx.x, qi = blockIdx.y;
   const int n = query_entries(a.q_pos, qi, a.n_max);
@@ -428,16 +428,32 @@ __global__ __launch_bounds__(256) void index_filter(SelArgs a) {
     for (int i = 0; i < 8; ++i) key[i] = (base + i < nloc) ? f2key(sc[base + i]) : 0u;
   }
   const uint32_t tau = query_tau_lo(a, qi, n, red);
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;  // the chunk's candidate key range, for the select
 #pragma unroll
-  for (int i = 0; i < 8; ++i) cnt += (base + i < nloc && key[i] >= tau) ? 1 : 0;
+  for (int i = 0; i < 8; ++i) {
+    const bool c = base + i < nloc && key[i] >= tau;
+    cnt += c ? 1 : 0;
+    kmin = c ? min(kmin, key[i]) : kmin;
+    kmax = c ? max(kmax, key[i]) : kmax;
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if ((threadIdx.x & 63) == 0) {
+    kmin_sh[threadIdx.x >> 6] = kmin;
+    kmax_sh[threadIdx.x >> 6] = kmax;
+  }
   int total;
-  int off = block_exscan256(cnt, scan_sh, &total);
+  int off = block_exscan256(cnt, scan_sh, &total);  // (its barriers also publish kmin/kmax_sh)
   uint2* dst = a.cand + (int64_t)qi * a.n_cap + j0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     if (base + i < nloc && key[i] >= tau) dst[off++] = make_uint2(key[i], (uint32_t)(j0 + base + i));
   }
-  if (threadIdx.x == 0) a.cand_cnt[(int64_t)qi * a.chunks + chunk] = total;
+  if (threadIdx.x == 0) {
+    const uint32_t lo = min(min(kmin_sh[0], kmin_sh[1]), min(kmin_sh[2], kmin_sh[3]));
+    const uint32_t hi = max(max(kmax_sh[0], kmax_sh[1]), max(kmax_sh[2], kmax_sh[3]));
+    a.cand_info[(int64_t)qi * a.chunks + chunk] = make_int4(total, (int)lo, (int)hi, 0);
+  }
 }
 
 // ---- select: exact k-th largest among the candidates, winners in ascending entry order.
@@ -479,30 +495,6 @@ __device__ __forceinline__ uint2 cand_at(const uint2* cand_sh, const uint2* gcan
     if (off_sh[mid] <= g) lo = mid; else hi = mid - 1;
   }
   return gcand[(int64_t)lo * C + (g - off_sh[lo])];
-}
-
-// Min and max key over the candidates (block-wide).
-template <bool IN_LDS>
-__device__ void cand_range(int m, const uint2* cand_sh, const uint2* gcand, const int* off_sh,
-                           int nchunks, uint32_t* red, uint32_t& lo, uint32_t& hi) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  lo = 0xFFFFFFFFu;
-  uint32_t nhi = 0xFFFFFFFFu;  // min of ~key
-  for (int g = tid; g < m; g += kSelThreads) {
-    const uint32_t key = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x;
-    lo = min(lo, key);
-    nhi = min(nhi, ~key);
-  }
-  lo = wave_min_u32(lo);
-  nhi = wave_min_u32(nhi);
-  if (lane == 0) { red[w] = lo; red[kSelWaves + w] = nhi; }
-  __syncthreads();
-  lo = red[0];
-  nhi = red[kSelWaves];
-#pragma unroll
-  for (int i = 1; i < kSelWaves; ++i) { lo = min(lo, red[i]); nhi = min(nhi, red[kSelWaves + i]); }
-  hi = ~nhi;
-  __syncthreads();  // red is reused
 }
 
 // The kprime-th largest key among the m candidates (all in [lo, hi]) and how many keys equal to
@@ -656,13 +648,25 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
     const int c = min(w + u * kSelWaves, nchunks - 1);
     v[u] = gcand[(int64_t)c * C + lane];
   }
-  const int cnt = tid < nchunks ? a.cand_cnt[(int64_t)qi * a.chunks + tid] : 0;
+  // and, in the same trip, each chunk's candidate count and key range (from the filter)
+  const int4 inf = tid < nchunks ? a.cand_info[(int64_t)qi * a.chunks + tid] : make_int4(0, -1, 0, 0);
+  const int cnt = min(max(inf.x, 0), C);
+  uint32_t lo = wave_min_u32((uint32_t)inf.y), hi = wave_max_u32((uint32_t)inf.z);
+  if (lane == 0) {
+    red[w] = lo;
+    red[kSelWaves + w] = hi;
+  }
   int tot2[2];
-  off_sh[tid] = sel_exscan2(cnt, 0, scan_sh, tot2).x;
+  off_sh[tid] = sel_exscan2(cnt, 0, scan_sh, tot2).x;  // (its barriers also publish red)
   const int m = tot2[0];
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) {
+    lo = min(lo, red[i]);
+    hi = max(hi, red[kSelWaves + i]);
+  }
   if (tid == 0) off_sh[nchunks] = m;
   __syncthreads();
-  uint32_t tau, lo, hi;
+  uint32_t tau;
   int ties_needed;
   if (m <= kSelCap) {
 #pragma unroll
@@ -678,12 +682,10 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
       for (int j = j0 + lane; j < len; j += 64) cand_sh[off_sh[c] + j] = gcand[(int64_t)c * C + j];
     }
     __syncthreads();
-    cand_range<true>(m, cand_sh, gcand, off_sh, nchunks, red, lo, hi);
     radix_select<true>(m, kprime, lo, hi, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh,
                        small_sh, tau, ties_needed);
     write_winners<true>(a, qi, m, tau, ties_needed, cand_sh, gcand, off_sh, nchunks, scan_sh);
   } else {
-    cand_range<false>(m, cand_sh, gcand, off_sh, nchunks, red, lo, hi);
     radix_select<false>(m, kprime, lo, hi, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh,
                         small_sh, tau, ties_needed);
     write_winners<false>(a, qi, m, tau, ties_needed, cand_sh, gcand, off_sh, nchunks, scan_sh);
@@ -730,7 +732,7 @@ size_t index_workspace_bytes(int total_q, int max_context, int k) {
   add((size_t)total_q * n_cap * sizeof(float));
   add((size_t)total_q * chunks * sizeof(uint32_t));
   add((size_t)total_q * n_cap * sizeof(uint2));
-  add((size_t)total_q * chunks * sizeof(int32_t));
+  add((size_t)total_q * chunks * sizeof(int4));
   return bytes;
 }
 
@@ -745,7 +747,7 @@ IndexWorkspace index_workspace_carve(void* ws, int total_q, int max_context, int
   w.scores = (float*)take((size_t)total_q * w.n_cap * sizeof(float));
   w.bounds = (uint32_t*)take((size_t)total_q * w.chunks * sizeof(uint32_t));
   w.cand = (uint2*)take((size_t)total_q * w.n_cap * sizeof(uint2));
-  w.cand_cnt = (int32_t*)take((size_t)total_q * w.chunks * sizeof(int32_t));
+  w.cand_info = (int4*)take((size_t)total_q * w.chunks * sizeof(int4));
   return w;
 }
 
@@ -774,7 +776,7 @@ hipError_t launch_index_select(const IndexLaunch& a, int32_t* topk_idx, float* t
   s.scores = ws.scores;
   s.bounds = ws.bounds;
   s.cand = ws.cand;
-  s.cand_cnt = ws.cand_cnt;
+  s.cand_info = ws.cand_info;
   s.topk_idx = topk_idx;
   s.topk_score = topk_score;
   hipLaunchKernelGGL(index_filter, dim3(ws.chunks, a.total_q), dim3(256), 0, stream, s);

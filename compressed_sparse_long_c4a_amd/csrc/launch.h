@@ -45,7 +45,7 @@ struct IndexWorkspace {
   float* scores;       // [total_q][n_cap]
   uint32_t* bounds;    // [total_q][chunks]   key lower bound of each full chunk
   uint2* cand;         // [total_q][n_cap]    (key, entry) candidates, chunk-sparse
-  int32_t* cand_cnt;   // [total_q][chunks]
+  int4* cand_info;     // [total_q][chunks]   candidate count, least and largest candidate key
   int chunks;          // per query
   int64_t n_cap;       // chunks * kIndexChunk
 };
