@@ -499,27 +499,33 @@ __device__ __forceinline__ uint2 cand_at(const uint2* cand_sh, const uint2* gcan
 
 // The kprime-th largest key among the m candidates (all in [lo, hi]) and how many keys equal to
 // it are selected: a most-significant-digit radix select on d = key - lo, 11 bits per pass (keys
-// decided by a higher digit drop out of later passes).  Once the bin that holds the answer has
+// decided by a higher digit drop out of later passes).  With `have`, hist already holds the
+// first pass's histogram (built while the candidates were gathered).  Once the bin that holds the answer has
 // at most 64 keys, one wave ranks them directly instead of further passes.
 template <bool IN_LDS>
-__device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, const uint2* cand_sh,
-                             const uint2* gcand, const int* off_sh, int nchunks, uint32_t* hist,
-                             int* misc, int* scan_sh, uint32_t* small_sh, uint32_t& tau,
-                             int& ties_needed) {
+__device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, bool have,
+                             const uint2* cand_sh, const uint2* gcand, const int* off_sh,
+                             int nchunks, uint32_t* hist, int* misc, int* scan_sh,
+                             uint32_t* small_sh, uint32_t& tau, int& ties_needed) {
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t prefix = 0;  // decided high digits of d
   int need = kprime;
   int top = bit_len(hi - lo);
   while (top > 0) {
     const int shift = max(0, top - kDigitBits);
-    hist[tid] = 0;
-    hist[tid + kSelThreads] = 0;
-    if (tid == 0) misc[2] = 0;
-    __syncthreads();
-    for (int g = tid; g < m; g += kSelThreads) {
-      const uint32_t d = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x - lo;
-      if (top >= 32 || (d >> top) == (prefix >> top)) atomicAdd(&hist[(d >> shift) & (kBins - 1)], 1u);
+    if (have) {
+      if (tid == 0) misc[2] = 0;
+    } else {
+      hist[tid] = 0;
+      hist[tid + kSelThreads] = 0;
+      if (tid == 0) misc[2] = 0;
+      __syncthreads();
+      for (int g = tid; g < m; g += kSelThreads) {
+        const uint32_t d = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x - lo;
+        if (top >= 32 || (d >> top) == (prefix >> top)) atomicAdd(&hist[(d >> shift) & (kBins - 1)], 1u);
+      }
     }
+    have = false;
     __syncthreads();
     // thread t owns bins 2047 - 2t and 2046 - 2t (descending); the thread whose running count
     // from the top crosses `need` holds the bin of the kprime-th largest key
@@ -638,6 +644,8 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
   }
   const int nchunks = (n + C - 1) / C;
   const uint2* gcand = a.cand + (int64_t)qi * a.n_cap;
+  hist[tid] = 0;  // (published by the barriers of the count scan below)
+  hist[tid + kSelThreads] = 0;
   // one trip: the per-chunk candidate counts (one chunk per thread) and, speculatively, the
   // first 64 slots of every chunk's list (wave w reads chunks w, w + 16, ..., up to 8 of them;
   // slots past a list's end hold stale data of this query's slice and are discarded)
@@ -669,24 +677,30 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
   uint32_t tau;
   int ties_needed;
   if (m <= kSelCap) {
+    // the gather also builds the first radix pass's histogram (bins of the candidates' range)
+    const int shift0 = max(0, bit_len(hi - lo) - kDigitBits);
+    auto put = [&](int slot, uint2 c) {
+      cand_sh[slot] = c;
+      atomicAdd(&hist[min((c.x - lo) >> shift0, (uint32_t)(kBins - 1))], 1u);
+    };
 #pragma unroll
     for (int u = 0; u < kPieces; ++u) {
       const int c = w + u * kSelWaves;
       const int len = c < nchunks ? off_sh[c + 1] - off_sh[c] : 0;
-      if (lane < len) cand_sh[off_sh[c] + lane] = v[u];
+      if (lane < len) put(off_sh[c] + lane, v[u]);
     }
     // the rest: chunks beyond the first 8 per wave, and lists longer than 64
     for (int c = w; c < nchunks; c += kSelWaves) {
       const int len = off_sh[c + 1] - off_sh[c];
       const int j0 = c < w + kPieces * kSelWaves ? 64 : 0;
-      for (int j = j0 + lane; j < len; j += 64) cand_sh[off_sh[c] + j] = gcand[(int64_t)c * C + j];
+      for (int j = j0 + lane; j < len; j += 64) put(off_sh[c] + j, gcand[(int64_t)c * C + j]);
     }
     __syncthreads();
-    radix_select<true>(m, kprime, lo, hi, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh,
+    radix_select<true>(m, kprime, lo, hi, true, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh,
                        small_sh, tau, ties_needed);
     write_winners<true>(a, qi, m, tau, ties_needed, cand_sh, gcand, off_sh, nchunks, scan_sh);
   } else {
-    radix_select<false>(m, kprime, lo, hi, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh,
+    radix_select<false>(m, kprime, lo, hi, false, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh,
                         small_sh, tau, ties_needed);
     write_winners<false>(a, qi, m, tau, ties_needed, cand_sh, gcand, off_sh, nchunks, scan_sh);
   }
