@@ -92,6 +92,73 @@ def counters_traffic():
         return None
 
 
+def time_launches(fn, reps: int = 50, replays: int = 5) -> float:
+    """Mean microseconds per call of fn (one launch each): `reps` calls captured in a HIP graph
+    and replayed, HIP events around the replays (no host launch cost in the figure)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * replays)
+
+
+def next_rows(cfg) -> dict:
+    """Rows beyond the step, each timed on its own: the query norm + RoPE + window-key kernel
+    (csa_q_norm_rope_swa) at the decode step's shapes and at the chunked prefill's."""
+    import torch
+    import compressed_sparse_long_c4a_amd as csa
+    dev = "cuda"
+    out = {}
+    # (name, sequences, queries and new rows per sequence, heads, context after the step, window dtype)
+    shapes = [("decode_1m_b4", 4, 1, 128, 1 << 20, "fp8"),
+              ("prefill_4k_on_64k", 1, 4096, 64, 65536 + 4096, "bf16")]
+    for name, batch, per, heads, ctx_after, swa_dt in shapes:
+        total = batch * per
+        q = torch.randn(total, heads, 576, device=dev).to(torch.bfloat16)
+        q_pos = torch.tensor([ctx_after - per + i for _ in range(batch) for i in range(per)],
+                             dtype=torch.int32, device=dev)
+        ctx_lens = torch.full((batch,), ctx_after - per, dtype=torch.int32, device=dev)
+        cu_new = torch.arange(0, total + 1, per, dtype=torch.int32, device=dev)
+        raw = torch.randn(total, 576, device=dev).to(torch.bfloat16)
+        nblk = (ctx_after + 255) // 256
+        bt = torch.arange(batch * nblk, dtype=torch.int32, device=dev).view(batch, nblk)
+        if swa_dt == "fp8":
+            rows = torch.zeros(batch * nblk, 256, 576, dtype=torch.uint8, device=dev)
+            scales = torch.ones(batch * nblk, 256, device=dev)
+        else:
+            rows = torch.zeros(batch * nblk, 256, 576, dtype=torch.bfloat16, device=dev)
+            scales = None
+        swa = csa.PagedCache(rows, bt, scales)
+        q_out = torch.empty_like(q)
+        gamma = torch.rand(576, device=dev) + 0.5
+        fn = lambda: csa.q_norm_rope_swa(q_pos, q, q_out=q_out, gamma=gamma, ctx_lens=ctx_lens,
+                                         cu_new=cu_new, new_raw=raw, swa=swa)
+        us = time_launches(fn)
+        row_out = 576 + 4 if swa_dt == "fp8" else 576 * 2
+        # queries in and out (bf16), raw rows in (bf16), window rows out, the gain
+        nbytes = 2 * q.numel() * 2 + raw.numel() * 2 + total * row_out + 576 * 4
+        out[name] = {"kernel": "q_norm_rope_swa_kernel", "queries": total, "heads": heads,
+                     "window_rows": total, "window_dtype": swa_dt, "us_per_launch": round(us, 2),
+                     "algorithmic_bytes": nbytes, "achieved_gbs": round(nbytes / us / 1e3, 1),
+                     "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del q, q_out, raw, rows, scales, swa
+    return out
+
+
 def clone_caches(g: dict) -> dict:
     from compressed_sparse_long_c4a_amd import PagedCache
     from compressed_sparse_long_c4a_amd.pipeline import CACHE_KEYS
@@ -126,6 +193,8 @@ def main() -> int:
     ap.add_argument("--config", default=None, help="workload name (default: the 1M c4a fp8 decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the separate timings of the rows beyond the step")
     ap.add_argument("--two-stream", action="store_true",
                     help="also time the schedule with the main-KV compress on a second stream")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -279,6 +348,9 @@ def main() -> int:
             "traffic": counters_traffic(), "launch_us": round(score_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": ab["index_score"],
         }
+    if not args.no_next_rows:
+        print("# timing the rows beyond the step", file=sys.stderr, flush=True)
+        result["next_rows"] = {"q_norm_rope_swa": next_rows(cfg)}
     if not args.no_cpu_baseline:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, d)

@@ -80,6 +80,8 @@ _SIGNATURES = {
     "csa_index_topk": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _CP, _I, _P, _P, _P, _SZ]),
     "csa_index_score": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _CP, _I, _P, _SZ]),
     "csa_index_select": (_I, [_P, _I, _P, _P, _I, _I, _I, _P, _P, _P, _SZ]),
+    "csa_q_norm_rope_swa": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _P, _F, _F, _I, _I, _P, _P, _I,
+                                 _P, _I, _CP]),
     "csa_sparse_attn_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "csa_sparse_attn_decode": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _CP, _I, _P, _I, _CP, _I,
                                     _F, _F, _I, _P, _P, _P, _SZ]),
@@ -214,6 +216,38 @@ def compress_insert(ratio: int, ctx_lens: torch.Tensor, cu_new: torch.Tensor, ne
         _ptr(new_raw), dtype_code(new_raw.dtype), cu_entries.data_ptr(), gate_logits.shape[0],
         _ptr(gate_logits), _ptr(gamma), eps, rope_base, rope_dims, _cref(state), _cref(out), _cref(swa))
     _check(st, "csa_compress_insert")
+
+
+def q_norm_rope_swa(q_pos: torch.Tensor, q: torch.Tensor, q_out: torch.Tensor | None = None,
+                    gamma: torch.Tensor | None = None, eps: float = 1e-6, rope_base: float = 10000.0,
+                    rope_dims: int = 64, ctx_lens: torch.Tensor | None = None,
+                    cu_new: torch.Tensor | None = None, new_raw: torch.Tensor | None = None,
+                    swa: PagedCache | None = None) -> torch.Tensor:
+    """Query heads RMS-normalised and rotated at their positions (returned, in q's dtype); with
+    a window cache, every new raw row stored there as RoPE_p(x_p).  One launch."""
+    _dev(q_pos, "q_pos", torch.int32, 1)
+    _dev(q, "q", (torch.float32, torch.bfloat16), 3)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _dev(q_out, "q_out", q.dtype, 3)
+    if q_out.shape != q.shape or q.shape[0] != q_pos.shape[0]:
+        raise ValueError("q_out must match q, and q_pos must have one entry per query")
+    if gamma is not None:
+        _dev(gamma, "gamma", torch.float32, 1)
+    batch, total_new, raw_dt = 0, 0, F32
+    if swa is not None:
+        _dev(ctx_lens, "ctx_lens", torch.int32, 1)
+        _dev(cu_new, "cu_new", torch.int32, 1)
+        _dev(new_raw, "new_raw", (torch.float32, torch.bfloat16), 2)
+        batch, total_new, raw_dt = ctx_lens.shape[0], new_raw.shape[0], dtype_code(new_raw.dtype)
+        if cu_new.shape[0] != batch + 1:
+            raise ValueError("cu_new needs batch + 1 entries")
+    st = lib().csa_q_norm_rope_swa(
+        _stream(), q.shape[0], _ptr(q_pos), _ptr(q), _ptr(q_out), dtype_code(q.dtype), q.shape[1],
+        q.shape[2], _ptr(gamma), eps, rope_base, rope_dims, batch, _ptr(ctx_lens), _ptr(cu_new),
+        total_new, _ptr(new_raw), raw_dt, _cref(swa))
+    _check(st, "csa_q_norm_rope_swa")
+    return q_out
 
 
 class CompressJob:

@@ -187,6 +187,45 @@ size_t csa_sparse_attn_workspace_size(int total_q, int n_heads, int dim, int rat
   return csa::attn_workspace_bytes(total_q, n_heads, dim, p);
 }
 
+int csa_q_norm_rope_swa(csa_stream_t stream, int total_q, const int32_t* q_pos, const void* q_in,
+                        void* q_out, int q_dtype, int n_heads, int dim, const float* q_gamma,
+                        float eps, float rope_base, int rope_dims, int batch,
+                        const int32_t* ctx_lens, const int32_t* cu_new, int total_new,
+                        const void* new_raw, int raw_dtype, const csa_cache* swa) {
+  if (total_q < 0 || n_heads < 1) return CSA_EINVAL;
+  if (q_dtype != CSA_F32 && q_dtype != CSA_BF16) return CSA_ENOTSUP;
+  if (dim < 8 || dim > 1024 || (dim & 7)) return CSA_ENOTSUP;
+  if (rope_dims < 8 || (rope_dims & 7) || rope_dims > dim || rope_dims > 128) return CSA_EINVAL;
+  if (!(eps >= 0.f) || !(rope_base > 0.f)) return CSA_EINVAL;
+  if (total_q > 0 && (!q_pos || !q_in || !q_out)) return CSA_EINVAL;
+  if (swa) {
+    if (batch < 1 || total_new < 0 || !ctx_lens || !cu_new) return CSA_EINVAL;
+    if (raw_dtype != CSA_F32 && raw_dtype != CSA_BF16) return CSA_ENOTSUP;
+    if (total_new > 0 && !new_raw) return CSA_EINVAL;
+    if (!cache_ok(swa, 256, dim)) return CSA_EINVAL;
+  }
+  csa::QNormLaunch L{};
+  L.total_q = total_q;
+  L.q_pos = q_pos;
+  L.q_in = q_in;
+  L.q_out = q_out;
+  L.q_dtype = q_dtype;
+  L.n_heads = n_heads;
+  L.dim = dim;
+  L.q_gamma = q_gamma;
+  L.eps = eps;
+  L.rope_base = rope_base;
+  L.rope_dims = rope_dims;
+  L.batch = batch;
+  L.ctx_lens = ctx_lens;
+  L.cu_new = cu_new;
+  L.total_new = swa ? total_new : 0;
+  L.new_raw = new_raw;
+  L.raw_dtype = raw_dtype;
+  L.swa = swa;
+  return hip_status(csa::launch_q_norm_rope_swa(L, (hipStream_t)stream));
+}
+
 int csa_sparse_attn_decode(csa_stream_t stream, int batch, const int32_t* cu_q,
                            const int32_t* q_pos, int total_q, int max_context, const void* q,
                            int q_dtype, int n_heads, const csa_cache* kv, int ratio,

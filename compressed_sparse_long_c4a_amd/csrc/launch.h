@@ -37,6 +37,26 @@ struct CompressLaunch {
 };
 hipError_t launch_compress(const CompressLaunch& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- query norm + window keys
+struct QNormLaunch {
+  int total_q;
+  const int32_t* q_pos;
+  const void* q_in;
+  void* q_out;
+  int q_dtype, n_heads, dim;
+  const float* q_gamma;
+  float eps, rope_base;
+  int rope_dims;
+  int batch;
+  const int32_t* ctx_lens;
+  const int32_t* cu_new;
+  int total_new;
+  const void* new_raw;
+  int raw_dtype;
+  const csa_cache* swa;  // NULL: queries only
+};
+hipError_t launch_q_norm_rope_swa(const QNormLaunch& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- indexer
 // Entries handled by one workgroup of the score / filter kernels.
 constexpr int kIndexChunk = 2048;

@@ -221,6 +221,41 @@ int csa_index_select(csa_stream_t stream, int batch, const int32_t* cu_q, const 
                      void* workspace, size_t workspace_bytes);
 
 /*
+ * csa_q_norm_rope_swa -- query normalisation + RoPE and the window keys in one launch
+ * ([vLLM-V4] section 3 part 2, third fusion: fused Q norm + KV RoPE + K insert, one warp
+ * per query head or key head, no cross-warp communication).
+ *
+ * For every query i and head h (the pages name the operations only; the reading is the
+ * compressor's RMSNorm and RoPE applied per query head):
+ *   n = q_in[i][h] / sqrt(mean(q_in[i][h]^2) + eps) * q_gamma   (over the head's dim values);
+ *   q_out[i][h] = RoPE_{q_pos[i]}(n): the last rope_dims dimensions rotated in consecutive
+ *                 pairs (2j, 2j+1) by q_pos[i] * rope_base^(-2j/rope_dims) (angles in
+ *                 float64), rounded to q_dtype.
+ * If `swa` is not NULL, every new raw row x_p -- sequence b held ctx_lens[b] raw tokens and
+ * receives new_raw rows [cu_new[b], cu_new[b+1]) at positions ctx_lens[b], ... -- is stored
+ * in `swa` at p as RoPE_p(x_p) in swa->dtype (fp8: scale = amax/448, codes RNE): the same rows
+ * csa_compress_insert writes when it is given a window cache.
+ *
+ * Arguments:
+ *   total_q >= 0.  q_pos [total_q] int32 >= 0.  q_in, q_out [total_q][n_heads][dim] of
+ *   q_dtype (F32 or BF16), not overlapping.  n_heads >= 1.  dim a multiple of 8, <= 1024.
+ *   q_gamma [dim] float32 or NULL (= 1).  eps >= 0.  rope_base > 0.  rope_dims a multiple
+ *   of 8, 8..min(dim, 128).
+ *   Window keys (read only when swa != NULL): batch >= 1, ctx_lens [batch] int32 >= 0,
+ *   cu_new [batch+1] int32 prefix sums with cu_new[batch] = total_new (host), new_raw
+ *   [total_new][dim] of raw_dtype (F32 or BF16); swa: rows_per_block 256, the same dim,
+ *   any dtype, not overlapping new_raw or q_out.
+ * total_q = 0 and total_new = 0 are valid; with neither, nothing is launched.
+ * Returns CSA_EINVAL for inconsistent arguments, CSA_ENOTSUP for an unsupported dtype or
+ * dim; a zero-length array may be NULL.
+ */
+int csa_q_norm_rope_swa(csa_stream_t stream, int total_q, const int32_t* q_pos, const void* q_in,
+                        void* q_out, int q_dtype, int n_heads, int dim, const float* q_gamma,
+                        float eps, float rope_base, int rope_dims, int batch,
+                        const int32_t* ctx_lens, const int32_t* cu_new, int total_new,
+                        const void* new_raw, int raw_dtype, const csa_cache* swa);
+
+/*
  * csa_sparse_attn_decode -- multi-query attention with K = V over the selected
  * compressed entries plus the uncompressed sliding window, then inverse RoPE
  * ([vLLM-V4] section 2: shared K/V, top-k sparse attention, window of 128;

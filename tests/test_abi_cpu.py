@@ -112,3 +112,40 @@ def test_compress_many_validation(csa):
     assert L.csa_compress_insert_many(None, 1, 1, 1, 1, 2, bad) == csa.EINVAL
     mismatch = (csa._CJob * 1)(csa._CJob(4, 1, csa.F32, 1, 1, 1, None, 1e-6, 1e4, 64, P(st), P(out), None))
     assert L.csa_compress_insert_many(None, 1, 1, 1, 1, 1, mismatch) == csa.EINVAL
+
+
+def test_q_norm_rope_swa_validation(csa):
+    """csa_q_norm_rope_swa rejects bad dtypes, dims, rope spans and window arguments before
+    launching (fake, never dereferenced pointers); empty calls launch nothing."""
+    L = csa.lib()
+    P = ctypes.pointer
+    sw = csa._CCache(1, None, csa.BF16, 576, 256, 10, 1, 8)
+    sw_bad = csa._CCache(1, None, csa.BF16, 512, 256, 10, 1, 8)
+    # (stream, total_q, q_pos, q_in, q_out, q_dtype, heads, dim, gamma, eps, base, rope_dims,
+    #  batch, ctx_lens, cu_new, total_new, new_raw, raw_dtype, swa)
+    args = [None, 4, 1, 1, 1, csa.BF16, 128, 576, None, 1e-6, 1e4, 64, 4, 1, 1, 4, 1, csa.BF16, P(sw)]
+    # (the unmodified argument list is valid and is never passed: it would launch)
+
+    def with_(**kw):
+        names = ["stream", "total_q", "q_pos", "q_in", "q_out", "q_dtype", "heads", "dim", "gamma",
+                 "eps", "base", "rope_dims", "batch", "ctx_lens", "cu_new", "total_new", "new_raw",
+                 "raw_dtype", "swa"]
+        a = list(args)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.csa_q_norm_rope_swa(*a)
+
+    assert with_(q_dtype=csa.FP8_E4M3) == csa.ENOTSUP
+    assert with_(dim=580) == csa.ENOTSUP
+    assert with_(dim=2048) == csa.ENOTSUP
+    assert with_(rope_dims=60) == csa.EINVAL
+    assert with_(rope_dims=256) == csa.EINVAL
+    assert with_(eps=-1.0) == csa.EINVAL
+    assert with_(heads=0) == csa.EINVAL
+    assert with_(q_out=None) == csa.EINVAL
+    assert with_(swa=P(sw_bad)) == csa.EINVAL          # window cache of another dim
+    assert with_(cu_new=None) == csa.EINVAL
+    assert with_(raw_dtype=csa.FP8_E4M3) == csa.ENOTSUP
+    # nothing to do: returns without launching
+    assert with_(total_q=0, q_pos=None, q_in=None, q_out=None, swa=None) == csa.OK
+    assert with_(total_q=0, q_pos=None, q_in=None, q_out=None, total_new=0, new_raw=None) == csa.OK
