@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import geometry
+from . import formats, geometry
 from .paged import PagedCache
 from .rope import inverse_rope
 
@@ -80,3 +80,20 @@ def sparse_attn_decode(cu_q, q_pos, q: np.ndarray, kv: PagedCache, ratio: int, t
             out[i] = inverse_rope(o, t, rope_base, rope_dims)
             lse[i] = l
     return out, lse
+
+
+def output_fp8(out: np.ndarray):
+    """The output rows as fp8 for the output projection ([vLLM-V4] section 3 part 2, second
+    fusion: inverse RoPE, then fp8 quantisation).  Reading (the pages give no layout): each
+    (query, head) row is quantised like an fp8 cache row (formats.fp8_quantize_row: one float32
+    scale amax/448 per row, nearest-even saturating E4M3 codes of row / scale).
+
+    out [..., d] float64 -> (codes [..., d] uint8, scales [...] float32).
+    """
+    out = np.asarray(out, dtype=np.float64)
+    flat = out.reshape(-1, out.shape[-1])
+    codes = np.zeros(flat.shape, dtype=np.uint8)
+    scales = np.zeros(flat.shape[0], dtype=np.float32)
+    for r in range(flat.shape[0]):
+        codes[r], scales[r] = formats.fp8_quantize_row(flat[r])
+    return codes.reshape(out.shape), scales.reshape(out.shape[:-1])

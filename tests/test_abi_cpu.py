@@ -24,7 +24,7 @@ def csa():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(csa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree(csa):

@@ -134,3 +134,33 @@ def test_window_edges():
     o, _ = attention.sparse_attn_decode([0, 1], [t], q, kv, 4, np.array([[3, 9, n_vis, -1]]), swa,
                                         W, 0.04, 1e4, 64)
     assert np.array_equal(o, base)
+
+
+def test_output_fp8_rows():
+    """The fp8 output rows ([vLLM-V4] second fusion): per (query, head) row, scale = amax/448
+    in float32 and codes that decode (code value * scale) to within half an E4M3 step of the
+    row; the row's largest magnitude is exactly code 448 (0x7E or 0xFE); an all-zero row has
+    scale 1 and zero codes."""
+    from oracle.attention import output_fp8
+    from oracle import formats
+    rng = np.random.default_rng(11)
+    out = rng.standard_normal((3, 2, 576)) * rng.uniform(0.01, 50.0, size=(3, 2, 1))
+    out[2, 1] = 0.0
+    codes, scales = output_fp8(out)
+    assert codes.shape == out.shape and codes.dtype == np.uint8 and scales.shape == (3, 2)
+    for i in range(3):
+        for h in range(2):
+            row = out[i, h]
+            amax = np.max(np.abs(row))
+            if amax == 0:
+                assert scales[i, h] == 1.0 and not codes[i, h].any()
+                continue
+            assert scales[i, h] == np.float32(amax / 448.0)
+            dec = formats.fp8_e4m3_to_f64(codes[i, h]) * np.float64(scales[i, h])
+            q = row / np.float64(scales[i, h])
+            # half an E4M3 step of each value (normal binades: 2^(e-4); subnormals: 2^-10)
+            e = np.floor(np.log2(np.maximum(np.abs(q), 2.0 ** -6)))
+            half = np.ldexp(1.0, (e - 4).astype(int)) * np.float64(scales[i, h])
+            assert np.all(np.abs(dec - row) <= half * (1 + 1e-12))
+            j = int(np.argmax(np.abs(row)))
+            assert codes[i, h, j] in (0x7E, 0xFE)
