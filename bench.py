@@ -159,6 +159,37 @@ def next_rows(cfg) -> dict:
     return out
 
 
+def attn_fp8_rows(cfg, step, g) -> dict:
+    """The step's attention (partial + merge launches) with its output rows written as fp8
+    codes + one scale per row (csa_sparse_attn_decode_fp8) against the float32 rows, on the
+    benchmark workload's own inputs and top-k lists; HIP-graph timed like next_rows."""
+    import torch
+    import compressed_sparse_long_c4a_amd as csa
+    topk = step.topk if "index" in cfg.stages else g.get("topk")
+    args = (g["cu_q"], g["q_pos"], g["q"], g["kv"], cfg.ratio, topk, g["swa"], cfg.window,
+            cfg.softmax_scale, cfg.max_context)
+    total_q, heads, dim = g["q"].shape
+    codes = torch.empty((total_q, heads, dim), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((total_q, heads), dtype=torch.float32, device="cuda")
+    L = csa.lib()
+    ws = step.attn_ws
+
+    def fp8_call():
+        st = L.csa_sparse_attn_decode_fp8(
+            csa._stream(), g["cu_q"].shape[0] - 1, g["cu_q"].data_ptr(), g["q_pos"].data_ptr(),
+            total_q, cfg.max_context, g["q"].data_ptr(), csa.dtype_code(g["q"].dtype), heads,
+            csa._cref(g["kv"]), cfg.ratio, csa._ptr(topk), 0 if topk is None else topk.shape[1],
+            csa._cref(g["swa"]), cfg.window, cfg.softmax_scale, cfg.rope_base, 64,
+            codes.data_ptr(), scales.data_ptr(), None, None, ws.data_ptr(), ws.numel())
+        assert st == 0, st
+
+    us_fp8 = time_launches(fp8_call, reps=20)
+    us_f32 = time_launches(lambda: step.attn(g, with_lse=False), reps=20)
+    return {"kernels": "attn_partial_fp8 + attn_merge", "workload": cfg.name,
+            "us_per_call_fp8_rows": round(us_fp8, 2), "us_per_call_f32_rows": round(us_f32, 2),
+            "output_bytes_fp8": total_q * heads * (dim + 4), "output_bytes_f32": total_q * heads * dim * 4}
+
+
 def clone_caches(g: dict) -> dict:
     from compressed_sparse_long_c4a_amd import PagedCache
     from compressed_sparse_long_c4a_amd.pipeline import CACHE_KEYS
@@ -350,7 +381,8 @@ def main() -> int:
         }
     if not args.no_next_rows:
         print("# timing the rows beyond the step", file=sys.stderr, flush=True)
-        result["next_rows"] = {"q_norm_rope_swa": next_rows(cfg)}
+        result["next_rows"] = {"q_norm_rope_swa": next_rows(cfg),
+                               "attn_fp8_output": attn_fp8_rows(cfg, step, reps[0])}
     if not args.no_cpu_baseline:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, d)

@@ -85,6 +85,8 @@ _SIGNATURES = {
     "csa_sparse_attn_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "csa_sparse_attn_decode": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _CP, _I, _P, _I, _CP, _I,
                                     _F, _F, _I, _P, _P, _P, _SZ]),
+    "csa_sparse_attn_decode_fp8": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _CP, _I, _P, _I, _CP,
+                                        _I, _F, _F, _I, _P, _P, _P, _P, _P, _SZ]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -384,3 +386,36 @@ def sparse_attn_decode(cu_q, q_pos, q, kv: PagedCache, ratio: int, topk_idx, swa
         workspace.numel())
     _check(st, "csa_sparse_attn_decode")
     return out, lse
+
+
+def sparse_attn_decode_fp8(cu_q, q_pos, q, kv: PagedCache, ratio: int, topk_idx, swa: PagedCache,
+                           window: int, softmax_scale: float, max_context: int,
+                           rope_base: float = 10000.0, rope_dims: int = 64, with_f32: bool = False,
+                           with_lse: bool = False, workspace: torch.Tensor | None = None):
+    """The attention output as fp8 rows: (codes [total_q, H, dim] uint8, scales [total_q, H]
+    float32, the float32 rows or None, lse or None)."""
+    _dev(cu_q, "cu_q", torch.int32, 1)
+    _dev(q_pos, "q_pos", torch.int32, 1)
+    _dev(q, "q", (torch.bfloat16, torch.float32), 3)
+    total_q, heads, dim = q.shape
+    k = 0
+    if topk_idx is not None:
+        _dev(topk_idx, "topk_idx", torch.int32, 2)
+        if topk_idx.shape[0] != total_q:
+            raise ValueError("topk_idx must have one row per query")
+        k = topk_idx.shape[1]
+    codes = torch.empty((total_q, heads, dim), dtype=torch.uint8, device=q.device)
+    scales = torch.empty((total_q, heads), dtype=torch.float32, device=q.device)
+    out = torch.empty((total_q, heads, dim), dtype=torch.float32, device=q.device) if with_f32 else None
+    lse = torch.empty((total_q, heads), dtype=torch.float32, device=q.device) if with_lse else None
+    ws_bytes = sparse_attn_workspace_size(total_q, heads, dim, ratio, topk_idx is not None, k,
+                                          max_context, window)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib().csa_sparse_attn_decode_fp8(
+        _stream(), cu_q.shape[0] - 1, cu_q.data_ptr(), q_pos.data_ptr(), total_q, max_context,
+        q.data_ptr(), dtype_code(q.dtype), heads, _cref(kv), ratio, _ptr(topk_idx), k, _cref(swa),
+        window, softmax_scale, rope_base, rope_dims, codes.data_ptr(), scales.data_ptr(), _ptr(out),
+        _ptr(lse), workspace.data_ptr(), workspace.numel())
+    _check(st, "csa_sparse_attn_decode_fp8")
+    return codes, scales, out, lse

@@ -226,15 +226,18 @@ int csa_q_norm_rope_swa(csa_stream_t stream, int total_q, const int32_t* q_pos, 
   return hip_status(csa::launch_q_norm_rope_swa(L, (hipStream_t)stream));
 }
 
-int csa_sparse_attn_decode(csa_stream_t stream, int batch, const int32_t* cu_q,
-                           const int32_t* q_pos, int total_q, int max_context, const void* q,
-                           int q_dtype, int n_heads, const csa_cache* kv, int ratio,
-                           const int32_t* topk_idx, int k, const csa_cache* swa, int window,
-                           float softmax_scale, float rope_base, int rope_dims, float* out,
-                           float* lse, void* workspace, size_t workspace_bytes) {
+// Shared by the float32 and the fp8 output entry points.
+static int sparse_attn(csa_stream_t stream, int batch, const int32_t* cu_q, const int32_t* q_pos,
+                       int total_q, int max_context, const void* q, int q_dtype, int n_heads,
+                       const csa_cache* kv, int ratio, const int32_t* topk_idx, int k,
+                       const csa_cache* swa, int window, float softmax_scale, float rope_base,
+                       int rope_dims, float* out, float* lse, uint8_t* out_fp8, float* out_scales,
+                       void* workspace, size_t workspace_bytes) {
   if (ratio != 4 && ratio != 128) return CSA_EINVAL;
   if (batch <= 0 || total_q < 0 || !cu_q) return CSA_EINVAL;
-  if (total_q > 0 && (!q_pos || !q || !out)) return CSA_EINVAL;  // zero-length arrays may be NULL
+  if (total_q > 0 && (!q_pos || !q)) return CSA_EINVAL;  // zero-length arrays may be NULL
+  if (total_q > 0 && !out && !out_fp8) return CSA_EINVAL;
+  if (total_q > 0 && out_fp8 && !out_scales) return CSA_EINVAL;
   if (max_context <= 0 || window < 0 || window > 4096) return CSA_EINVAL;
   if (topk_idx && (k <= 0 || k > 65536)) return CSA_EINVAL;
   if (!cache_ok(kv, 256 / ratio, -1) || !cache_ok(swa, 256, kv->dim)) return CSA_EINVAL;
@@ -253,8 +256,33 @@ int csa_sparse_attn_decode(csa_stream_t stream, int batch, const int32_t* cu_q,
     return CSA_EWORKSPACE;
   csa::AttnLaunch L{batch, cu_q, q_pos, total_q, max_context, q, q_dtype, n_heads, kv, ratio,
                     topk_idx, has_topk ? k : 0, swa, window, softmax_scale, rope_base, rope_dims,
-                    out, lse};
+                    out, lse, out_fp8, out_scales};
   return hip_status(csa::launch_sparse_attn(L, p, workspace, (hipStream_t)stream));
+}
+
+int csa_sparse_attn_decode(csa_stream_t stream, int batch, const int32_t* cu_q,
+                           const int32_t* q_pos, int total_q, int max_context, const void* q,
+                           int q_dtype, int n_heads, const csa_cache* kv, int ratio,
+                           const int32_t* topk_idx, int k, const csa_cache* swa, int window,
+                           float softmax_scale, float rope_base, int rope_dims, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes) {
+  if (total_q > 0 && !out) return CSA_EINVAL;
+  return sparse_attn(stream, batch, cu_q, q_pos, total_q, max_context, q, q_dtype, n_heads, kv,
+                     ratio, topk_idx, k, swa, window, softmax_scale, rope_base, rope_dims, out,
+                     lse, nullptr, nullptr, workspace, workspace_bytes);
+}
+
+int csa_sparse_attn_decode_fp8(csa_stream_t stream, int batch, const int32_t* cu_q,
+                               const int32_t* q_pos, int total_q, int max_context, const void* q,
+                               int q_dtype, int n_heads, const csa_cache* kv, int ratio,
+                               const int32_t* topk_idx, int k, const csa_cache* swa, int window,
+                               float softmax_scale, float rope_base, int rope_dims,
+                               uint8_t* out_fp8, float* out_scales, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes) {
+  if (total_q > 0 && (!out_fp8 || !out_scales)) return CSA_EINVAL;
+  return sparse_attn(stream, batch, cu_q, q_pos, total_q, max_context, q, q_dtype, n_heads, kv,
+                     ratio, topk_idx, k, swa, window, softmax_scale, rope_base, rope_dims, out,
+                     lse, out_fp8, out_scales, workspace, workspace_bytes);
 }
 
 }  // extern "C"

@@ -751,11 +751,15 @@ struct MergeArgs {
   const float* part_ml;
   float* out;
   float* lse;
+  uint8_t* out_fp8;
+  float* out_scales;
   RopeTable rope;
 };
 
 // One wave per (query, head): split weights from the partial statistics, weighted sum of the
-// partial outputs, normalisation and R_t^{-1} on the last rope_dims dims.  Each lane owns the
+// partial outputs, normalisation and R_t^{-1} on the last rope_dims dims; the row leaves as
+// float32 and/or as fp8 codes with one scale (amax / 448, from a wave max: [vLLM-V4] section 3
+// part 2, second fusion, inverse RoPE + fp8 quantisation for the output projection).  Each lane owns the
 // float4 columns lane, lane + 64, lane + 128 of the row; the partial rows of a round of splits
 // are loaded before the statistics are read, so both memory trips overlap.  No LDS, no
 // workgroup barrier.
@@ -827,19 +831,37 @@ __global__ __launch_bounds__(256) void attn_merge(MergeArgs a) {
 
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   const int rope0 = a.dim - a.rope_dims;  // first rotated dim
-  float* orow = a.out + ((int64_t)qi * a.n_heads + h) * a.dim;
+  const int64_t row = (int64_t)qi * a.n_heads + h;
+  float4 r[kMergeCols];
+  float amax = 0.f;
 #pragma unroll
   for (int j = 0; j < kMergeCols; ++j) {
+    r[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (lane + 64 * j >= dim4) continue;
     const int d = 4 * (lane + 64 * j);
-    float4 r = make_float4(acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv);
+    r[j] = make_float4(acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv);
     if (d >= rope0) {  // pairs (d, d+1) and (d+2, d+3) by -t theta_i
       float c0, s0, c1, s1;
       rope_cos_sin(-(double)t, a.rope.theta[(d - rope0) / 2], c0, s0);
       rope_cos_sin(-(double)t, a.rope.theta[(d - rope0) / 2 + 1], c1, s1);
-      r = make_float4(r.x * c0 - r.y * s0, r.x * s0 + r.y * c0, r.z * c1 - r.w * s1, r.z * s1 + r.w * c1);
+      r[j] = make_float4(r[j].x * c0 - r[j].y * s0, r[j].x * s0 + r[j].y * c0,
+                         r[j].z * c1 - r[j].w * s1, r[j].z * s1 + r[j].w * c1);
     }
-    *(float4*)(orow + d) = r;
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(r[j].x), fabsf(r[j].y)), fmaxf(fabsf(r[j].z), fabsf(r[j].w))));
+    if (a.out) *(float4*)(a.out + row * a.dim + d) = r[j];
+  }
+  if (a.out_fp8) {
+    amax = wave_max(amax);
+    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int j = 0; j < kMergeCols; ++j) {
+      if (lane + 64 * j >= dim4) continue;
+      const int d = 4 * (lane + 64 * j);
+      const uint32_t codes = (uint32_t)f32_to_fp8(r[j].x / scale) | ((uint32_t)f32_to_fp8(r[j].y / scale) << 8) |
+                             ((uint32_t)f32_to_fp8(r[j].z / scale) << 16) | ((uint32_t)f32_to_fp8(r[j].w / scale) << 24);
+      *(uint32_t*)(a.out_fp8 + row * a.dim + d) = codes;
+    }
+    if (lane == 0) a.out_scales[row] = scale;
   }
 }
 
@@ -942,6 +964,8 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, const AttnPlan& p, void* work
   m.part_ml = a.part_ml;
   m.out = L.out;
   m.lse = L.lse;
+  m.out_fp8 = L.out_fp8;
+  m.out_scales = L.out_scales;
   hipLaunchKernelGGL(attn_merge, dim3((L.n_heads + 3) / 4, L.total_q), dim3(256), 0, stream, m);
   return hipGetLastError();
 }

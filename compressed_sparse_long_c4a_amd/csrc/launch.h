@@ -116,8 +116,10 @@ struct AttnLaunch {
   int window;
   float softmax_scale, rope_base;
   int rope_dims;
-  float* out;
+  float* out;           // [total_q][n_heads][dim] float32, or NULL when only fp8 is wanted
   float* lse;
+  uint8_t* out_fp8;     // NULL, or [total_q][n_heads][dim] OCP E4M3 codes of the same rows
+  float* out_scales;    // with out_fp8: [total_q][n_heads], one scale per row (amax / 448)
 };
 hipError_t launch_sparse_attn(const AttnLaunch& a, const AttnPlan& p, void* workspace,
                               hipStream_t stream);

@@ -294,6 +294,28 @@ int csa_sparse_attn_decode(csa_stream_t stream, int batch, const int32_t* cu_q,
                            float rope_base, int rope_dims, float* out, float* lse,
                            void* workspace, size_t workspace_bytes);
 
+/*
+ * csa_sparse_attn_decode_fp8 -- csa_sparse_attn_decode with the output row quantised to fp8 in
+ * the same launch as the inverse RoPE ([vLLM-V4] section 3 part 2, second fusion: inverse RoPE
+ * + fp8 quantisation, the input of the output projection's fp8 matrix products).  The pages do
+ * not give the fp8 layout; each output row (query, head) is stored like an fp8 cache row:
+ * out_scales[i][h] = amax / 448 over the row's dim values (1 for an all-zero row) and
+ * out_fp8[i][h][d] = the OCP E4M3 code of out[i][h][d] / scale, rounded to nearest even.
+ *
+ * Arguments as csa_sparse_attn_decode, plus out_fp8 [total_q][n_heads][dim] uint8 and
+ * out_scales [total_q][n_heads] float32 (both required when total_q > 0); `out` may be NULL
+ * (only the fp8 row is written) or receive the float32 row the codes were taken from.  The
+ * workspace is csa_sparse_attn_workspace_size(...) bytes as for csa_sparse_attn_decode.
+ */
+int csa_sparse_attn_decode_fp8(csa_stream_t stream, int batch, const int32_t* cu_q,
+                               const int32_t* q_pos, int total_q, int max_context,
+                               const void* q, int q_dtype, int n_heads,
+                               const csa_cache* kv, int ratio, const int32_t* topk_idx, int k,
+                               const csa_cache* swa, int window, float softmax_scale,
+                               float rope_base, int rope_dims, uint8_t* out_fp8,
+                               float* out_scales, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes);
+
 #ifdef __cplusplus
 }
 #endif
