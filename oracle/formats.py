@@ -9,6 +9,13 @@
   keys as 128 such codes plus one float32 scale; [vLLM-V4] section 3 uses a
   per-token fp8 attention cache in decode.  Stored as numpy uint8 codes.
 
+* FP4 (indexer cache rows, [SGLang-pools] section 7): two 4-bit values per byte and one scale
+  per 16 original values.  Readings (the pages fix neither the element nor the scale format):
+  the element is OCP E2M1 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes
+  0, 0.5, 1, 1.5, 2, 3, 4, 6), element 2i in the low nibble of byte i; the scale is a power of
+  two stored as an E8M0 byte (value 2**(byte - 127)), the smallest one that keeps the block's
+  largest magnitude within 6 (no clipping; 1 for an all-zero block).
+
 Rounding is round-to-nearest-even from the exact float64 value, done once.
 """
 
@@ -114,6 +121,83 @@ def f64_to_fp8_e4m3(x: np.ndarray) -> np.ndarray:
     return codes.astype(np.uint8)
 
 
+# --------------------------------------------------------------------- fp4
+
+FP4_MAX = 6.0
+FP4_BLOCK = 16
+
+
+def fp4_e2m1_to_f64(nibbles: np.ndarray) -> np.ndarray:
+    """Decode E2M1 4-bit codes (values 0..15) by the format's definition."""
+    c = np.asarray(nibbles, dtype=np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    exp = (c >> 1) & 0x3
+    man = c & 0x1
+    val = np.where(exp == 0, man * 0.5, np.ldexp(1.0 + man / 2.0, exp - 1))
+    return sign * val
+
+
+def round_to_fp4_e2m1(x: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 value (ties to the even mantissa), saturating at +-6; returns float64.
+
+    Spacing: 0.5 below 2, 1 in [2, 4), 2 in [4, 6].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), FP4_MAX)
+    quantum = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    r = np.rint(a / quantum) * quantum        # rint: half to even on the quantum grid
+    return np.copysign(np.minimum(r, FP4_MAX), x)
+
+
+def f64_to_fp4_e2m1(x: np.ndarray) -> np.ndarray:
+    """Round (ties to even, saturating) and encode to E2M1 nibbles (values 0..15)."""
+    r = round_to_fp4_e2m1(x)
+    a = np.abs(r)
+    code = np.zeros(r.shape, dtype=np.int64)
+    code[a == 0.5] = 0x1
+    nz = a >= 1.0
+    e = _binade_exponent(a[nz])                # 0, 1 or 2
+    man = np.rint((a[nz] / np.ldexp(1.0, e) - 1.0) * 2.0).astype(np.int64)
+    code[nz] = ((e + 1) << 1) | man
+    code[np.signbit(r) & (a > 0)] |= 0x8
+    return code.astype(np.uint8)
+
+
+def e8m0_to_f64(b: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes: 2**(b - 127)."""
+    return np.ldexp(1.0, np.asarray(b, dtype=np.int64) - 127)
+
+
+def fp4_quantize_row(c: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """One row (length a multiple of 16) to FP4: (packed bytes [d/2], E8M0 scale bytes [d/16]).
+
+    Per block of 16 values: scale = 2**ceil(log2(amax / 6)) (1 for an all-zero block), codes =
+    nearest-even E2M1 of value / scale; element 2i in the low nibble of byte i.
+    """
+    c = np.asarray(c, dtype=np.float64)
+    d = c.shape[-1]
+    assert d % FP4_BLOCK == 0
+    blocks = c.reshape(d // FP4_BLOCK, FP4_BLOCK)
+    amax = np.max(np.abs(blocks), axis=1)
+    k = np.zeros(len(amax), dtype=np.int64)
+    nz = amax > 0
+    # smallest k with amax / 2**k <= 6: k = ceil(log2(amax / 6)), found exactly with frexp
+    m, e = np.frexp(amax[nz] / FP4_MAX)      # amax/6 = m * 2**e, m in [0.5, 1)
+    k[nz] = np.where(m == 0.5, e - 1, e)
+    nib = f64_to_fp4_e2m1(blocks / np.ldexp(1.0, k)[:, None]).reshape(d)
+    packed = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+    return packed, (k + 127).astype(np.uint8)
+
+
+def fp4_unpack(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Exact float64 values of FP4 rows: packed [..., d/2] bytes, scales [..., d/16] E8M0."""
+    p = np.asarray(packed, dtype=np.uint8)
+    nib = np.stack([p & 0xF, p >> 4], axis=-1).reshape(p.shape[:-1] + (2 * p.shape[-1],))
+    v = fp4_e2m1_to_f64(nib)
+    sc = e8m0_to_f64(scales)
+    return v * np.repeat(sc, FP4_BLOCK, axis=-1)
+
+
 def fp8_quantize_row(c: np.ndarray) -> tuple[np.ndarray, np.float32]:
     """Per-row fp8 quantization: one float32 scale = amax / 448 and E4M3 codes of c / scale.
 
@@ -131,7 +215,7 @@ def fp8_quantize_row(c: np.ndarray) -> tuple[np.ndarray, np.float32]:
 
 # --------------------------------------------------------------- generic
 
-DTYPES = ("f32", "bf16", "fp8")
+DTYPES = ("f32", "bf16", "fp8", "fp4")
 
 
 def decode_stored(values: np.ndarray, dtype: str, scales: np.ndarray | None = None) -> np.ndarray:
@@ -143,6 +227,8 @@ def decode_stored(values: np.ndarray, dtype: str, scales: np.ndarray | None = No
     if dtype == "fp8":
         v = fp8_e4m3_to_f64(values)
         return v * np.asarray(scales, dtype=np.float32).astype(np.float64)[..., None]
+    if dtype == "fp4":
+        return fp4_unpack(values, scales)
     raise ValueError(dtype)
 
 
@@ -154,4 +240,6 @@ def encode_row(c: np.ndarray, dtype: str):
         return f64_to_bf16_bits(c), None
     if dtype == "fp8":
         return fp8_quantize_row(c)
+    if dtype == "fp4":
+        return fp4_quantize_row(c)
     raise ValueError(dtype)

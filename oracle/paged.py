@@ -24,10 +24,12 @@ from . import formats
 
 @dataclass
 class PagedCache:
-    rows: np.ndarray                 # [num_blocks, rows_per_block, dim]: float32 | uint16 (bf16) | uint8 (fp8)
-    dtype: str                       # "f32" | "bf16" | "fp8"
+    rows: np.ndarray                 # [num_blocks, rows_per_block, dim]: float32 | uint16 (bf16) |
+                                     # uint8 (fp8 codes); fp4: [..., dim / 2] uint8, two codes a byte
+    dtype: str                       # "f32" | "bf16" | "fp8" | "fp4"
     block_table: np.ndarray          # int32 [batch, bt_stride]
-    scales: np.ndarray | None = None  # float32 [num_blocks, rows_per_block], fp8 only
+    scales: np.ndarray | None = None  # fp8: float32 [num_blocks, rows_per_block];
+                                      # fp4: uint8 E8M0 [num_blocks, rows_per_block, dim / 16]
 
     @property
     def rows_per_block(self) -> int:
@@ -35,7 +37,7 @@ class PagedCache:
 
     @property
     def dim(self) -> int:
-        return self.rows.shape[2]
+        return self.rows.shape[2] * (2 if self.dtype == "fp4" else 1)
 
     def locate(self, b: int, r):
         r = np.asarray(r, dtype=np.int64)
@@ -54,7 +56,7 @@ class PagedCache:
         blk, slot = self.locate(b, r)
         stored, scale = formats.encode_row(value, self.dtype)
         self.rows[blk, slot] = stored
-        if self.dtype == "fp8":
+        if self.dtype in ("fp8", "fp4"):
             self.scales[blk, slot] = scale
 
     @staticmethod
@@ -69,9 +71,13 @@ class PagedCache:
         ids = np.arange(batch * nb, dtype=np.int32)
         if perm_seed is not None:
             ids = np.random.default_rng(perm_seed).permutation(ids).astype(np.int32)
-        store = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
-        rows = np.zeros((batch * nb, rows_per_block, dim), dtype=store)
-        scales = np.ones((batch * nb, rows_per_block), dtype=np.float32) if dtype == "fp8" else None
+        store = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "fp4": np.uint8}[dtype]
+        rows = np.zeros((batch * nb, rows_per_block, dim // 2 if dtype == "fp4" else dim), dtype=store)
+        scales = None
+        if dtype == "fp8":
+            scales = np.ones((batch * nb, rows_per_block), dtype=np.float32)
+        elif dtype == "fp4":
+            scales = np.full((batch * nb, rows_per_block, dim // 16), 127, dtype=np.uint8)
         return PagedCache(rows, dtype, ids.reshape(batch, nb), scales)
 
     def copy(self) -> "PagedCache":
