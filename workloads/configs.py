@@ -25,7 +25,7 @@ class StepConfig:
     raw_dtype: str                   # "f32" | "bf16"
     stages: tuple[str, ...]
     idx_heads: int = 64
-    idx_dtype: str = "fp8"           # indexer key cache
+    idx_dtype: str = "fp8"           # indexer key cache ("fp8", "fp4", "bf16" or "f32")
     idx_q_dtype: str = "bf16"
     k: int = 512
     window: int = 128
@@ -81,6 +81,10 @@ C4A_PREFILL_64K = StepConfig(
     stages=("compress", "compress_idx", "index", "attn"), k=512)
 
 CONFIGS = [REF, C4A_128K_B32, C128A_1M_B8, C4A_1M_B4_FP8, C4A_PREFILL_64K]
+
+# The 1M fp8 decode with the indexer cache in FP4 (two E2M1 codes a byte, one power-of-two
+# scale per 16 values): 72-byte keys instead of 132.
+C4A_1M_B4_FP4IDX = replace(C4A_1M_B4_FP8, name="c4a_decode_1m_b4_fp8_fp4idx", idx_dtype="fp4")
 HEADLINE = C4A_1M_B4_FP8
 
 

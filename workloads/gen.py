@@ -11,6 +11,8 @@ Value recipes:
 * fp8 rows: E4M3 codes of N(0, 1) * 100 draws (clamped to the format's +-448
   range before torch's cast) and per-row float32 scales U(0.5, 1.5) / 100, so
   code * scale is roughly N(0, 1) with a per-row spread;
+* fp4 rows (indexer keys): uniformly random E2M1 codes, two per byte, and one E8M0 scale byte
+  per 16 values drawn uniformly from 124..128 (2**-3 .. 2**1), drawn as codes directly;
 * block tables: a random permutation of the physical block ids in use.
 """
 
@@ -49,6 +51,16 @@ class Gen:
     def fp8_scales(self, name: str, shape) -> torch.Tensor:
         return self.uniform(name, shape, 0.5, 1.5) / _FP8_SPAN
 
+    def fp4_bytes(self, name: str, shape) -> torch.Tensor:
+        """Packed E2M1 codes: shape[-1] logical values -> shape[-1] / 2 bytes."""
+        nib = torch.randint(0, 16, (*shape[:-1], shape[-1]), generator=self.gen(name), dtype=torch.int32)
+        return (nib[..., 0::2] | (nib[..., 1::2] << 4)).to(torch.uint8)
+
+    def fp4_scales(self, name: str, shape) -> torch.Tensor:
+        """E8M0 bytes, one per 16 values: shape[-1] logical values -> shape[-1] / 16 bytes."""
+        return torch.randint(124, 129, (*shape[:-1], shape[-1] // 16), generator=self.gen(name),
+                             dtype=torch.int32).to(torch.uint8)
+
     def permutation(self, name: str, n: int) -> torch.Tensor:
         return torch.randperm(n, generator=self.gen(name)).to(torch.int32)
 
@@ -60,6 +72,8 @@ class Gen:
         """Stored rows of a cache dtype: returns (rows, scales or None)."""
         if dtype == "fp8":
             return self.fp8_codes(name, shape), self.fp8_scales(name + ".scale", shape[:-1])
+        if dtype == "fp4":
+            return self.fp4_bytes(name, shape), self.fp4_scales(name + ".scale", shape)
         return self.normal(name, shape, torch.bfloat16 if dtype == "bf16" else torch.float32), None
 
 
@@ -84,5 +98,5 @@ def paged_rows(g: Gen, name: str, batch: int, rows_per_block: int, dim: int, dty
     rows, scales = g.rows(name, (nb, rows_per_block, dim), dtype)
     rows[0].zero_()
     if scales is not None:
-        scales[0].fill_(1.0)
+        scales[0].fill_(127 if dtype == "fp4" else 1.0)
     return rows, scales, bt
