@@ -27,13 +27,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "c4a sparse decode query-tokens/s and achieved HBM GB/s at 1M context"
 HBM_PEAK_GBS = 8000.0
-INDEX_ROW_BYTES = 132          # 128 fp8 codes + one float32 scale
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "index_score_mfma_c4a_1m_b4_counters.txt")
 INDEX_SRC = os.path.join(ROOT, "compressed_sparse_long_c4a_amd", "csrc", "index.hip")
 
 
 def row_bytes(dtype: str, dim: int) -> int:
-    return {"f32": 4 * dim, "bf16": 2 * dim, "fp8": dim + 4}[dtype]
+    """Bytes of one stored row: fp8 codes + a float32 scale; fp4 two codes a byte + one E8M0
+    byte per 16 values."""
+    return {"f32": 4 * dim, "bf16": 2 * dim, "fp8": dim + 4, "fp4": dim // 2 + dim // 16}[dtype]
 
 
 def algorithmic_bytes(cfg, d) -> dict:
@@ -43,6 +44,7 @@ def algorithmic_bytes(cfg, d) -> dict:
     qpos = d["q_pos"].tolist()
     n_vis = [(t + 1) // cfg.ratio for t in qpos]
     kvrow = row_bytes(cfg.kv_dtype, D)
+    idx_row = row_bytes(cfg.idx_dtype, 128)
     rawb = 2 if cfg.raw_dtype == "bf16" else 4
     Wc = 8 if cfg.ratio == 4 else 128
     e = int(d["cu_entries"][-1])
@@ -52,10 +54,10 @@ def algorithmic_bytes(cfg, d) -> dict:
         out["compress"] = (e * (Wc * D * rawb + Wc * 4 + kvrow)          # window rows, logits, entry
                            + new * (D * rawb + kvrow + D * rawb))          # raw row, window row, state row
     if "compress_idx" in cfg.stages:
-        out["compress_idx"] = e * (Wc * 128 * rawb + Wc * 4 + INDEX_ROW_BYTES) + new * 2 * 128 * rawb
+        out["compress_idx"] = e * (Wc * 128 * rawb + Wc * 4 + idx_row) + new * 2 * 128 * rawb
     if "index" in cfg.stages:
         qb = 2 if cfg.idx_q_dtype == "bf16" else 4
-        out["index_score"] = sum(n_vis) * INDEX_ROW_BYTES + total_q * cfg.idx_heads * (128 * qb + 4)
+        out["index_score"] = sum(n_vis) * idx_row + total_q * cfg.idx_heads * (128 * qb + 4)
         out["index_select"] = total_q * cfg.k * 4
     if "attn" in cfg.stages:
         rows = sum((min(cfg.k, n) if "index" in cfg.stages else n) + min(W, t + 1) for n, t in zip(n_vis, qpos))
@@ -188,6 +190,48 @@ def attn_fp8_rows(cfg, step, g) -> dict:
     return {"kernels": "attn_partial_fp8 + attn_merge", "workload": cfg.name,
             "us_per_call_fp8_rows": round(us_fp8, 2), "us_per_call_f32_rows": round(us_f32, 2),
             "output_bytes_fp8": total_q * heads * (dim + 4), "output_bytes_f32": total_q * heads * dim * 4}
+
+
+def fp4_indexer_rows(cfg, d, reps, steps: int) -> dict:
+    """The same step with the indexer key cache in fp4 (two E2M1 codes a byte, one E8M0 scale
+    per 16 values: 72-byte keys instead of 132), every other input shared with the timed step:
+    the eager step time and the score kernel's launch time from HIP events, as for the
+    roofline of the fp8 step."""
+    import dataclasses
+    import torch
+    from compressed_sparse_long_c4a_amd import PagedCache, pipeline
+    from workloads import inputs
+    cfg4 = dataclasses.replace(cfg, name=cfg.name + "_fp4idx", idx_dtype="fp4")
+    rows, scales, bt = inputs.redraw_indexer(cfg4, d)["idx"]
+    rows, scales, bt = rows.cuda(), scales.cuda(), bt.cuda()
+    g4 = []
+    for i, g in enumerate(reps):
+        r = dict(g)
+        r["idx"] = PagedCache(rows if i == 0 else rows.clone(), bt, scales if i == 0 else scales.clone())
+        g4.append(r)
+    step = pipeline.Step(cfg4, g4[0], with_scores=False)
+    for i in range(5):
+        step.run(g4[i % len(g4)], with_lse=False)
+    for g in g4:
+        step.fast(g)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        step.fast(g4[i % len(g4)], ev[i])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    score_us = statistics.mean(x.elapsed_time(y) for x, y in ev) * 1e3
+    nbytes = algorithmic_bytes(cfg4, d)["index_score"]
+    total_q = d["q_pos"].shape[0]
+    return {"workload": cfg4.name, "kernel": "index_score_mfma (fp4 keys)",
+            "ms_per_step": round(ms, 5), "query_tokens_per_s": round(total_q / (ms / 1e3), 1),
+            "score_launch_us": round(score_us, 2), "score_algorithmic_bytes": nbytes,
+            "score_achieved_gbs": round(nbytes / score_us / 1e3, 1),
+            "score_frac": round(nbytes / score_us / 1e3 / HBM_PEAK_GBS, 4),
+            "index_row_bytes": row_bytes("fp4", 128)}
 
 
 def clone_caches(g: dict) -> dict:
@@ -383,6 +427,8 @@ def main() -> int:
         print("# timing the rows beyond the step", file=sys.stderr, flush=True)
         result["next_rows"] = {"q_norm_rope_swa": next_rows(cfg),
                                "attn_fp8_output": attn_fp8_rows(cfg, step, reps[0])}
+        if has_index and cfg.idx_dtype == "fp8" and cfg.idx_q_dtype == "bf16":
+            result["next_rows"]["fp4_indexer"] = fp4_indexer_rows(cfg, d, reps, min(K, 100))
     if not args.no_cpu_baseline:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, d)

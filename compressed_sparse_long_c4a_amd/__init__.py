@@ -23,7 +23,7 @@ import os
 
 import torch
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
 OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 ABI_VERSION = 1
 
@@ -158,16 +158,26 @@ def _stream() -> int:
 class PagedCache:
     """A paged cache in device memory (layout of ``csa_cache`` in include/csa.h).
 
-    rows:        [num_blocks, rows_per_block, dim] float32 | bfloat16 | uint8 (fp8 E4M3 codes)
+    rows:        [num_blocks, rows_per_block, dim] float32 | bfloat16 | uint8 (fp8 E4M3 codes),
+                 or [num_blocks, rows_per_block, dim / 2] uint8 (fp4: two E2M1 codes a byte,
+                 the lower element in the low nibble)
     block_table: [batch, bt_stride] int32 physical block ids
-    scales:      [num_blocks, rows_per_block] float32, fp8 caches only
+    scales:      fp8: [num_blocks, rows_per_block] float32; fp4: [num_blocks, rows_per_block,
+                 dim / 16] uint8 E8M0 bytes (2^(s - 127)); None otherwise
+
+    uint8 rows with uint8 scales form an fp4 cache, with float32 scales an fp8 cache.
     """
 
     def __init__(self, rows: torch.Tensor, block_table: torch.Tensor, scales: torch.Tensor | None = None):
         _dev(rows, "rows", ndim=3)
         _dev(block_table, "block_table", torch.int32, 2)
         self.dtype = dtype_code(rows.dtype)
-        if self.dtype == FP8_E4M3:
+        if self.dtype == FP8_E4M3 and scales is not None and scales.dtype == torch.uint8:
+            self.dtype = FP4_E2M1
+            _dev(scales, "scales", torch.uint8, 3)
+            if tuple(scales.shape) != (rows.shape[0], rows.shape[1], rows.shape[2] // 8) or rows.shape[2] % 8:
+                raise ValueError("fp4 scales must be [num_blocks, rows_per_block, dim / 16]")
+        elif self.dtype == FP8_E4M3:
             if scales is None:
                 raise ValueError("fp8 cache needs scales")
             _dev(scales, "scales", torch.float32, 2)
@@ -177,14 +187,15 @@ class PagedCache:
 
     @property
     def dim(self) -> int:
-        return self.rows.shape[2]
+        """Elements per row (fp4: two per byte)."""
+        return self.rows.shape[2] * (2 if self.dtype == FP4_E2M1 else 1)
 
     @property
     def rows_per_block(self) -> int:
         return self.rows.shape[1]
 
     def c(self) -> _CCache:
-        return _CCache(self.rows.data_ptr(), _ptr(self.scales), self.dtype, self.rows.shape[2],
+        return _CCache(self.rows.data_ptr(), _ptr(self.scales), self.dtype, self.dim,
                        self.rows.shape[1], self.rows.shape[0], self.block_table.data_ptr(),
                        self.block_table.shape[1])
 

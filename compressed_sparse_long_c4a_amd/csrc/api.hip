@@ -9,7 +9,9 @@ namespace {
 
 constexpr int kMaxContextIndex = 8 * 1024 * 1024;  // select kernel: <= 1024 chunks of 2048 entries
 
-bool dtype_ok(int dt) { return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP8_E4M3; }
+bool dtype_ok(int dt) {
+  return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP8_E4M3 || dt == CSA_FP4_E2M1;
+}
 
 // A cache descriptor with the given geometry (dim < 0: any dim).
 bool cache_ok(const csa_cache* c, int rows_per_block, int dim) {
@@ -17,7 +19,8 @@ bool cache_ok(const csa_cache* c, int rows_per_block, int dim) {
   if (!dtype_ok(c->dtype) || c->rows_per_block != rows_per_block) return false;
   if (dim >= 0 && c->dim != dim) return false;
   if (c->dim <= 0 || c->bt_stride <= 0 || c->num_blocks <= 0) return false;
-  if (c->dtype == CSA_FP8_E4M3 && !c->scales) return false;
+  if ((c->dtype == CSA_FP8_E4M3 || c->dtype == CSA_FP4_E2M1) && !c->scales) return false;
+  if (c->dtype == CSA_FP4_E2M1 && (c->dim & 15)) return false;
   return true;
 }
 
@@ -59,6 +62,7 @@ static int compress_job_check(const csa_compress_job& j, int batch, int total_ne
   if (j.state->dtype != j.raw_dtype) return CSA_EINVAL;
   if (!cache_ok(j.out, 256 / j.ratio, dim)) return CSA_EINVAL;
   if (j.swa && !cache_ok(j.swa, 256, dim)) return CSA_EINVAL;
+  if (j.swa && j.swa->dtype == CSA_FP4_E2M1) return CSA_ENOTSUP;
   if (dim < 2 || dim > 1024 || (dim & 1)) return CSA_ENOTSUP;
   if (j.rope_dims < 2 || (j.rope_dims & 1) || j.rope_dims > dim || j.rope_dims > 128) return CSA_EINVAL;
   (void)batch;
@@ -203,6 +207,7 @@ int csa_q_norm_rope_swa(csa_stream_t stream, int total_q, const int32_t* q_pos, 
     if (raw_dtype != CSA_F32 && raw_dtype != CSA_BF16) return CSA_ENOTSUP;
     if (total_new > 0 && !new_raw) return CSA_EINVAL;
     if (!cache_ok(swa, 256, dim)) return CSA_EINVAL;
+    if (swa->dtype == CSA_FP4_E2M1) return CSA_ENOTSUP;
   }
   csa::QNormLaunch L{};
   L.total_q = total_q;
@@ -241,7 +246,7 @@ static int sparse_attn(csa_stream_t stream, int batch, const int32_t* cu_q, cons
   if (max_context <= 0 || window < 0 || window > 4096) return CSA_EINVAL;
   if (topk_idx && (k <= 0 || k > 65536)) return CSA_EINVAL;
   if (!cache_ok(kv, 256 / ratio, -1) || !cache_ok(swa, 256, kv->dim)) return CSA_EINVAL;
-  if (kv->dtype != swa->dtype) return CSA_ENOTSUP;
+  if (kv->dtype != swa->dtype || kv->dtype == CSA_FP4_E2M1) return CSA_ENOTSUP;
   if (kv->dim != 576 && kv->dim != 512) return CSA_ENOTSUP;
   if (q_dtype != CSA_BF16 && q_dtype != CSA_F32) return CSA_ENOTSUP;
   if (n_heads < 1 || n_heads > 128) return CSA_ENOTSUP;

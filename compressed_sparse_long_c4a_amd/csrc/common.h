@@ -19,7 +19,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // a power of two (2, 64 or 256) and is kept as its log2 so paged addressing needs no division.
 struct DevCache {
   void* rows;
-  float* scales;
+  float* scales;  // float32 per row (fp8) or uint8 E8M0 per 16 values (fp4)
   const int32_t* bt;
   int32_t dtype, dim, rpb_shift, bt_stride;
 };
@@ -34,7 +34,7 @@ inline DevCache to_dev(const csa_cache* c) {
   DevCache d{};
   if (!c) return d;
   d.rows = c->rows;
-  d.scales = c->scales;
+  d.scales = (float*)c->scales;  // fp4 caches: uint8 E8M0 bytes, read through a cast
   d.bt = c->block_table;
   d.dtype = c->dtype;
   d.dim = c->dim;
@@ -115,6 +115,53 @@ __device__ __forceinline__ float fp8_to_f32(uint8_t c) {
 // float32 -> OCP E4M3 code, round to nearest even.  Callers keep |x| <= 448.
 __device__ __forceinline__ uint8_t f32_to_fp8(float x) {
   return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xFF);
+}
+
+// ---- FP4: OCP E2M1 codes (sign, 2 exponent bits, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2,
+// 3, 4, 6), two per byte with the lower element in the low nibble, and E8M0 block scales.
+
+// E8M0 scale byte s (1..254) as the float32 2^(s - 127): s is the float's exponent field.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) { return __uint_as_float(s << 23); }
+
+// Eight E2M1 codes (one word, element 2i in the low nibble of byte i) times `scale` (a power of
+// two) as eight bfloat16 values; exact.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Eight E2M1 codes (one word, as above) times `scale` as float32; exact.
+__device__ __forceinline__ void fp4x8_to_f32(uint32_t w, float scale, float* x) {
+  const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0);
+  const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 1);
+  const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 2);
+  const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 3);
+  x[0] = v0[0]; x[1] = v0[1]; x[2] = v1[0]; x[3] = v1[1];
+  x[4] = v2[0]; x[5] = v2[1]; x[6] = v3[0]; x[7] = v3[1];
+}
+
+// float32 -> E2M1 code: nearest value, ties to the even code, saturating at 6; -0 and values
+// that round to 0 give code 0.  The seven midpoints between neighbouring magnitudes decide:
+// a tie at 0.25, 1.25, 2.5 or 5 goes down (to an even code), at 0.75, 1.75 or 3.5 up.
+__device__ __forceinline__ uint32_t f32_to_fp4(float x) {
+  const float a = fabsf(x);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return m | ((x < 0.f && m) ? 8u : 0u);
+}
+
+// Exponent k of the smallest power-of-two scale with amax / 2^k <= 6, for amax > 0: with
+// amax = f * 2^e (f in [0.5, 1)), 6 * 2^k = 0.75 * 2^(k + 3), so k = e - 3, plus one when
+// f > 0.75.  Clamped to the E8M0 bytes 1..254 (k in [-126, 127]).
+__device__ __forceinline__ int fp4_scale_exp(float amax) {
+  int e;
+  const float f = frexpf(amax, &e);
+  return min(max(e - 3 + (f > 0.75f ? 1 : 0), -126), 127);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {

@@ -62,7 +62,8 @@ __device__ void rope_lds(float* v_sh, int dim, int rope_dims, double position, c
 }
 
 // Store the row staged in v_sh at physical row `prow` of cache c, rounded to its dtype.
-// FP8 rows get scale = amax / 448 (1 for an all-zero row) and nearest-even codes of v / scale.
+// FP8 rows get scale = amax / 448 (1 for an all-zero row) and nearest-even codes of v / scale;
+// FP4 rows one power-of-two scale per 16 values ([SGLang-pools] section 7).
 __device__ void store_row(const DevCache& c, int64_t prow, const float* v_sh, int dim,
                           float* red_sh) {
   const int tid = threadIdx.x;
@@ -74,6 +75,24 @@ __device__ void store_row(const DevCache& c, int64_t prow, const float* v_sh, in
     uint8_t* dst = (uint8_t*)c.rows + prow * dim;
     for (int d = tid; d < dim; d += 256) dst[d] = f32_to_fp8(v_sh[d] / scale);
     if (tid == 0) c.scales[prow] = scale;
+  } else if (c.dtype == CSA_FP4_E2M1) {
+    // one thread per block of 16 values: scale 2^k, the smallest with amax / 2^k <= 6 (k = 0
+    // for an all-zero block), and nearest-even E2M1 codes of v / 2^k, packed low nibble first
+    if (tid < (dim >> 4)) {
+      const float* v = v_sh + 16 * tid;
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      const int k = amax > 0.f ? fp4_scale_exp(amax) : 0;
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w0 |= f32_to_fp4(ldexpf(v[i], -k)) << (4 * i);
+        w1 |= f32_to_fp4(ldexpf(v[8 + i], -k)) << (4 * i);
+      }
+      *(uint2*)((uint8_t*)c.rows + prow * (dim >> 1) + 8 * tid) = make_uint2(w0, w1);
+      ((uint8_t*)c.scales)[prow * (dim >> 4) + tid] = (uint8_t)(k + 127);
+    }
   } else if (c.dtype == CSA_BF16) {
     uint16_t* dst = (uint16_t*)c.rows + prow * dim;
     for (int d = tid; d < dim; d += 256) dst[d] = f32_to_bf16_bits(v_sh[d]);

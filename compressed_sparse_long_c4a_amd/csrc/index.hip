@@ -3,7 +3,8 @@
 // [vLLM-V4] section 2 (DeepSeek Sparse Attention): a query attends only to the top-k
 // compressed entries; a 1M-token context still holds ~250K c4a entries.  [vLLM-V4]
 // appendix: a query at t may use entry j only if 4j + 3 <= t.  [SGLang-pools] section 4:
-// an indexer key is 128 fp8 values plus one float32 scale.
+// an indexer key is 128 fp8 values plus one float32 scale; [SGLang-pools] section 7 and
+// [vLLM-V4] section 2: as fp4, 64 bytes of two-a-byte codes plus one scale per 16 values.
 // Score (reading of the DSA indexer): s_j = sum_h w_h * relu(q_h . k_j).
 //
 // Three kernels:
@@ -133,16 +134,18 @@ __device__ void finish_chunk(const ScoreArgs& a, int qi, int chunk, int n, int n
   }
 }
 
-// ---- MFMA score kernel: bf16 queries, fp8 or bf16 keys, HT tiles of 16 heads (<= 64 heads).
+// ---- MFMA score kernel: bf16 queries, fp8, fp4 or bf16 keys, HT tiles of 16 heads (<= 64 heads).
 // Wave w of the workgroup takes the 16-entry tiles w, w+4, ... of the chunk, so in group gi
 // the four waves cover the four 64-entry blocks 4 gi .. 4 gi + 3 together.  The physical ids
 // of the chunk's blocks are fetched once; key loads run one group ahead of the MFMA work
 // (two register buffers), so a wave always has a group of keys in flight.
 template <int KEY_DT>
 struct KeyGroup {
-  static constexpr int NW = KEY_DT == CSA_FP8_E4M3 ? 2 : 4;  // 16-byte words per lane per tile
+  static constexpr int NW = KEY_DT == CSA_FP8_E4M3 ? 2 : KEY_DT == CSA_FP4_E2M1 ? 1 : 4;  // 16-byte words per lane per tile
+  static constexpr int ROW = 16 * 4 * NW;  // bytes per key row (fp4: 64, the scales apart)
   uint4 raw[4][NW];
-  float scale;  // lane (e, g): scale of entry e of the group's tile g
+  float scale;       // fp8, lane (e, g): scale of entry e of the group's tile g
+  uint32_t sc4[4];   // fp4, per tile: the two E8M0 bytes of this lane's 32 dimensions
 };
 
 template <int KEY_DT, int HT>
@@ -199,9 +202,12 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
       prow_g = lg == u ? prow : prow_g;
       // load i reads one 64-byte half line of each of the tile's 16 rows: lane group lg takes
       // bytes 64 i + 16 lg .. +15 (the K order of the A operand matches)
-      const uint4* src = (const uint4*)((const uint8_t*)a.cache.rows + prow * (KEY_DT == CSA_FP8_E4M3 ? 128 : 256) + 16 * lg);
+      // (fp4: one load, dims 32 lg .. 32 lg + 31, and the scale bytes 2 lg, 2 lg + 1 of the
+      // row's eight, one per 16 dims)
+      const uint4* src = (const uint4*)((const uint8_t*)a.cache.rows + prow * KeyGroup<KEY_DT>::ROW + 16 * lg);
 #pragma unroll
       for (int i = 0; i < NW; ++i) kg.raw[u][i] = src[4 * i];
+      if constexpr (KEY_DT == CSA_FP4_E2M1) kg.sc4[u] = ((const uint16_t*)a.cache.scales)[prow * 4 + lg];
     }
     if constexpr (KEY_DT == CSA_FP8_E4M3) kg.scale = a.cache.scales[prow_g];
     else kg.scale = 1.f;
@@ -218,6 +224,13 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
                                 kg.raw[u][1].x, kg.raw[u][1].y, kg.raw[u][1].z, kg.raw[u][1].w};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kb[ks] = fp8x8_to_bf16x8(wd[2 * ks], wd[2 * ks + 1]);
+      } else if constexpr (KEY_DT == CSA_FP4_E2M1) {
+        // word ks holds dims 32 lg + 8 ks .. +7, in scale block 2 lg + ks / 2; the block scale
+        // is applied in the conversion (a power of two: exact in bf16)
+        const uint32_t wd[4] = {kg.raw[u][0].x, kg.raw[u][0].y, kg.raw[u][0].z, kg.raw[u][0].w};
+        const float s0 = e8m0_to_f32(kg.sc4[u] & 0xFFu), s1 = e8m0_to_f32(kg.sc4[u] >> 8);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[ks] = fp4x8_to_bf16x8(wd[ks], ks < 2 ? s0 : s1);
       } else {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kb[ks] = __builtin_bit_cast(bf16x8, kg.raw[u][ks]);
@@ -238,7 +251,7 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
       sacc = rows_reduce(sacc, [](float x, float y) { return x + y; });
       mine = lg == u ? sacc : mine;
     }
-    mine *= kg.scale;
+    if constexpr (KEY_DT == CSA_FP8_E4M3) mine *= kg.scale;
     // tile < C / 16 always, so every lane's slot is inside this chunk
     const int eloc = (16 * gi + 4 * lg + wv) * 16 + ln;
     sc_sh[eloc] = mine;
@@ -257,12 +270,15 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
   __syncthreads();
   // A operand: lane (head ln of tile mt, group lg) holds the dims its key lanes hold for
   // k-step ks (fp8: 64 (ks / 2) + 16 lg + 8 (ks % 2) + 0..7, the eight codes of half a
-  // 16-byte load; bf16: 32 ks + 8 lg + 0..7, one 16-byte load).
+  // 16-byte load; fp4: 32 lg + 8 ks + 0..7, one word of the lane's load; bf16: 32 ks + 8 lg +
+  // 0..7, one 16-byte load).
 #pragma unroll
   for (int mt = 0; mt < HT; ++mt) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int d0 = KEY_DT == CSA_FP8_E4M3 ? 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1) : 32 * ks + 8 * lg;
+      const int d0 = KEY_DT == CSA_FP8_E4M3   ? 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1)
+                     : KEY_DT == CSA_FP4_E2M1 ? 32 * lg + 8 * ks
+                                              : 32 * ks + 8 * lg;
       qa[mt][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)&q_sh[(16 * mt + ln) * QROW + d0]);
     }
     const float4 w4 = *(const float4*)&w_sh[16 * mt + 4 * lg];
@@ -349,14 +365,21 @@ __global__ __launch_bounds__(256) void index_score_f32(ScoreArgs a) {
     for (int eloc = threadIdx.x; eloc < nloc; eloc += 256) {
       const int64_t prow = phys_row(a.cache, b, j0 + eloc);
       float key[128];
+      if (a.cache.dtype == CSA_FP4_E2M1) {
+        const uint32_t* r = (const uint32_t*)((const uint8_t*)a.cache.rows + prow * 64);
+        const uint8_t* sb = (const uint8_t*)a.cache.scales + prow * 8;
 #pragma unroll
-      for (int d = 0; d < 128; ++d) {
-        if (a.cache.dtype == CSA_FP8_E4M3)
-          key[d] = fp8_to_f32(((const uint8_t*)a.cache.rows)[prow * 128 + d]) * a.cache.scales[prow];
-        else if (a.cache.dtype == CSA_BF16)
-          key[d] = bf16_bits_to_f32(((const uint16_t*)a.cache.rows)[prow * 128 + d]);
-        else
-          key[d] = ((const float*)a.cache.rows)[prow * 128 + d];
+        for (int wi = 0; wi < 16; ++wi) fp4x8_to_f32(r[wi], e8m0_to_f32(sb[wi >> 1]), key + 8 * wi);
+      } else {
+#pragma unroll
+        for (int d = 0; d < 128; ++d) {
+          if (a.cache.dtype == CSA_FP8_E4M3)
+            key[d] = fp8_to_f32(((const uint8_t*)a.cache.rows)[prow * 128 + d]) * a.cache.scales[prow];
+          else if (a.cache.dtype == CSA_BF16)
+            key[d] = bf16_bits_to_f32(((const uint16_t*)a.cache.rows)[prow * 128 + d]);
+          else
+            key[d] = ((const float*)a.cache.rows)[prow * 128 + d];
+        }
       }
       float s = h0 == 0 ? 0.f : sc_sh[eloc];
       for (int h = 0; h < hn; ++h) {
@@ -773,6 +796,7 @@ hipError_t launch_index_score(const IndexLaunch& a, const IndexWorkspace& ws, hi
   } else {
     const int ht = (a.n_heads + 15) / 16;
     if (a.idx_cache->dtype == CSA_FP8_E4M3) launch_mfma<CSA_FP8_E4M3>(s, ht, grid, stream);
+    else if (a.idx_cache->dtype == CSA_FP4_E2M1) launch_mfma<CSA_FP4_E2M1>(s, ht, grid, stream);
     else launch_mfma<CSA_BF16>(s, ht, grid, stream);
   }
   return hipGetLastError();

@@ -51,7 +51,8 @@ typedef struct ihipStream_t* csa_stream_t;
 typedef enum {
   CSA_F32 = 0,       /* IEEE float32 */
   CSA_BF16 = 1,      /* bfloat16 */
-  CSA_FP8_E4M3 = 2   /* OCP E4M3 ("e4m3fn") codes with one float32 scale per row */
+  CSA_FP8_E4M3 = 2,  /* OCP E4M3 ("e4m3fn") codes with one float32 scale per row */
+  CSA_FP4_E2M1 = 3   /* OCP E2M1 codes, two per byte, with one E8M0 scale byte per 16 values */
 } csa_dtype;
 
 /* Status codes. */
@@ -78,10 +79,22 @@ enum {
  * their float32 scales in a separate [num_blocks][rows_per_block] array
  * (value = code * scale; 128 codes + 4 scale bytes = the 132-byte indexer row
  * of [SGLang-pools] section 4).  Scales must be positive.
+ *
+ * FP4 rows ([SGLang-pools] section 7, FP4 quantisation: two 4-bit values a
+ * byte and one scale per 16 values; [vLLM-V4] section 2 puts the indexer
+ * cache in fp4) hold dim / 2 bytes, element 2i in the low nibble of byte i and
+ * element 2i + 1 in the high nibble; `scales` then points at uint8 E8M0 bytes
+ * [num_blocks][rows_per_block][dim / 16], byte s meaning 2^(s - 127), and
+ * value = E2M1(code) * 2^(s - 127).  Scale bytes must lie in 1..254.  `dim`
+ * counts elements (128 for an indexer row of 64 + 8 bytes) and is a multiple
+ * of 16.  FP4 is accepted for compressed-entry caches written by the
+ * compressor and for the indexer cache, not for attention or window caches.
  */
 typedef struct csa_cache {
-  void*          rows;            /* [num_blocks][rows_per_block][dim] elements of `dtype` (fp8: uint8 codes) */
-  float*         scales;          /* [num_blocks][rows_per_block] float32 for CSA_FP8_E4M3, else NULL */
+  void*          rows;            /* [num_blocks][rows_per_block][dim] elements of `dtype` (fp8: uint8 codes;
+                                     fp4: [..][dim / 2] bytes) */
+  void*          scales;          /* float32 [num_blocks][rows_per_block] for CSA_FP8_E4M3, uint8
+                                     [num_blocks][rows_per_block][dim / 16] for CSA_FP4_E2M1, else NULL */
   int32_t        dtype;           /* csa_dtype */
   int32_t        dim;             /* elements per row */
   int32_t        rows_per_block;  /* 64 (c4a), 2 (c128a) or 256 (window, state) */
@@ -120,7 +133,9 @@ int64_t csa_num_entries(int ratio, int64_t num_tokens);
  *   y   = sum_r w_r x_r;  n = y / sqrt(mean(y^2) + eps) * gamma  (whole row);
  *   c   = RoPE_{a_j}(n): the last rope_dims dimensions rotated in consecutive
  *         pairs (2i, 2i+1) by a_j * rope_base^(-2i/rope_dims) (angles in float64);
- *   out row j = c rounded to out->dtype (fp8: scale = amax/448, codes RNE).
+ *   out row j = c rounded to out->dtype (fp8: scale = amax/448, codes RNE; fp4: per
+ *         block of 16 values the smallest power-of-two scale 2^k with amax / 2^k <= 6,
+ *         k clamped to [-126, 127], codes RNE with ties to the even code).
  * Raw rows at positions below ctx_lens[b] are read from `state` (which must hold
  * the last W positions); the new rows among the last W positions after the call
  * are written to `state` (the rolling residual registered as sliding-window KV,
@@ -134,8 +149,9 @@ int64_t csa_num_entries(int ratio, int64_t num_tokens);
  *   total_entries = cu_entries[batch] (host).  gate_logits [total_entries][W] float32.
  *   gamma [dim] float32 or NULL (= 1).  eps >= 0.  rope_base > 0.  rope_dims even,
  *   2..min(dim, 128).  state: rows_per_block 256, dtype = raw_dtype, same dim.
- *   out: rows_per_block 256 / ratio, dim = state dim, any dtype.  swa: NULL or
- *   rows_per_block 256, same dim, any dtype.  dim <= 1024.
+ *   out: rows_per_block 256 / ratio, dim = state dim, any dtype (FP4_E2M1: dim a
+ *   multiple of 16).  swa: NULL or rows_per_block 256, same dim, F32, BF16 or
+ *   FP8_E4M3.  dim <= 1024.
  * Cache rows must not alias new_raw; out, state and swa must be distinct memory.
  */
 int csa_compress_insert(csa_stream_t stream, int ratio, int batch,
@@ -192,8 +208,8 @@ int csa_compress_insert_many(csa_stream_t stream, int batch, const int32_t* ctx_
  *   q_idx [total_q][n_heads_idx][128] of q_dtype: CSA_BF16 (1 <= n_heads_idx <= 64)
  *         or CSA_F32 (any n_heads_idx >= 1).
  *   head_w [total_q][n_heads_idx] float32.
- *   idx_cache: dim 128, rows_per_block 64, dtype FP8_E4M3 or BF16 (any dtype
- *         with CSA_F32 queries).
+ *   idx_cache: dim 128, rows_per_block 64, dtype FP8_E4M3, FP4_E2M1 or BF16 (any
+ *         dtype with CSA_F32 queries).
  *   1 <= k <= 65536.  topk_idx [total_q][k] int32.  topk_score [total_q][k] or NULL.
  *   workspace of at least csa_index_workspace_size(total_q, max_context, k) bytes.
  */
@@ -244,7 +260,7 @@ int csa_index_select(csa_stream_t stream, int batch, const int32_t* cu_q, const 
  *   Window keys (read only when swa != NULL): batch >= 1, ctx_lens [batch] int32 >= 0,
  *   cu_new [batch+1] int32 prefix sums with cu_new[batch] = total_new (host), new_raw
  *   [total_new][dim] of raw_dtype (F32 or BF16); swa: rows_per_block 256, the same dim,
- *   any dtype, not overlapping new_raw or q_out.
+ *   F32, BF16 or FP8_E4M3, not overlapping new_raw or q_out.
  * total_q = 0 and total_new = 0 are valid; with neither, nothing is launched.
  * Returns CSA_EINVAL for inconsistent arguments, CSA_ENOTSUP for an unsupported dtype or
  * dim; a zero-length array may be NULL.

@@ -21,9 +21,16 @@ def np_rows(t: torch.Tensor) -> np.ndarray:
     return t.numpy().copy()
 
 
+def cache_fmt(rows: torch.Tensor, scales) -> str:
+    """Stored format of a cache's rows: uint8 rows with uint8 (E8M0) scales are fp4."""
+    if rows.dtype == torch.uint8 and scales is not None and scales.dtype == torch.uint8:
+        return "fp4"
+    return DT[rows.dtype]
+
+
 def oracle_cache(triple) -> PagedCache:
     rows, scales, bt = triple
-    return PagedCache(np_rows(rows), DT[rows.dtype], bt.numpy().copy(),
+    return PagedCache(np_rows(rows), cache_fmt(rows, scales), bt.numpy().copy(),
                       None if scales is None else scales.numpy().copy())
 
 
@@ -139,6 +146,36 @@ def check_rounded_row(gpu_vals: np.ndarray, exact: np.ndarray, fmt: str, gpu_sca
     return bool(ok_s and np.all(err <= tol)), float(np.max(err / tol))
 
 
+def check_fp4_row(packed: np.ndarray, sbytes: np.ndarray, exact: np.ndarray):
+    """A stored fp4 row (packed bytes [d/2], E8M0 bytes [d/16]) against the exact row [d].
+
+    Per block of 16 values, with the float32 accuracy of the kernel
+    delta = 1e-5 |exact| + 1e-6 max|row| (as in check_rounded_row):
+    * the scale 2^k is the smallest power of two with amax / 2^k <= 6, up to delta on amax
+      (an all-zero block has k = 0);
+    * every code is a rounding, at scale 2^k, of a value within delta of the exact one: within
+      half the E2M1 spacing at that magnitude (0.25 below 2, 0.5 below 4, 1 up to 6).
+    Returns (ok, worst err/tol)."""
+    exact = np.asarray(exact, dtype=np.float64)
+    d = exact.size
+    blocks = exact.reshape(d // 16, 16)
+    k = np.asarray(sbytes, dtype=np.int64) - 127
+    amax = np.max(np.abs(blocks), axis=1)
+    row_max = float(np.max(amax)) if amax.size else 0.0
+    tiny = 1e-5 * amax + 1e-6 * row_max
+    top = 6.0 * np.ldexp(1.0, k)
+    ok_s = np.where(amax > 0, (amax - tiny <= top) & (amax + tiny > top / 2), k == 0)
+    sc = np.ldexp(1.0, k)[:, None]
+    vals = formats.fp4_unpack(packed, sbytes).reshape(d // 16, 16) / sc
+    c = blocks / sc
+    a = np.abs(c)
+    half = np.where(a < 2.0, 0.25, np.where(a < 4.0, 0.5, 1.0))
+    delta = (1e-5 * np.abs(blocks) + 1e-6 * row_max) / sc
+    ratio = np.abs(vals - c) / (half + delta)
+    worst = float(np.max(ratio)) if ratio.size else 0.0
+    return bool(np.all(ok_s) and np.all(ratio <= 1.0)), (worst if np.all(ok_s) else 1e9)
+
+
 def topk_acceptable(gpu_ids: np.ndarray, scores: np.ndarray, k: int, rel: float = 1e-5):
     """R11: |G| = k', every id scoring above tau(1+rel) is in G, every id in G scores >= tau(1-rel).
     Also checks the output form: ascending ids, no duplicates, -1 padding."""
@@ -179,11 +216,11 @@ def allclose_out(gpu: np.ndarray, ref: np.ndarray, atol: float = 1e-5, rtol: flo
 def decode_gpu_rows(rows: torch.Tensor, scales, blocks_slots):
     """Stored values of the given (block, slot) rows of a GPU cache copied to CPU."""
     r = rows.cpu()
-    dt = DT[r.dtype]
+    dt = cache_fmt(r, scales)
     blk, slot = blocks_slots
     vals = np_rows(r[blk, slot])
     sc = None if scales is None else scales.cpu().numpy()[blk, slot]
-    return formats.decode_stored(vals, dt, sc if dt == "fp8" else None), sc
+    return formats.decode_stored(vals, dt, sc if dt in ("fp8", "fp4") else None), sc
 
 
-__all__ = ["run_oracle", "check_rounded_row", "topk_acceptable", "allclose_out", "geometry"]
+__all__ = ["run_oracle", "check_rounded_row", "check_fp4_row", "cache_fmt", "topk_acceptable", "allclose_out", "geometry"]

@@ -78,8 +78,14 @@ def compare(cfg, d: dict, step, ores: dict) -> dict:
     if "compress_idx" in cfg.stages:
         ic = cpu_cache("idx")
         for (b, j), c in ores["idx_entries"].items():
-            gv, gs = _rows_at(ic, d["idx"][2], b, j)
-            ok, r = O.check_rounded_row(gv, c, cfg.idx_dtype, gs, _oracle_scale(ores["idx"], b, j))
+            if cfg.idx_dtype == "fp4":
+                rows, scales = ic
+                rpb = rows.shape[1]
+                blk, slot = int(d["idx"][2][b, j // rpb]), j % rpb
+                ok, r = O.check_fp4_row(rows[blk, slot].numpy(), scales[blk, slot].numpy(), c)
+            else:
+                gv, gs = _rows_at(ic, d["idx"][2], b, j)
+                ok, r = O.check_rounded_row(gv, c, cfg.idx_dtype, gs, _oracle_scale(ores["idx"], b, j))
             note("idx_entry", ok, r, (b, j))
 
     same_set = {}

@@ -149,3 +149,39 @@ def test_q_norm_rope_swa_validation(csa):
     # nothing to do: returns without launching
     assert with_(total_q=0, q_pos=None, q_in=None, q_out=None, swa=None) == csa.OK
     assert with_(total_q=0, q_pos=None, q_in=None, q_out=None, total_new=0, new_raw=None) == csa.OK
+
+
+def test_fp4_cache_validation(csa):
+    """FP4 caches (CSA_FP4_E2M1): scales required, dim a multiple of 16; accepted as the
+    indexer cache and the compressor's entry cache, refused for attention and window caches
+    (fake, never dereferenced pointers)."""
+    L = csa.lib()
+    P = ctypes.pointer
+    st = csa._CCache(1, None, csa.BF16, 576, 256, 10, 1, 8)
+    st128 = csa._CCache(1, None, csa.BF16, 128, 256, 10, 1, 8)
+    out4 = csa._CCache(1, 1, csa.FP4_E2M1, 128, 64, 10, 1, 8)
+    out4_noscale = csa._CCache(1, None, csa.FP4_E2M1, 128, 64, 10, 1, 8)
+    out4_dim = csa._CCache(1, 1, csa.FP4_E2M1, 584, 64, 10, 1, 8)
+    st584 = csa._CCache(1, None, csa.BF16, 584, 256, 10, 1, 8)
+    sw4 = csa._CCache(1, 1, csa.FP4_E2M1, 128, 256, 10, 1, 8)
+    # compressor: fp4 entry cache needs scales and dim % 16 == 0; fp4 window output refused
+    assert L.csa_compress_insert(None, 4, 1, 1, 1, 1, 1, csa.BF16, 1, 1, 1, None, 1e-6, 1e4, 64,
+                                 P(st128), P(out4_noscale), None) == csa.EINVAL
+    assert L.csa_compress_insert(None, 4, 1, 1, 1, 1, 1, csa.BF16, 1, 1, 1, None, 1e-6, 1e4, 64,
+                                 P(st584), P(out4_dim), None) == csa.EINVAL
+    assert L.csa_compress_insert(None, 4, 1, 1, 1, 1, 1, csa.BF16, 1, 1, 1, None, 1e-6, 1e4, 64,
+                                 P(st128), P(out4), P(sw4)) == csa.ENOTSUP
+    # indexer: an fp4 cache passes the cache checks (the small workspace is what fails)
+    assert L.csa_index_topk(None, 1, 1, 1, 1, 1024, 1, csa.BF16, 64, 1, P(out4), 8, 1, None, 1, 16) \
+        == csa.EWORKSPACE
+    assert L.csa_index_topk(None, 1, 1, 1, 1, 1024, 1, csa.BF16, 64, 1, P(out4_noscale), 8, 1, None,
+                            1, 1 << 40) == csa.EINVAL
+    # attention: fp4 main / window caches are not supported
+    kv4 = csa._CCache(1, 1, csa.FP4_E2M1, 576, 64, 10, 1, 8)
+    sw4a = csa._CCache(1, 1, csa.FP4_E2M1, 576, 256, 10, 1, 8)
+    assert L.csa_sparse_attn_decode(None, 1, 1, 1, 1, 1024, 1, csa.BF16, 64, P(kv4), 4, 1, 16, P(sw4a),
+                                    128, 0.04, 1e4, 64, 1, None, 1, 1 << 40) == csa.ENOTSUP
+    # query norm: an fp4 window cache is refused
+    assert L.csa_q_norm_rope_swa(None, 4, 1, 1, 1, csa.BF16, 128, 576, None, 1e-6, 1e4, 64, 4, 1, 1,
+                                 4, 1, csa.BF16, P(sw4a)) == csa.ENOTSUP
+    del st

@@ -18,6 +18,8 @@ FULL = {
     "c4a_decode_128k_b32_bf16": (C.C4A_128K_B32, None),
     "c128a_decode_1m_b8_bf16": (C.C128A_1M_B8, None),
     "c4a_decode_1m_b4_fp8": (C.C4A_1M_B4_FP8, None),
+    # the same decode with the indexer cache in fp4 (72-byte keys)
+    "c4a_decode_1m_b4_fp8_fp4idx": (C.C4A_1M_B4_FP4IDX, None),
     # first and last queries of the chunk, each residue mod 4 at both ends, block edges
     "c4a_prefill_4k_on_64k_bf16": (C.C4A_PREFILL_64K, [0, 1, 2, 3, 252, 255, 256, 1023, 2048, 3071,
                                                        4092, 4093, 4094, 4095]),

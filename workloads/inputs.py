@@ -65,6 +65,16 @@ def draw(cfg: StepConfig) -> dict:
     return d
 
 
+def redraw_indexer(cfg: StepConfig, d: dict) -> dict:
+    """The inputs d of the same step with the indexer key cache drawn in cfg.idx_dtype (same
+    block table); every other array is shared with d."""
+    g = Gen(cfg.seed)
+    n1 = [l // cfg.ratio for l in d["L1"]]
+    r = dict(d)
+    r["idx"] = paged_rows(g, "idx", cfg.batch, 64, 128, cfg.idx_dtype, max(n1), [(0, n) for n in n1])
+    return r
+
+
 def random_topk(cfg: StepConfig, d: dict, fill: float = 1.0, seed_name: str = "topk") -> torch.Tensor:
     """A synthetic top-k list per query: distinct ids below each query's causal limit, in random
     order, with the tail padded by -1 (``fill`` = fraction of the k slots used)."""
