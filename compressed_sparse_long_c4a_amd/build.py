@@ -20,8 +20,9 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-# Per-source extra hipcc flags (none at present).
-FILE_FLAGS: dict[str, list[str]] = {}
+# Per-source extra hipcc flags.  index.hip: MFMA accumulators in ordinary VGPRs, so the score
+# epilogue (relu, head weights) reads them without one v_accvgpr_read per value.
+FILE_FLAGS: dict[str, list[str]] = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:

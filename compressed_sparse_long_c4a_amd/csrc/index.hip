@@ -96,6 +96,10 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
 // Bits needed to hold v (0 for v = 0).
 __device__ __forceinline__ int bit_len(uint32_t v) { return v ? 32 - __clz((int)v) : 0; }
 
+// max(x, 0) as one integer max on the bits: a negative float is a negative int32 (-0 gives
+// +0); fmaxf would add a canonicalising max per value.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Lower bound of the kc-th largest of the C scores in sc_sh: one 256-bin histogram over the
 // chunk's own key range [kmin, kmax]; the bound is the lower edge of the bin that holds the
 // kc-th largest key.
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
 #pragma unroll
       for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sacc = fmaf(wt[mt][jj], fmaxf(acc[mt][jj], 0.f), sacc);
+        for (int jj = 0; jj < 4; ++jj) sacc = fmaf(wt[mt][jj], relu_bits(acc[mt][jj]), sacc);
       sacc = rows_reduce(sacc, [](float x, float y) { return x + y; });
       mine = lg == u ? sacc : mine;
     }
