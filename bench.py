@@ -7,7 +7,10 @@ scale, fp8 indexer keys (64 heads x 128), 128 query heads of 576, top-k 2048, wi
 A step is the whole hot path: compress the new token (main KV + window row, and indexer
 key), index scores + exact top-k, sparse K=V attention + inverse RoPE.  Inputs are resident
 in HBM before timing; steps rotate over several copies of the caches so that repeated steps
-cannot be served from the 256 MB Infinity Cache.
+cannot be served from the 256 MB Infinity Cache.  The headline time is the K steps replayed
+from a HIP graph (one step per cache replica in the graph), as the pages deploy with full
+graphs; the same K steps issued eagerly are timed too (ms_per_step_eager), and that eager
+loop is where the dominant kernel's launches are timed with HIP events.
 
 Prints one JSON line.  --gpus N > 1 is not supported (one GPU only).
 """
@@ -234,6 +237,26 @@ def fp4_indexer_rows(cfg, d, reps, steps: int) -> dict:
             "index_row_bytes": row_bytes("fp4", 128)}
 
 
+def stream_read_gbs(nbytes: int = 2 << 30, reps: int = 10) -> float:
+    """Achievable read bandwidth on this device: the library's streaming-read probe over
+    `nbytes` (well beyond the 256 MB infinity cache), HIP events around `reps` launches;
+    GB/s of bytes read."""
+    import torch
+    import compressed_sparse_long_c4a_amd as csa
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = csa.read_probe(x)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        csa.read_probe(x, sink)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    del x
+    return nbytes / us / 1e3
+
+
 def clone_caches(g: dict) -> dict:
     from compressed_sparse_long_c4a_amd import PagedCache
     from compressed_sparse_long_c4a_amd.pipeline import CACHE_KEYS
@@ -270,6 +293,8 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the separate timings of the rows beyond the step")
+    ap.add_argument("--no-stream-probe", action="store_true",
+                    help="skip the 2 GiB read that measures the achievable read bandwidth")
     ap.add_argument("--two-stream", action="store_true",
                     help="also time the schedule with the main-KV compress on a second stream")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -386,7 +411,11 @@ def main() -> int:
     ab = algorithmic_bytes(cfg, d)
     step_bytes = sum(ab.values())
     total_q = d["q_pos"].shape[0]
-    value = total_q / (ms_step / 1e3)
+    # the headline: the K steps replayed from the HIP graph (the pages deploy with full CUDA
+    # graphs); the eager issue of the same K steps is reported beside it
+    graph_head = graph_ms is not None and K % len(reps) == 0
+    ms_head = graph_ms if graph_head else ms_step
+    value = total_q / (ms_head / 1e3)
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -394,14 +423,16 @@ def main() -> int:
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(ms_head, 5),
+        "timing": "hip_graph_replay" if graph_head else "eager",
+        "ms_per_step_eager": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "hbm_gbs": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
-        "hbm_frac": round(step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_gbs": round(step_bytes / (ms_head / 1e3) / 1e9, 1),
+        "hbm_frac": round(step_bytes / (ms_head / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": step_bytes,
         "stages_us": stages,
         "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 5),
@@ -423,6 +454,11 @@ def main() -> int:
             "traffic": counters_traffic(), "launch_us": round(score_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": ab["index_score"],
         }
+        if not args.no_stream_probe:
+            sr = stream_read_gbs()
+            result["roofline"]["stream_read_gbs"] = round(sr, 1)
+            result["roofline"]["frac_of_stream_read"] = round(achieved / sr, 4)
+            result["hbm_frac_of_stream_read"] = round(step_bytes / (ms_head / 1e3) / 1e9 / sr, 4)
     if not args.no_next_rows:
         print("# timing the rows beyond the step", file=sys.stderr, flush=True)
         result["next_rows"] = {"q_norm_rope_swa": next_rows(cfg),

@@ -87,6 +87,8 @@ _SIGNATURES = {
                                     _F, _F, _I, _P, _P, _P, _SZ]),
     "csa_sparse_attn_decode_fp8": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _CP, _I, _P, _I, _CP,
                                         _I, _F, _F, _I, _P, _P, _P, _P, _P, _SZ]),
+    "csa_read_probe": (_I, [_P, _P, _SZ, _P]),
+    "csa_read_probe_sink_words": (_I, []),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -430,3 +432,14 @@ def sparse_attn_decode_fp8(cu_q, q_pos, q, kv: PagedCache, ratio: int, topk_idx,
         _ptr(lse), workspace.data_ptr(), workspace.numel())
     _check(st, "csa_sparse_attn_decode_fp8")
     return codes, scales, out, lse
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """One launch of the streaming-read probe over every byte of `buf` (a measurement utility:
+    time it to get the achievable read bandwidth).  Returns the sink words."""
+    _dev(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(lib().csa_read_probe_sink_words(), dtype=torch.int32, device=buf.device)
+    _check(lib().csa_read_probe(_stream(), buf.data_ptr(), nbytes, sink.data_ptr()), "csa_read_probe")
+    return sink

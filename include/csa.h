@@ -332,6 +332,18 @@ int csa_sparse_attn_decode_fp8(csa_stream_t stream, int batch, const int32_t* cu
                                float* out_scales, float* out, float* lse,
                                void* workspace, size_t workspace_bytes);
 
+/*
+ * csa_read_probe -- a measurement utility, not a step of the method: reads `bytes` bytes of the
+ * device buffer `buf` once each with 16-byte loads and writes one word per workgroup to `sink`
+ * (the XOR of the words it read, so no load can be dropped).  Timed on a buffer larger than
+ * the 256 MB infinity cache it gives the device's achievable streaming read bandwidth, the
+ * ceiling beside the 8 TB/s peak against which the indexer score kernel is reported.
+ *   buf: 16-byte aligned, bytes a positive multiple of 16; sink: csa_read_probe_sink_words()
+ *   uint32 words.  Returns CSA_EINVAL otherwise.
+ */
+int csa_read_probe(csa_stream_t stream, const void* buf, size_t bytes, uint32_t* sink);
+int csa_read_probe_sink_words(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -185,3 +185,15 @@ def test_fp4_cache_validation(csa):
     assert L.csa_q_norm_rope_swa(None, 4, 1, 1, 1, csa.BF16, 128, 576, None, 1e-6, 1e4, 64, 4, 1, 1,
                                  4, 1, csa.BF16, P(sw4a)) == csa.ENOTSUP
     del st
+
+
+def test_read_probe_validation(csa):
+    """The read probe refuses a NULL buffer or sink, an empty or ragged size and a misaligned
+    buffer before launching (fake, never dereferenced pointers)."""
+    L = csa.lib()
+    assert L.csa_read_probe_sink_words() > 0
+    assert L.csa_read_probe(None, None, 1024, 16) == csa.EINVAL
+    assert L.csa_read_probe(None, 16, 1024, None) == csa.EINVAL
+    assert L.csa_read_probe(None, 16, 0, 16) == csa.EINVAL
+    assert L.csa_read_probe(None, 16, 1000, 16) == csa.EINVAL
+    assert L.csa_read_probe(None, 8, 1024, 16) == csa.EINVAL
