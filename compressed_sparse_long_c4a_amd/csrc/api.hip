@@ -186,9 +186,14 @@ size_t csa_sparse_attn_workspace_size(int total_q, int n_heads, int dim, int rat
   if (total_q <= 0 || n_heads <= 0 || dim <= 0 || (ratio != 4 && ratio != 128) || max_context <= 0 ||
       window < 0)
     return 0;
-  const csa::AttnPlan p = csa::attn_plan(total_q, n_heads, ratio, has_topk, k, max_context, window);
+  // the larger of the two kernels' plans (the dtypes are not arguments here)
+  const csa::AttnPlan p = csa::attn_plan(total_q, n_heads, ratio, has_topk, k, max_context, window,
+                                         csa::kAttnRowsCapFp8);
+  const csa::AttnPlan p2 = csa::attn_plan(total_q, n_heads, ratio, has_topk, k, max_context, window,
+                                          csa::kAttnRowsCapGeneric);
   if (p.max_rows > csa::kAttnMaxRows) return 0;
-  return csa::attn_workspace_bytes(total_q, n_heads, dim, p);
+  return std::max(csa::attn_workspace_bytes(total_q, n_heads, dim, p),
+                  csa::attn_workspace_bytes(total_q, n_heads, dim, p2));
 }
 
 int csa_q_norm_rope_swa(csa_stream_t stream, int total_q, const int32_t* q_pos, const void* q_in,
@@ -255,7 +260,8 @@ static int sparse_attn(csa_stream_t stream, int batch, const int32_t* cu_q, cons
   if (total_q == 0) return CSA_OK;
   const int has_topk = topk_idx != nullptr;
   const csa::AttnPlan p =
-      csa::attn_plan(total_q, n_heads, ratio, has_topk, has_topk ? k : 0, max_context, window);
+      csa::attn_plan(total_q, n_heads, ratio, has_topk, has_topk ? k : 0, max_context, window,
+                     csa::attn_rows_cap(kv->dtype, q_dtype));
   if (p.max_rows > csa::kAttnMaxRows) return CSA_ENOTSUP;
   if (!workspace || workspace_bytes < csa::attn_workspace_bytes(total_q, n_heads, kv->dim, p))
     return CSA_EWORKSPACE;

@@ -47,7 +47,8 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSplits = 256;
-constexpr int kRowsPerSplit = 1024;  // most rows a workgroup handles (addresses staged in LDS)
+constexpr int kRowsPerSplit = kAttnRowsCapGeneric;  // most rows a workgroup handles (addresses staged in LDS)
+constexpr int kRowsPerSplitF8 = kAttnRowsCapFp8;     // the same for attn_partial_fp8
 constexpr int kRG = 2;               // row groups per workgroup (of four quarter waves each)
 constexpr int kWaves = 4 * kRG;
 constexpr int kThreads = 64 * kWaves;
@@ -63,7 +64,30 @@ struct Args {
   float sm_scale2;  // softmax_scale * log2(e)
   float* part_o;    // [total_q][splits][hgp][DIM]
   float* part_ml;   // [total_q][splits][hgp][2]  (m in log2 units, l)
+  int xcd_map;      // 1-D grid with the head groups of a (split, query) on one XCD
+  int units;        // splits * total_q
 };
+
+// Workgroup coordinates (split, head group, query).  With the XCD map the grid is 1-D:
+// consecutive workgroup ids go to the eight XCDs in turn, so the head groups of one (split,
+// query) get ids eight apart -- they run on the same XCD at about the same time and read the
+// split's rows once from HBM and then from that XCD's L2.  Ids past the last unit exit.
+__device__ __forceinline__ bool wg_coords(const Args& a, int& s, int& hg, int& qi) {
+  if (!a.xcd_map) {
+    s = blockIdx.x;
+    hg = blockIdx.y;
+    qi = blockIdx.z;
+    return true;
+  }
+  const int id = blockIdx.x, x = id & 7, slot = id >> 3;
+  const int G = a.hgp / 16;
+  const int u = 8 * (slot / G) + x;
+  if (u >= a.units) return false;
+  hg = slot - G * (slot / G);
+  s = u % a.splits;
+  qi = u / a.splits;
+  return true;
+}
 
 __device__ __forceinline__ bf16x8 f32x8_to_bf16(const float* x) {
   bf16x8 r;
@@ -141,7 +165,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial(Args a) {
   __shared__ f32x4 sx_sh[2][kRG][4][64];  // partial S^T of each quarter: [step parity][row group]
   __shared__ float ml_sh[kRG][16][2];
 
-  const int s = blockIdx.x, hg = blockIdx.y, qi = blockIdx.z;
+  int s, hg, qi;
+  if (!wg_coords(a, s, hg, qi)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: scalar branches below)
   const int ln = lane & 15, lg = lane >> 4;
@@ -477,8 +502,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_fp8(Args a) {
   constexpr int NKS = DIM / 32;        // k-steps of a full row
   constexpr int MQ = (NKS + 3) / 4;    // k-steps of the largest quarter
   constexpr int VROW = DIM + 16;       // LDS bytes per staged row
-  __shared__ int64_t off_sh[kRowsPerSplit];
-  __shared__ float scale_sh[kRowsPerSplit];  // row scale; 0 marks padding
+  __shared__ int64_t off_sh[kRowsPerSplitF8];
+  __shared__ float scale_sh[kRowsPerSplitF8];  // row scale; 0 marks padding
   constexpr int V_BYTES = kRG * kChunk * VROW;
   constexpr int MERGE_BYTES = 16 * (DIM + 4) * 4;
   __shared__ __attribute__((aligned(16))) char v_sh[V_BYTES > MERGE_BYTES ? V_BYTES : MERGE_BYTES];
@@ -501,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_fp8(Args a) {
   // ---- loads that need nothing else: query position, sequence, list entries, Q^T
   const int t = a.q_pos[qi];
   const int b = seq_of_wave(a.cu_q, a.batch, qi);
-  constexpr int RPT = kRowsPerSplit / kThreads;
+  constexpr int RPT = kRowsPerSplitF8 / kThreads;
   int ent[RPT];
 #pragma unroll
   for (int u = 0; u < RPT; ++u) {
@@ -888,14 +913,16 @@ void launch_q<CSA_FP8_E4M3>(const Args& args, int qdt, int dim, dim3 grid, hipSt
     if (dim == 576) hipLaunchKernelGGL((attn_partial_fp8<576>), grid, dim3(kThreads), 0, stream, args);
     else hipLaunchKernelGGL((attn_partial_fp8<512>), grid, dim3(kThreads), 0, stream, args);
   } else {
-    launch_dim<CSA_FP8_E4M3, CSA_F32>(args, dim, grid, stream);
+    // (fp8 rows with f32 queries: the generic kernel on the XCD-grouped grid)
+    const dim3 g1((unsigned)(8 * (int64_t)(args.hgp / 16) * ((args.units + 7) / 8)));
+    launch_dim<CSA_FP8_E4M3, CSA_F32>(args, dim, g1, stream);
   }
 }
 
 }  // namespace
 
 AttnPlan attn_plan(int total_q, int n_heads, int ratio, int has_topk, int k, int max_context,
-                   int window) {
+                   int window, int rows_cap) {
   AttnPlan p{};
   const int64_t n_max = max_context / ratio;
   p.max_rows = (has_topk ? (int64_t)k : n_max) + std::min<int64_t>(window, max_context);
@@ -905,8 +932,8 @@ AttnPlan attn_plan(int total_q, int n_heads, int ratio, int has_topk, int k, int
   // aim at one workgroup per compute unit (256 CUs); a split is a whole number of 128-row
   // steps (the fp8 kernel's step: two row groups of 64 rows)
   int64_t bpw = std::max<int64_t>(4, (blocks32 * units + 255) / 256);
-  bpw = std::min<int64_t>((std::min(bpw, blocks32) + 3) / 4 * 4, kRowsPerSplit / 32);
-  // callers keep max_rows <= kMaxSplits * kRowsPerSplit, so splits <= kMaxSplits
+  bpw = std::min<int64_t>((std::min(bpw, blocks32) + 3) / 4 * 4, rows_cap / 32);
+  // callers keep max_rows <= kMaxSplits * kAttnRowsCapFp8 (kAttnMaxRows), so splits <= kMaxSplits
   const int64_t splits = (blocks32 + bpw - 1) / bpw;
   p.splits = (int)splits;
   p.rows_per_split = (int)(bpw * 32);
@@ -945,10 +972,15 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, const AttnPlan& p, void* work
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + ((slots * dim * sizeof(float) + 255) & ~(size_t)255));
   const dim3 grid(p.splits, p.head_groups, L.total_q);
+  a.units = p.splits * L.total_q;
+  // the generic kernel (bf16 / f32 rows, or f32 queries) takes the XCD-grouped 1-D grid; the
+  // fp8-row kernel with bf16 queries keeps the 3-D grid
+  a.xcd_map = !(L.kv->dtype == CSA_FP8_E4M3 && L.q_dtype == CSA_BF16);
+  const dim3 grid_xcd((unsigned)(8 * (int64_t)p.head_groups * ((a.units + 7) / 8)));
   switch (L.kv->dtype) {
     case CSA_FP8_E4M3: launch_q<CSA_FP8_E4M3>(a, L.q_dtype, dim, grid, stream); break;
-    case CSA_BF16: launch_q<CSA_BF16>(a, L.q_dtype, dim, grid, stream); break;
-    default: launch_q<CSA_F32>(a, L.q_dtype, dim, grid, stream); break;
+    case CSA_BF16: launch_q<CSA_BF16>(a, L.q_dtype, dim, grid_xcd, stream); break;
+    default: launch_q<CSA_F32>(a, L.q_dtype, dim, grid_xcd, stream); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -90,6 +90,13 @@ hipError_t launch_index_select(const IndexLaunch& a, int32_t* topk_idx, float* t
 // ---------------------------------------------------------------- attention
 // Rows (top-k list length or visible entries, plus window) one query may attend to.
 constexpr int64_t kAttnMaxRows = 256 * 1024;
+// Most rows one attention workgroup takes (their addresses are staged in LDS): the fp8-row
+// kernel with bf16 queries holds 1,024, the generic kernel 2,048.
+constexpr int kAttnRowsCapFp8 = 1024;
+constexpr int kAttnRowsCapGeneric = 2048;
+inline int attn_rows_cap(int kv_dtype, int q_dtype) {
+  return kv_dtype == CSA_FP8_E4M3 && q_dtype == CSA_BF16 ? kAttnRowsCapFp8 : kAttnRowsCapGeneric;
+}
 
 struct AttnPlan {
   int splits;          // row splits per (query, head group)
@@ -98,7 +105,7 @@ struct AttnPlan {
   int64_t max_rows;
 };
 AttnPlan attn_plan(int total_q, int n_heads, int ratio, int has_topk, int k, int max_context,
-                   int window);
+                   int window, int rows_cap);
 size_t attn_workspace_bytes(int total_q, int n_heads, int dim, const AttnPlan& p);
 
 struct AttnLaunch {

@@ -77,3 +77,42 @@ def test_compressor_writes_fp4_entries(gpu, ratio):
         assert ok, f"entry {(b, j)}: err/tol {r:.3g}"
     assert len(ent) == int(d["cu_entries"][-1]) > 0
     print(f"  {len(ent)} fp4 entries of 576 values; worst err/tol {worst:.3f}", flush=True)
+
+
+# the first positions of a sequence with the indexer cache in fp4: no entry yet, entry 0 with
+# its zero-padded slots (a block scale from a partly zero row), k >= n and k < n
+EARLY_FP4 = D(C.C4A_1M_B4_FP4IDX, name="c4a_early_positions_fp4idx", ctx_after=(1, 2, 3, 4, 5, 8, 9, 130),
+              n_heads=16, k=8)
+
+
+@pytest.mark.gpu
+def test_early_positions_fp4_indexer(gpu):
+    print(f"case {EARLY_FP4.name}", flush=True)
+    rep = P.run_step_parity(EARLY_FP4, verbose=True)
+    assert not rep["fail"], rep["fail"][:10]
+
+
+def _zero_fp4_keys(d):
+    rows, scales, _ = d["idx"]
+    rows.zero_()
+    scales.fill_(127)
+
+
+@pytest.mark.gpu
+def test_all_scores_tied_fp4(gpu):
+    """Every fp4 key decodes to zero: the selection is the k' lowest entry ids, scores 0."""
+    cfg = D(C.C4A_1M_B4_FP4IDX, name="c4a_all_ties_fp4idx", ctx_after=(20000, 9000, 5), n_heads=16,
+            k=700, stages=("index", "attn"))
+    print(f"case {cfg.name}", flush=True)
+    from compressed_sparse_long_c4a_amd import pipeline
+    d = inputs.draw(cfg)
+    _zero_fp4_keys(d)
+    g = pipeline.to_device(d)
+    step = pipeline.Step(cfg, g)
+    step.run()
+    torch.cuda.synchronize()
+    topk, sc = step.topk.cpu().numpy(), step.topk_score.cpu().numpy()
+    for i, t in enumerate(d["q_pos"].tolist()):
+        kk = min(cfg.k, (t + 1) // 4)
+        assert np.array_equal(topk[i, :kk], np.arange(kk)), i
+        assert np.all(topk[i, kk:] == -1) and np.all(sc[i] == 0.0)
