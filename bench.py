@@ -272,14 +272,20 @@ def cpu_baseline(cfg, d) -> dict:
     from threadpoolctl import threadpool_info
     from tests import oracle_step as O
     caches = O.prepare(d)
-    t0 = time.perf_counter()
-    O.run_oracle(cfg, d, caches=caches)
-    dt = time.perf_counter() - t0
+    # the whole step, repeated until at least 10 s of host time have been spent (at most 8
+    # times; a repeat rewrites the same cache rows)
+    reps, dt = 0, 0.0
+    while reps < 8 and (reps == 0 or dt < 10.0):
+        t0 = time.perf_counter()
+        O.run_oracle(cfg, d, caches=caches)
+        dt += time.perf_counter() - t0
+        reps += 1
     total_q = d["q_pos"].shape[0]
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": total_q / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": reps * total_q / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole step of the same workload ({total_q} queries: compress, index "
-                      f"scores and top-k, attention, inverse RoPE) on the float64 oracle, {dt:.1f} s"}
+                      f"scores and top-k, attention, inverse RoPE) on the float64 oracle, run "
+                      f"{reps} times in {dt:.1f} s"}
 
 
 def main() -> int:
