@@ -102,6 +102,70 @@ __device__ void store_row(const DevCache& c, int64_t prow, const float* v_sh, in
   }
 }
 
+// Eight consecutive raw elements (16 bytes of bf16, 32 of float32) as float32.
+template <int RAW>
+struct Chunk8 {
+  uint4 w[RAW == CSA_BF16 ? 1 : 2];
+  __device__ __forceinline__ void load(const char* p) {
+#pragma unroll
+    for (int i = 0; i < (RAW == CSA_BF16 ? 1 : 2); ++i) w[i] = ((const uint4*)p)[i];
+  }
+  __device__ __forceinline__ float at(int j) const {
+    if constexpr (RAW == CSA_BF16) {
+      const uint32_t v = (&w[0].x)[j >> 1];
+      return __uint_as_float((j & 1) ? (v & 0xFFFF0000u) : (v << 16));
+    } else {
+      return __uint_as_float((&w[j >> 2].x)[j & 3]);
+    }
+  }
+};
+
+// y = sum_r w_r x_r over a 128-row window (c128a) with 16-byte loads: thread (chunk c, phase
+// g) of the P = 256 / (dim / 8) phases sums dims 8 c .. 8 c + 7 of rows g, g + P, ... (in that
+// order, sixteen loads in flight), and the P partial sums meet in LDS, added in phase order.
+// The result lands in y as the caller holds it (dims tid + 256 k).
+template <int RAW, int P>
+__device__ void window_sum_wide(const char* raw, const int64_t* off_sh, const float* w_sh, int dim,
+                                float* part_sh, float (&y)[kPerThread]) {
+  constexpr int ESZ = RAW == CSA_BF16 ? 2 : 4;
+  constexpr int NR = (128 + P - 1) / P;  // rows per phase (the last may lie past the window)
+  constexpr int kRing = 16;
+  const int tid = threadIdx.x;
+  const int nch = dim >> 3, c = tid % nch, g = tid / nch;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (g < P) {
+    Chunk8<RAW> x[kRing];
+    auto issue = [&](int i, Chunk8<RAW>& dst) {
+      const int r = min(g + P * i, 127);
+      const int64_t o = off_sh[r] == kNoRow ? 0 : off_sh[r];
+      dst.load(raw + o + (int64_t)(8 * c) * ESZ);
+    };
+#pragma unroll
+    for (int i = 0; i < kRing && i < NR; ++i) issue(i, x[i]);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int r = g + P * i;
+      const float wr = r < 128 && off_sh[min(r, 127)] != kNoRow ? w_sh[min(r, 127)] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wr, x[i % kRing].at(j), acc[j]);
+      if (i + kRing < NR) issue(i + kRing, x[i % kRing]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part_sh[g * dim + 8 * c + j] = acc[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int d = tid + 256 * k;
+    float t = 0.f;
+    if (d < dim) {
+#pragma unroll
+      for (int q = 0; q < P; ++q) t += part_sh[q * dim + d];
+    }
+    y[k] = t;
+  }
+}
+
 // Sequence tables staged in LDS: the prefix sums `cu` (entries or new tokens), the context
 // lengths and the new-token offsets; for batch <= 256 one trip loads them all, larger batches
 // look entries up in global memory.
@@ -124,7 +188,7 @@ __device__ __forceinline__ int seq_lookup(const SeqTables& t, const int32_t* cu,
 
 template <int RAW>
 __device__ void compress_task(const Args& a, const Job& J, int local, SeqTables& tab, float* v_sh,
-                              float* w_sh, int64_t* off_sh, float* red_sh) {
+                              float* w_sh, int64_t* off_sh, float* red_sh, float* part_sh) {
   typedef typename std::conditional<RAW == CSA_BF16, uint16_t, float>::type Elem;
   constexpr int ESZ = sizeof(Elem);
   const int tid = threadIdx.x;
@@ -180,11 +244,13 @@ __device__ void compress_task(const Args& a, const Job& J, int local, SeqTables&
     if (tid < W) w_sh[tid] = ex / den;
     __syncthreads();
 
-    // trip 3: y = sum_r w_r x_r, eight rows' loads in flight together (a missing row loads the
-    // first new row, which exists whenever an entry is emitted, and is then discarded)
+    // trip 3: y = sum_r w_r x_r in row order, eight rows per group (a missing row loads the
+    // first new row, which exists whenever an entry is emitted, and is then discarded).  A
+    // c4a window is one group; a c128a window of 576 or 512 dims takes the 16-byte-load path
+    // above, other widths run 16 groups as straight-line code with four in flight
     float y[kPerThread] = {0.f, 0.f, 0.f, 0.f};
-    for (int r0 = 0; r0 < W; r0 += 8) {
-      Elem x[8][kPerThread];
+    typedef Elem Group[8][kPerThread];
+    auto load8 = [&](int r0, Group& x) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int64_t o = off_sh[r0 + u] == kNoRow ? 0 : off_sh[r0 + u];
@@ -192,12 +258,33 @@ __device__ void compress_task(const Args& a, const Job& J, int local, SeqTables&
         for (int k = 0; k < kPerThread; ++k)
           x[u][k] = *(const Elem*)(raw + o + (int64_t)min(tid + 256 * k, dim - 1) * ESZ);
       }
+    };
+    auto add8 = [&](int r0, const Group& x) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const bool has = off_sh[r0 + u] != kNoRow;
         const float wr = w_sh[r0 + u];
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) y[k] = fmaf(wr, has ? to_f32(x[u][k]) : 0.f, y[k]);
+      }
+    };
+    if (W == 8) {
+      Group x;
+      load8(0, x);
+      add8(0, x);
+    } else if (dim == 576) {
+      window_sum_wide<RAW, 3>(raw, off_sh, w_sh, dim, part_sh, y);
+    } else if (dim == 512) {
+      window_sum_wide<RAW, 4>(raw, off_sh, w_sh, dim, part_sh, y);
+    } else {  // W = 128, other widths
+      constexpr int kRing = 4;
+      Group x[kRing];
+#pragma unroll
+      for (int g = 0; g < kRing; ++g) load8(8 * g, x[g]);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        add8(8 * g, x[g % kRing]);
+        if (g + kRing < 16) load8(8 * (g + kRing), x[g % kRing]);
       }
     }
 
@@ -265,15 +352,16 @@ __global__ __launch_bounds__(256) void compress_kernel(Args a) {
   __shared__ int64_t off_sh[128];
   __shared__ float red_sh[8];
   __shared__ SeqTables tab;
+  __shared__ float part_sh[2048];  // the wide window sum's per-phase partial rows
   int jb = 0;  // the job of this workgroup (uniform)
   for (int i = 1; i < a.num_jobs; ++i)
     if ((int)blockIdx.x >= a.job[i].wg_begin) jb = i;
   const Job& J = a.job[jb];
   const int local = blockIdx.x - J.wg_begin;
   if (J.raw_dtype == CSA_BF16)
-    compress_task<CSA_BF16>(a, J, local, tab, v_sh, w_sh, off_sh, red_sh);
+    compress_task<CSA_BF16>(a, J, local, tab, v_sh, w_sh, off_sh, red_sh, part_sh);
   else
-    compress_task<CSA_F32>(a, J, local, tab, v_sh, w_sh, off_sh, red_sh);
+    compress_task<CSA_F32>(a, J, local, tab, v_sh, w_sh, off_sh, red_sh, part_sh);
 }
 
 }  // namespace
