@@ -10,9 +10,10 @@
 // Three kernels:
 //  1. score  -- grid (chunk of 2048 entries, query).  The contraction q . k_j is dense
 //     (64 heads x 128 dims per key), so it runs on MFMA: A = the query's heads (registers),
-//     B = 16 keys per tile streamed from HBM (fp8 codes widened exactly to bf16).  The head
-//     sum, relu and the per-row scale are applied to the MFMA output in registers.  Each
-//     workgroup also writes a lower bound on the kc-th largest score of its chunk.
+//     B = 16 keys per tile streamed from HBM (fp8 or fp4 codes widened exactly to bf16, an fp4
+//     block scale applied in the widening).  The head sum, relu and the fp8 row scale are
+//     applied to the MFMA output in registers.  Each workgroup also writes a lower bound on
+//     the kc-th largest score of its chunk.
 //  2. filter -- grid (chunk, query).  tau_lo = min over the full chunks of their bounds is a
 //     lower bound on the k-th largest score (each full chunk holds kc keys above its bound,
 //     and chunks * kc >= k), so every selected entry has score >= tau_lo.  Survivors are
@@ -125,7 +126,8 @@ __device__ uint32_t chunk_bound(const float* sc_sh, int kc, uint32_t* hist, int*
   return bound;
 }
 
-// Shared tail of both score kernels: write the chunk's bound when the chunk is full.
+// Tail of the float32 score kernel: write the chunk's bound when the chunk is full (the MFMA
+// kernel reduces the same bound from its registers).
 __device__ void finish_chunk(const ScoreArgs& a, int qi, int chunk, int n, int nloc,
                              const float* sc_sh, uint32_t* hist, int* misc, uint32_t* red) {
   const int kprime = min(a.k, n);
