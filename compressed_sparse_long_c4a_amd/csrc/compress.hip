@@ -31,6 +31,7 @@ constexpr int64_t kNoRow = INT64_MIN;  // window slot at a negative position
 
 struct Job {
   int ratio, W, coff, dim, rope_dims, total_entries, has_swa, raw_dtype;
+  int wide;  // 16-byte row loads allowed (raw rows and state rows 16-byte aligned)
   int wg_begin;  // first workgroup of this job
   const void* new_raw;
   const int32_t* cu_entries;
@@ -110,12 +111,16 @@ struct Chunk8 {
 #pragma unroll
     for (int i = 0; i < (RAW == CSA_BF16 ? 1 : 2); ++i) w[i] = ((const uint4*)p)[i];
   }
+  // (j is a constant in the unrolled callers, so the component selection folds away)
+  static __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+  }
   __device__ __forceinline__ float at(int j) const {
     if constexpr (RAW == CSA_BF16) {
-      const uint32_t v = (&w[0].x)[j >> 1];
+      const uint32_t v = word(w[0], j >> 1);
       return __uint_as_float((j & 1) ? (v & 0xFFFF0000u) : (v << 16));
     } else {
-      return __uint_as_float((&w[j >> 2].x)[j & 3]);
+      return __uint_as_float(word(w[j >> 2], j & 3));
     }
   }
 };
@@ -272,9 +277,9 @@ __device__ void compress_task(const Args& a, const Job& J, int local, SeqTables&
       Group x;
       load8(0, x);
       add8(0, x);
-    } else if (dim == 576) {
+    } else if (J.wide && dim == 576) {
       window_sum_wide<RAW, 3>(raw, off_sh, w_sh, dim, part_sh, y);
-    } else if (dim == 512) {
+    } else if (J.wide && dim == 512) {
       window_sum_wide<RAW, 4>(raw, off_sh, w_sh, dim, part_sh, y);
     } else {  // W = 128, other widths
       constexpr int kRing = 4;
@@ -385,6 +390,7 @@ hipError_t launch_compress(const CompressLaunch& c, hipStream_t stream) {
     J.total_entries = s.total_entries;
     J.has_swa = s.swa != nullptr;
     J.raw_dtype = s.raw_dtype;
+    J.wide = ((((uintptr_t)s.new_raw) | ((uintptr_t)s.state->rows)) & 15) == 0;
     J.wg_begin = blocks;
     J.new_raw = s.new_raw;
     J.cu_entries = s.cu_entries;

@@ -133,3 +133,44 @@ def test_empty_calls_launch_nothing(gpu):
                              torch.zeros((0, 64), dtype=torch.float32, device=dev), ic, 8, 256)
     assert topk.shape == (0, 8)
     torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("misalign", [False, True], ids=["aligned", "new-rows-2-bytes-off"])
+def test_c128a_compress_row_alignment(gpu, misalign):
+    """c128a entries from 128-row windows: with 16-byte aligned raw rows the compressor reads
+    them with 16-byte loads, with raw rows 2 bytes off 16-byte alignment it falls back to
+    element loads; both match the oracle's entries (rounded-row rule of tests/oracle_step)."""
+    import compressed_sparse_long_c4a_amd as csa
+    from compressed_sparse_long_c4a_amd import pipeline
+    from oracle import compress
+    from tests import oracle_step as O
+    cfg = D(C.C128A_1M_B8, name="c128a_compress_align", ctx_after=(1100, 700, 129, 5000),
+            new_tokens=(600, 1, 129, 300), q_per_seq=0, n_heads=16, stages=("compress",), gamma=True)
+    print(f"case {cfg.name} misaligned={misalign}", flush=True)
+    d = inputs.draw(cfg)
+    g = pipeline.to_device(d)
+    raw = g["new_raw"]
+    if misalign:
+        buf = torch.empty(raw.numel() + 1, dtype=raw.dtype, device=raw.device)
+        shifted = buf[1:].view(raw.shape)
+        shifted.copy_(raw)
+        raw = shifted
+        assert raw.data_ptr() % 16 == 2 and raw.is_contiguous()
+    csa.compress_insert(128, g["ctx_lens"], g["cu_new"], raw, g["cu_entries"], g["logits"], g["state"],
+                        g["kv"], swa=None, gamma=g["gamma"], eps=cfg.eps, rope_base=cfg.rope_base)
+    torch.cuda.synchronize()
+    kv_o, state_o = O.oracle_cache(d["kv"]), O.oracle_cache(d["state"])
+    rv, rdt = O.raw_values(d["new_raw"])
+    ent, _ = compress.compress_insert(128, d["ctx_lens"].tolist(), d["cu_new"].tolist(), rv, rdt,
+                                      d["cu_entries"].tolist(), d["logits"].numpy(),
+                                      d["gamma"].numpy().astype(np.float64), cfg.eps, cfg.rope_base, 64,
+                                      state_o, kv_o, None)
+    rows = g["kv"].rows.cpu()
+    bt = d["kv"][2]
+    assert len(ent) == int(d["cu_entries"][-1]) > 0
+    for (b, j), c in ent.items():
+        blk, slot = int(bt[b, j // 2]), j % 2
+        gv = O.formats.decode_stored(O.np_rows(rows[blk, slot]), "bf16")
+        ok, r = O.check_rounded_row(gv, c, "bf16")
+        assert ok, f"entry {(b, j)}: err/tol {r:.3g}"
