@@ -87,6 +87,8 @@ _SIGNATURES = {
                                     _F, _F, _I, _P, _P, _P, _SZ]),
     "csa_sparse_attn_decode_fp8": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _CP, _I, _P, _I, _CP,
                                         _I, _F, _F, _I, _P, _P, _P, _P, _P, _SZ]),
+    "csa_compress_index_score": (_I, [_P, _I, _P, _P, _I, _I, ctypes.POINTER(_CJob), _I, _P, _P, _I,
+                                      _I, _P, _I, _I, _P, _CP, _I, _P, _SZ]),
     "csa_read_probe": (_I, [_P, _P, _SZ, _P]),
     "csa_read_probe_sink_words": (_I, []),
 }
@@ -352,6 +354,28 @@ def index_score(cu_q, q_pos, q_idx, head_w, idx_cache: PagedCache, k: int, max_c
                                q_idx.data_ptr(), dtype_code(q_idx.dtype), heads, head_w.data_ptr(),
                                _cref(idx_cache), k, workspace.data_ptr(), workspace.numel())
     _check(st, "csa_index_score")
+
+
+def compress_index_score(ctx_lens: torch.Tensor, cu_new: torch.Tensor, total_new: int,
+                         jobs: list[CompressJob], idx_job: int, cu_q, q_pos, q_idx, head_w,
+                         idx_cache: PagedCache, k: int, max_context: int,
+                         workspace: torch.Tensor) -> None:
+    """compress_insert_many followed by index_score, the compressors running in the score's
+    launch (jobs[idx_job] writes idx_cache and scores the entries it inserts)."""
+    _dev(ctx_lens, "ctx_lens", torch.int32, 1)
+    _dev(cu_new, "cu_new", torch.int32, 1)
+    batch, total_q, heads = _index_common(cu_q, q_pos, q_idx, head_w)
+    if ctx_lens.shape[0] != batch or cu_new.shape[0] != batch + 1:
+        raise ValueError("ctx_lens needs batch entries and cu_new batch + 1")
+    for j in jobs:
+        if j.args[2].shape[0] != batch + 1 or j.args[1].shape[0] != total_new:
+            raise ValueError("cu_entries needs batch + 1 entries and new_raw total_new rows")
+    arr = compress_jobs_array(jobs)
+    st = lib().csa_compress_index_score(
+        _stream(), batch, ctx_lens.data_ptr(), cu_new.data_ptr(), total_new, len(jobs), arr, idx_job,
+        cu_q.data_ptr(), q_pos.data_ptr(), total_q, max_context, q_idx.data_ptr(), dtype_code(q_idx.dtype),
+        heads, head_w.data_ptr(), _cref(idx_cache), k, workspace.data_ptr(), workspace.numel())
+    _check(st, "csa_compress_index_score")
 
 
 def index_select(cu_q, q_pos, k: int, max_context: int, workspace: torch.Tensor,

@@ -72,25 +72,35 @@ static int compress_job_check(const csa_compress_job& j, int batch, int total_ne
   return CSA_OK;
 }
 
+// Validates a compressor call and fills *L; *work = its workgroup count.
+static int compress_prepare(int batch, const int32_t* ctx_lens, const int32_t* cu_new, int total_new,
+                            int num_jobs, const csa_compress_job* jobs, csa::CompressLaunch* L,
+                            int64_t* work) {
+  if (batch <= 0 || total_new < 0 || !ctx_lens || !cu_new) return CSA_EINVAL;
+  if (num_jobs < 1 || num_jobs > csa::kMaxCompressJobs || !jobs) return CSA_EINVAL;
+  *L = csa::CompressLaunch{};
+  L->batch = batch;
+  L->ctx_lens = ctx_lens;
+  L->cu_new = cu_new;
+  L->total_new = total_new;
+  L->num_jobs = num_jobs;
+  *work = 0;
+  for (int i = 0; i < num_jobs; ++i) {
+    const int st = compress_job_check(jobs[i], batch, total_new, &L->jobs[i]);
+    if (st != CSA_OK) return st;
+    *work += (int64_t)jobs[i].total_entries + total_new;
+  }
+  if (*work > 0x7FFFFFFF) return CSA_ENOTSUP;
+  return CSA_OK;
+}
+
 int csa_compress_insert_many(csa_stream_t stream, int batch, const int32_t* ctx_lens,
                              const int32_t* cu_new, int total_new, int num_jobs,
                              const csa_compress_job* jobs) {
-  if (batch <= 0 || total_new < 0 || !ctx_lens || !cu_new) return CSA_EINVAL;
-  if (num_jobs < 1 || num_jobs > csa::kMaxCompressJobs || !jobs) return CSA_EINVAL;
-  csa::CompressLaunch L{};
-  L.batch = batch;
-  L.ctx_lens = ctx_lens;
-  L.cu_new = cu_new;
-  L.total_new = total_new;
-  L.num_jobs = num_jobs;
+  csa::CompressLaunch L;
   int64_t work = 0;
-  for (int i = 0; i < num_jobs; ++i) {
-    const int st = compress_job_check(jobs[i], batch, total_new, &L.jobs[i]);
-    if (st != CSA_OK) return st;
-    work += (int64_t)jobs[i].total_entries + total_new;
-  }
-  if (work == 0) return CSA_OK;
-  if (work > 0x7FFFFFFF) return CSA_ENOTSUP;
+  const int st = compress_prepare(batch, ctx_lens, cu_new, total_new, num_jobs, jobs, &L, &work);
+  if (st != CSA_OK || work == 0) return st;
   return hip_status(csa::launch_compress(L, (hipStream_t)stream));
 }
 
@@ -179,6 +189,42 @@ int csa_index_topk(csa_stream_t stream, int batch, const int32_t* cu_q, const in
   hipError_t e = csa::launch_index_score(L, ws, (hipStream_t)stream);
   if (e != hipSuccess) return CSA_EHIP;
   return hip_status(csa::launch_index_select(L, topk_idx, topk_score, ws, (hipStream_t)stream));
+}
+
+int csa_compress_index_score(csa_stream_t stream, int batch, const int32_t* ctx_lens,
+                             const int32_t* cu_new, int total_new, int num_jobs,
+                             const csa_compress_job* jobs, int idx_job, const int32_t* cu_q,
+                             const int32_t* q_pos, int total_q, int max_context, const void* q_idx,
+                             int q_dtype, int n_heads_idx, const float* head_w,
+                             const csa_cache* idx_cache, int k, void* workspace,
+                             size_t workspace_bytes) {
+  csa::CompressLaunch CL;
+  int64_t work = 0;
+  int st = compress_prepare(batch, ctx_lens, cu_new, total_new, num_jobs, jobs, &CL, &work);
+  if (st != CSA_OK) return st;
+  if (idx_job < 0 || idx_job >= num_jobs) return CSA_EINVAL;
+  st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace);
+  if (st != CSA_OK) return st;
+  st = score_check(total_q, q_idx, q_dtype, n_heads_idx, head_w, idx_cache);
+  if (st != CSA_OK) return st;
+  const csa_compress_job& ij = jobs[idx_job];
+  if (ij.ratio != 4 || ij.out->rows != idx_cache->rows || ij.out->dtype != idx_cache->dtype ||
+      ij.out->block_table != idx_cache->block_table)
+    return CSA_EINVAL;
+  const hipStream_t s = (hipStream_t)stream;
+  if (total_q == 0) return work == 0 ? CSA_OK : hip_status(csa::launch_compress(CL, s));
+  // one launch when the entry scoring stays small: every new indexer key is scored by its
+  // compressor workgroup for each query of its sequence
+  bool fuse = work > 0 && q_dtype == CSA_BF16 && n_heads_idx <= 64 &&
+              (int64_t)ij.total_entries * total_q <= 4096;
+  for (int i = 0; i < num_jobs; ++i) fuse = fuse && jobs[i].ratio == 4;
+  csa::IndexLaunch L{batch, cu_q, q_pos, total_q, max_context, q_idx, q_dtype, n_heads_idx,
+                     head_w, idx_cache, k};
+  const csa::IndexWorkspace ws = csa::index_workspace_carve(workspace, total_q, max_context, k);
+  if (fuse) return hip_status(csa::launch_compress_index_score(L, ws, CL, idx_job, s));
+  hipError_t e = work > 0 ? csa::launch_compress(CL, s) : hipSuccess;
+  if (e != hipSuccess) return CSA_EHIP;
+  return hip_status(csa::launch_index_score(L, ws, s));
 }
 
 size_t csa_sparse_attn_workspace_size(int total_q, int n_heads, int dim, int ratio, int has_topk,

@@ -23,6 +23,7 @@
 //     the candidates' own key range, then writes the winners in ascending entry order with one
 //     prefix scan, resolving exact ties towards lower entry ids.
 #include "common.h"
+#include "compress_dev.h"
 #include "launch.h"
 
 namespace csa {
@@ -42,6 +43,14 @@ struct ScoreArgs {
   DevCache cache;
   float* scores;
   uint32_t* bounds;
+  // With the compressor in the same launch (MFMA kernel only): grid rows y < comp_rows run its
+  // comp_wgs workgroups; ctx_lens[b] / 4 entries of sequence b existed before the step, the
+  // rest are inserted (and scored) by the compressor, so the score workgroups neither read nor
+  // score them.  ctx_lens is NULL otherwise.
+  const int32_t* ctx_lens;
+  int comp_rows, comp_wgs;
+  CompressArgs comp;
+  EntryScorer scorer;
 };
 
 __device__ __forceinline__ int query_entries(const int32_t* q_pos, int qi, int n_max) {
@@ -163,12 +172,22 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
   __shared__ uint32_t hist[256];
   __shared__ int misc[4];
   __shared__ uint32_t red[4], red2[4];
-  const int chunk = blockIdx.x, qi = blockIdx.y;
+  __shared__ CompressSmem<8> csm;
+  if ((int)blockIdx.y < a.comp_rows) {  // a compressor workgroup of the fused launch
+    const int blk = blockIdx.y * gridDim.x + blockIdx.x;
+    if (blk < a.comp_wgs) compress_block<8>(a.comp, blk, csm, &a.scorer);
+    return;
+  }
+  const int chunk = blockIdx.x, qi = blockIdx.y - a.comp_rows;
   const int b = seq_of_wave(a.cu_q, a.batch, qi);
   const int n = query_entries(a.q_pos, qi, a.n_max);
   const int64_t j0 = (int64_t)chunk * C;
   if (j0 >= n) return;
   const int nloc = (int)min((int64_t)C, n - j0);
+  // entries [nold_loc, nloc) of the chunk are this step's (fused launch only)
+  const int nold = a.ctx_lens ? a.ctx_lens[b] / 4 : 0x7FFFFFFF;
+  const int nold_loc = (int)max((int64_t)0, min((int64_t)nloc, (int64_t)nold - j0));
+  const bool any_old = nold_loc > 0;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const int H = a.n_heads;
@@ -202,7 +221,7 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int tile = min(16 * gi + 4 * u + wv, ntiles - 1);
-      const int eloc = min(tile * 16 + ln, nloc - 1);
+      const int eloc = min(tile * 16 + ln, nold_loc - 1);  // (this step's entries are not read)
       const int blk = __builtin_amdgcn_readlane(my_blk, min(4 * gi + u, nblk - 1));
       const int64_t prow = ((int64_t)blk << 6) + (eloc & 63);
       prow_g = lg == u ? prow : prow_g;
@@ -268,7 +287,7 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
   // conditions, so the wait counters keep one group of keys in flight behind the MFMA work
   constexpr int NG = C / 256;
   KeyGroup<KEY_DT> kg[2];
-  load_group(0, kg[0]);
+  if (any_old) load_group(0, kg[0]);
 #pragma unroll
   for (int p = 0; p < HT; ++p)
     *(uint4*)&q_sh[(16 * p + (threadIdx.x >> 4)) * QROW + 8 * (threadIdx.x & 15)] = qv[p];
@@ -294,19 +313,32 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
     wt[mt][3] = w4.w;
   }
 
+  if (any_old) {
 #pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    if (gi + 1 < NG) load_group(gi + 1, kg[(gi + 1) & 1]);
-    compute_group(gi, kg[gi & 1]);
+    for (int gi = 0; gi < NG; ++gi) {
+      if (gi + 1 < NG) load_group(gi + 1, kg[(gi + 1) & 1]);
+      compute_group(gi, kg[gi & 1]);
+    }
+  } else {  // every entry of the chunk is this step's
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) lane_keys[gi] = 0u;
   }
   // Epilogue.  Every lane holds 8 distinct entries' keys (entries past a partial chunk's end
   // repeat its last entry), so the chunk's key range is reduced from registers, and the same
   // barrier that completes sc_sh publishes the per-wave ranges.
   static_assert(C / 256 == 8, "eight groups per chunk");
-  uint32_t klo = lane_keys[0], khi = lane_keys[0];
+  // this step's entries (fused launch) get key 0, which no score reaches: left out of the bound
+  if (nold_loc < nloc) {
 #pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    klo = min(klo, lane_keys[i]);
+    for (int i = 0; i < 8; ++i) {
+      const int eloc = (16 * i + 4 * lg + wv) * 16 + ln;
+      if (eloc >= nold_loc && eloc < nloc) lane_keys[i] = 0u;
+    }
+  }
+  uint32_t klo = 0xFFFFFFFFu, khi = 0u;  // over the scored entries
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    klo = min(klo, lane_keys[i] ? lane_keys[i] : 0xFFFFFFFFu);
     khi = max(khi, lane_keys[i]);
   }
   klo = wave_min_u32(klo);
@@ -316,12 +348,17 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
     red2[wv] = khi;
   }
   __syncthreads();
-  // the chunk's scores leave in full lines, 16 bytes per thread and pass
-  {
+  // the chunk's scores leave in full lines, 16 bytes per thread and pass (this step's entries,
+  // written by the compressor, are skipped)
+  if (nold_loc == nloc) {
     float4* dst = (float4*)(a.scores + (int64_t)qi * a.n_cap + j0);
 #pragma unroll
     for (int p = 0; p < C / 1024; ++p)
       dst[p * 256 + threadIdx.x] = *(const float4*)&sc_sh[4 * (p * 256 + threadIdx.x)];
+  } else {
+    float* dst = a.scores + (int64_t)qi * a.n_cap + j0;
+    for (int e = threadIdx.x; e < C; e += 256)
+      if (e < nold_loc || e >= nloc) dst[e] = any_old ? sc_sh[e] : 0.f;
   }
   // the bound (full chunks): one 256-bin histogram over the chunk's own key range; the bound
   // is the lower edge of the bin that holds the kc-th largest key
@@ -335,9 +372,15 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
     }
     const uint32_t lo = min(min(red[0], red[1]), min(red[2], red[3]));
     const uint32_t hi = max(max(red2[0], red2[1]), max(red2[2], red2[3]));
+    if (nold_loc < kc) {  // fewer than kc scored entries (the rest are this step's): bound 0
+      if (threadIdx.x == 0) a.bounds[(int64_t)qi * a.chunks + chunk] = 0u;
+      return;
+    }
+    // the kc-th largest of the scored entries is a lower bound of the chunk's kc-th largest
     const int shift = max(0, bit_len(hi - lo) - 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) atomicAdd(&hist[((lane_keys[i] - lo) >> shift) & 255u], 1u);
+    for (int i = 0; i < 8; ++i)
+      if (lane_keys[i]) atomicAdd(&hist[((lane_keys[i] - lo) >> shift) & 255u], 1u);
     __syncthreads();
     if (wv == 0) {
       pick_bin_wave0(hist, kc, misc);  // (the crossing lane writes misc[0])
@@ -792,6 +835,25 @@ IndexWorkspace index_workspace_carve(void* ws, int total_q, int max_context, int
   w.cand = (uint2*)take((size_t)total_q * w.n_cap * sizeof(uint2));
   w.cand_info = (int4*)take((size_t)total_q * w.chunks * sizeof(int4));
   return w;
+}
+
+hipError_t launch_compress_index_score(const IndexLaunch& a, const IndexWorkspace& ws,
+                                       const CompressLaunch& c, int score_job, hipStream_t stream) {
+  ScoreArgs s = make_score_args(a, ws);
+  int blocks = 0;
+  s.comp = make_compress_args(c, &blocks);
+  s.comp_wgs = blocks;
+  s.comp_rows = (blocks + ws.chunks - 1) / ws.chunks;
+  s.ctx_lens = c.ctx_lens;
+  s.scorer = EntryScorer{score_job, a.n_heads, a.max_context / 4, ws.n_cap, a.cu_q, a.q_pos,
+                         (const uint16_t*)a.q_idx, a.head_w, ws.scores};
+  // the compressor's rows come first, so its workgroups are dispatched before the score's
+  const dim3 grid(ws.chunks, a.total_q + s.comp_rows);
+  const int ht = (a.n_heads + 15) / 16;
+  if (a.idx_cache->dtype == CSA_FP8_E4M3) launch_mfma<CSA_FP8_E4M3>(s, ht, grid, stream);
+  else if (a.idx_cache->dtype == CSA_FP4_E2M1) launch_mfma<CSA_FP4_E2M1>(s, ht, grid, stream);
+  else launch_mfma<CSA_BF16>(s, ht, grid, stream);
+  return hipGetLastError();
 }
 
 hipError_t launch_index_score(const IndexLaunch& a, const IndexWorkspace& ws, hipStream_t stream) {

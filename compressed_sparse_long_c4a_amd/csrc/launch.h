@@ -84,6 +84,10 @@ struct IndexLaunch {
   int k;
 };
 hipError_t launch_index_score(const IndexLaunch& a, const IndexWorkspace& ws, hipStream_t stream);
+// The compressor jobs of `c` and the index score in one launch (bf16 queries, <= 64 heads, ratio-4
+// jobs; jobs[score_job] writes the indexer keys of a.idx_cache).
+hipError_t launch_compress_index_score(const IndexLaunch& a, const IndexWorkspace& ws,
+                                       const CompressLaunch& c, int score_job, hipStream_t stream);
 hipError_t launch_index_select(const IndexLaunch& a, int32_t* topk_idx, float* topk_score,
                                const IndexWorkspace& ws, hipStream_t stream);
 

@@ -54,6 +54,9 @@ class Step:
         self.out = torch.empty((total_q, H, D), dtype=torch.float32, device=dev)
         self.lse = None
         self.side = None  # second stream for the overlapped schedule (created on first use)
+        # fast(): the step's compressors inside the index-score launch (csa_compress_index_score;
+        # the indexer-key job is the last of _jobs); run() keeps them a launch of their own
+        self.fused = "compress_idx" in cfg.stages and "index" in cfg.stages
         self._bound = {}  # id(g) -> pre-marshalled C calls of the step (see fast())
 
     def compress(self, g=None):
@@ -148,17 +151,27 @@ class Step:
             return r
         B = g["ctx_lens"].shape[0] if "ctx_lens" in g else g["cu_q"].shape[0] - 1
         jobs = self._jobs(g)
-        if jobs:  # every compressor of the step in one launch
+        total_q = g["q_pos"].shape[0]
+        fused = self.fused and bool(jobs)
+        if jobs and not fused:  # every compressor of the step in one launch
             arr = compress_jobs_array(jobs)
             refs.extend([jobs, arr])
             calls.append(("compress", L.csa_compress_insert_many, (
                 B, g["ctx_lens"].data_ptr(), g["cu_new"].data_ptr(), g["new_raw"].shape[0], len(jobs), arr)))
-        total_q = g["q_pos"].shape[0]
-        if "index" in c.stages:
+        if "index" in c.stages and fused:  # the compressors inside the score launch
+            arr = compress_jobs_array(jobs)
+            refs.extend([jobs, arr])
+            calls.append(("index_score", L.csa_compress_index_score, (
+                B, g["ctx_lens"].data_ptr(), g["cu_new"].data_ptr(), g["new_raw"].shape[0], len(jobs), arr,
+                len(jobs) - 1, g["cu_q"].data_ptr(), g["q_pos"].data_ptr(), total_q, c.max_context,
+                g["q_idx"].data_ptr(), dtype_code(g["q_idx"].dtype), g["q_idx"].shape[1],
+                g["head_w"].data_ptr(), cache(g["idx"]), c.k, self.idx_ws.data_ptr(), self.idx_ws.numel())))
+        elif "index" in c.stages:
             calls.append(("index_score", L.csa_index_score, (
                 B, g["cu_q"].data_ptr(), g["q_pos"].data_ptr(), total_q, c.max_context, g["q_idx"].data_ptr(),
                 dtype_code(g["q_idx"].dtype), g["q_idx"].shape[1], g["head_w"].data_ptr(), cache(g["idx"]),
                 c.k, self.idx_ws.data_ptr(), self.idx_ws.numel())))
+        if "index" in c.stages:
             calls.append(("index_select", L.csa_index_select, (
                 B, g["cu_q"].data_ptr(), g["q_pos"].data_ptr(), total_q, c.max_context, c.k,
                 self.topk.data_ptr(), None if self.topk_score is None else self.topk_score.data_ptr(),

@@ -333,6 +333,33 @@ int csa_sparse_attn_decode_fp8(csa_stream_t stream, int batch, const int32_t* cu
                                void* workspace, size_t workspace_bytes);
 
 /*
+ * csa_compress_index_score -- csa_compress_insert_many followed by csa_index_score, with the
+ * compressor running beside the score instead of before it ([vLLM-V4] section 3 part 2,
+ * multi-stream: the pages overlap the compressor with the indexer on a second stream; here
+ * the compressor's workgroups share the score's launch).  The score workgroups read and score
+ * only the entries that existed before the call (the first ctx_lens[b] / 4 of sequence b);
+ * the indexer-key compressor jobs[idx_job] scores each entry it inserts, from the key it
+ * stores, for every query of its sequence that sees the entry.  Scores and chunk bounds land in
+ * the workspace as csa_index_score leaves them, so csa_index_select follows unchanged.
+ *
+ * Arguments: those of csa_compress_insert_many (batch, ctx_lens, cu_new, total_new, num_jobs,
+ * jobs) and of csa_index_score (cu_q, q_pos, total_q, max_context, q_idx, q_dtype,
+ * n_heads_idx, head_w, idx_cache, k, workspace); jobs[idx_job] must have ratio 4 and write
+ * idx_cache (the same rows, dtype and block table).  Queries sit at positions the call
+ * inserts or before (q_pos < ctx_lens[b] + new_b).  The single launch is used for bf16 queries,
+ * at most 64 indexer heads, ratio-4 jobs and total_entries(jobs[idx_job]) * total_q <= 4096
+ * (decode); otherwise the compressor and the score run as two launches with the same result.
+ * Returns the status of the first failing check (nothing is launched then).
+ */
+int csa_compress_index_score(csa_stream_t stream, int batch, const int32_t* ctx_lens,
+                             const int32_t* cu_new, int total_new, int num_jobs,
+                             const csa_compress_job* jobs, int idx_job, const int32_t* cu_q,
+                             const int32_t* q_pos, int total_q, int max_context, const void* q_idx,
+                             int q_dtype, int n_heads_idx, const float* head_w,
+                             const csa_cache* idx_cache, int k, void* workspace,
+                             size_t workspace_bytes);
+
+/*
  * csa_read_probe -- a measurement utility, not a step of the method: reads `bytes` bytes of the
  * device buffer `buf` once each with 16-byte loads and writes one word per workgroup to `sink`
  * (the XOR of the words it read, so no load can be dropped).  Timed on a buffer larger than

@@ -122,21 +122,28 @@ def compare(cfg, d: dict, step, ores: dict) -> dict:
 
 
 def run_step_parity(cfg, queries=None, verbose: bool = False, prep=None, overlap: bool = False,
-                    fast: bool = False, with_scores: bool = True) -> dict:
+                    fast: bool = False, with_scores: bool = True, fast_only: bool = False) -> dict:
     """Draw inputs, run the GPU step and the oracle, compare.  Returns the report.
 
     overlap: the two-stream schedule.  fast: the launch sequence the benchmark times (one
     run(), then the step again through the pre-marshalled calls; a step is idempotent because
     every cache row it writes is a function of rows it does not write).  with_scores: also
-    request the top-k scores (the benchmark does not).  prep(d) may edit the drawn inputs."""
+    request the top-k scores (the benchmark does not).  fast_only: the pre-marshalled calls on
+    fresh inputs with no run() before them, so nothing the other path wrote can stand in for an
+    output the fast path failed to write.  prep(d) may edit the drawn inputs."""
     from compressed_sparse_long_c4a_amd import pipeline
     d = inputs.draw(cfg)
     if prep is not None:
         prep(d)
     g = pipeline.to_device(d)
     step = pipeline.Step(cfg, g, with_scores=with_scores)
-    step.run_overlapped() if overlap else step.run()
-    if fast:
+    if fast_only:
+        step.fast(g)
+    elif overlap:
+        step.run_overlapped()
+    else:
+        step.run()
+    if fast and not fast_only:
         torch.cuda.synchronize()
         step.lse = None
         step.fast(g)

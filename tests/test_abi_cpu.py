@@ -197,3 +197,30 @@ def test_read_probe_validation(csa):
     assert L.csa_read_probe(None, 16, 0, 16) == csa.EINVAL
     assert L.csa_read_probe(None, 16, 1000, 16) == csa.EINVAL
     assert L.csa_read_probe(None, 8, 1024, 16) == csa.EINVAL
+
+
+def test_compress_index_score_validation(csa):
+    """csa_compress_index_score checks the compressor jobs, the index arguments and that the
+    indexer-key job writes the indexer cache, before launching (fake pointers)."""
+    L = csa.lib()
+    P = ctypes.pointer
+    st = csa._CCache(1, None, csa.BF16, 576, 256, 10, 1, 8)
+    kv = csa._CCache(1, 1, csa.FP8_E4M3, 576, 64, 10, 1, 8)
+    ist = csa._CCache(2, None, csa.BF16, 128, 256, 10, 3, 8)
+    idx = csa._CCache(4, 5, csa.FP8_E4M3, 128, 64, 10, 6, 8)
+    other = csa._CCache(7, 5, csa.FP8_E4M3, 128, 64, 10, 6, 8)
+    main = csa._CJob(4, 1, csa.BF16, 1, 1, 1, None, 1e-6, 1e4, 64, P(st), P(kv), None)
+    ij = csa._CJob(4, 1, csa.BF16, 1, 1, 1, None, 1e-6, 1e4, 64, P(ist), P(idx), None)
+    ij_other = csa._CJob(4, 1, csa.BF16, 1, 1, 1, None, 1e-6, 1e4, 64, P(ist), P(other), None)
+    jobs = (csa._CJob * 2)(main, ij)
+
+    def call(jobs_arr, n, idx_job, ws_bytes=1 << 40, cache=idx):
+        return L.csa_compress_index_score(None, 1, 1, 1, 1, n, jobs_arr, idx_job, 1, 1, 1, 1024, 1,
+                                          csa.BF16, 64, 1, P(cache), 8, 1, ws_bytes)
+
+    assert call(jobs, 2, 2) == csa.EINVAL            # idx_job out of range
+    assert call(jobs, 2, -1) == csa.EINVAL
+    assert call(jobs, 2, 0) == csa.EINVAL            # job 0 does not write the indexer cache
+    assert call((csa._CJob * 2)(main, ij_other), 2, 1) == csa.EINVAL
+    assert call(jobs, 2, 1, ws_bytes=16) == csa.EWORKSPACE
+    assert call(jobs, 0, 0) == csa.EINVAL            # no job
