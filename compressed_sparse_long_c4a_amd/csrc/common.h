@@ -55,10 +55,18 @@ struct RopeTable {
   double theta[64];
 };
 
+// (the last table is kept per host thread: a decode loop asks for the same one every call)
 inline RopeTable make_rope_table(float base, int rope_dims) {
+  thread_local float last_base = 0.f;
+  thread_local int last_dims = -1;
+  thread_local RopeTable last{};
+  if (rope_dims == last_dims && base == last_base) return last;
   RopeTable t{};
   for (int i = 0; i < rope_dims / 2 && i < 64; ++i)
     t.theta[i] = std::pow((double)base, -2.0 * (double)i / (double)rope_dims);
+  last = t;
+  last_base = base;
+  last_dims = rope_dims;
   return t;
 }
 

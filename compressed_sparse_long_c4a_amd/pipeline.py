@@ -12,7 +12,8 @@ import torch
 import ctypes
 
 from . import (OK, CompressJob, CsaError, PagedCache, compress_insert, compress_insert_many,
-               compress_jobs_array, dtype_code, index_score, index_select, index_workspace_size, lib,
+               compress_index_score, compress_jobs_array, dtype_code, index_score, index_select,
+               index_workspace_size, lib,
                sparse_attn_decode, sparse_attn_workspace_size)
 
 CACHE_KEYS = ("kv", "swa", "state", "idx", "idx_state")
@@ -88,6 +89,15 @@ class Step:
         c = self.cfg
         compress_insert(4, g["ctx_lens"], g["cu_new"], g["new_idx_raw"], g["cu_entries"], g["idx_logits"],
                         g["idx_state"], g["idx"], None, None, c.eps, c.rope_base, 64)
+
+    def compress_index_score(self, g=None):
+        """Every compressor of the step inside the index-score launch (see fast())."""
+        g = g or self.g
+        c = self.cfg
+        jobs = self._jobs(g)
+        compress_index_score(g["ctx_lens"], g["cu_new"], g["new_raw"].shape[0], jobs, len(jobs) - 1,
+                             g["cu_q"], g["q_pos"], g["q_idx"], g["head_w"], g["idx"], c.k, c.max_context,
+                             self.idx_ws)
 
     def index_score(self, g=None):
         g = g or self.g
