@@ -14,6 +14,8 @@ of the method's definition:
 
 from __future__ import annotations
 
+import copy
+
 import numpy as np
 import torch
 
@@ -39,8 +41,29 @@ def _oracle_scale(ocache, b, r):
     return None if ocache.scales is None else float(ocache.scales[blk, slot])
 
 
+def _with_gpu_rows(ocache, gpu_cache, slots):
+    """A copy of an oracle cache that holds the GPU's stored rows at the (block, slot) pairs
+    ``slots`` (rows the step wrote and that passed their rounding check)."""
+    rows, scales = gpu_cache
+    c = copy.copy(ocache)
+    c.rows = ocache.rows.copy()
+    c.scales = None if ocache.scales is None else ocache.scales.copy()
+    for blk, slot in slots:
+        c.rows[blk, slot] = O.np_rows(rows[blk, slot])
+        if c.scales is not None:
+            c.scales[blk, slot] = scales[blk, slot].numpy()
+    return c
+
+
 def compare(cfg, d: dict, step, ores: dict) -> dict:
+    """Check every output of the step.  Stored rows are checked against the oracle's exact
+    values with the rounding allowance of tests/oracle_step.check_rounded_row; attention is then
+    checked against the oracle run on the rows the GPU stored (each stage on the GPU's own
+    inputs), because a value within float32 accuracy of a rounding midpoint may be rounded
+    either way and one code of a dominant window row moves the output by more than the
+    attention tolerance."""
     rep = {"fail": [], "checked": {}, "worst": {}}
+    stored = {"kv": [], "swa": []}  # (block, slot) of the written rows that passed
 
     def note(kind, ok, ratio, where):
         rep["checked"][kind] = rep["checked"].get(kind, 0) + 1
@@ -61,11 +84,15 @@ def compare(cfg, d: dict, step, ores: dict) -> dict:
             gv, gs = _rows_at(kv, d["kv"][2], b, j)
             ok, r = O.check_rounded_row(gv, c, fmt, gs, _oracle_scale(ores["kv"], b, j))
             note("entry", ok, r, (b, j))
+            if ok:
+                stored["kv"].append(tuple(int(x) for x in ores["kv"].locate(b, j)))
         swa = cpu_cache("swa")
         for (b, p), v in ores["window_rows"].items():
             gv, gs = _rows_at(swa, d["swa"][2], b, p)
             ok, r = O.check_rounded_row(gv, v, fmt, gs, _oracle_scale(ores["swa"], b, p))
             note("window_row", ok, r, (b, p))
+            if ok:
+                stored["swa"].append(tuple(int(x) for x in ores["swa"].locate(b, p)))
         st = cpu_cache("state")
         W = inputs.LOGITS_PER_ENTRY[cfg.ratio]
         raw = d["new_raw"]
@@ -108,11 +135,20 @@ def compare(cfg, d: dict, step, ores: dict) -> dict:
         out = step.out.cpu().numpy()
         lse = None if step.lse is None else step.lse.cpu().numpy()
         topk_gpu = step.topk.cpu().numpy() if "index" in cfg.stages else None
+        res = ores
+        if stored["kv"] or stored["swa"]:
+            res = dict(ores, kv=_with_gpu_rows(ores["kv"], cpu_cache("kv"), stored["kv"]),
+                       swa=_with_gpu_rows(ores["swa"], cpu_cache("swa"), stored["swa"]))
         for i in ores["queries"]:
-            ref_o, ref_l = ores["out"][i], ores["lse"][i]
-            if same_set.get(i, True) is False:
+            if "index" in cfg.stages and same_set.get(i, True) is False:
                 # a near tie (accepted above): the oracle attends over the GPU's own selection
-                ref_o, ref_l = O.attend_query(cfg, d, ores, i, topk_gpu[i])
+                ref_o, ref_l = O.attend_query(cfg, d, res, i, topk_gpu[i])
+            elif res is ores:
+                ref_o, ref_l = ores["out"][i], ores["lse"][i]
+            else:
+                ids = ores["topk"][i] if "index" in cfg.stages else (
+                    None if "topk" not in d else d["topk"][i].numpy())
+                ref_o, ref_l = O.attend_query(cfg, d, res, i, ids)
             ok, r = O.allclose_out(out[i], ref_o)
             note("out", ok, r, i)
             if lse is not None:

@@ -6,7 +6,7 @@ Cases: the 1M fp8 decode's shapes at shorter contexts; sequences whose new entry
 (no entry of that chunk existed before: the score workgroup only writes padding) or closes a
 full chunk (the chunk bound counts 2,047 scored entries); a k so large that the full chunk's
 bound needs more entries than were scored (bound 0); the first positions of a sequence (entry 0
-new); and an fp4 indexer cache.
+new); an fp4 indexer cache; several queries over several new tokens per sequence, ragged.
 """
 
 import dataclasses
@@ -29,6 +29,13 @@ CASES = {
     "early": D(C.C4A_1M_B4_FP8, name="fused_early", ctx_after=(1, 2, 3, 4, 5, 8, 9, 130), n_heads=16,
                k=8),
     "fp4_indexer": C.scaled(C.C4A_1M_B4_FP4IDX, (9220, 4099, 2562, 2049), k=256, name_suffix="fused"),
+    # several queries per sequence over several new tokens: a new entry is seen by the queries at
+    # or after its anchor only (9220: the last query; 4099: all four)
+    "multi_query": D(C.C4A_1M_B4_FP8, name="fused_multi_query", ctx_after=(9220, 4099, 2562, 2049),
+                     new_tokens=4, q_per_seq=4, k=256, n_heads=16),
+    # ragged: two entries in one sequence, none in another, queries fewer than new tokens
+    "ragged": D(C.C4A_1M_B4_FP8, name="fused_ragged", ctx_after=(8200, 4099, 2563, 2049),
+                new_tokens=(8, 5, 3, 1), q_per_seq=(8, 2, 3, 1), k=256, n_heads=16),
 }
 
 

@@ -4,6 +4,7 @@ Each case runs every stage of its workload (compress, index/top-k, attention) th
 ABI on identical seeded inputs and applies the acceptance rules of tests/pipeline_check.py.
 """
 
+import dataclasses
 import pytest
 
 from tests import pipeline_check as P
@@ -15,6 +16,10 @@ CASES = {
     "c4a_bf16_decode": C.scaled(C.C4A_128K_B32, (20480, 12288, 8191, 4102), k=512),
     "c128a_bf16_decode": C.scaled(C.C128A_1M_B8, (16384, 8192, 19456 - 1000, 300), gamma=True),
     "c4a_bf16_prefill": C.scaled(C.C4A_PREFILL_64K, (2048 + 512,), new_tokens=512, q_per_seq=512, k=128),
+    # fp8 caches, four new tokens and four queries per sequence (queries see the step's own
+    # entries and window rows, some in a block the step opens)
+    "c4a_fp8_multi_query": dataclasses.replace(P.SMALL_DECODE, name="c4a_fp8_multi_query", new_tokens=4,
+                                               q_per_seq=4, n_heads=16),
 }
 
 
