@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "c4a sparse decode query-tokens/s and achieved HBM GB/s at 1M context"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "index_score_mfma_c4a_1m_b4_counters.txt")
 INDEX_SRC = os.path.join(ROOT, "compressed_sparse_long_c4a_amd", "csrc", "index.hip")
 
@@ -40,12 +41,23 @@ def row_bytes(dtype: str, dim: int) -> int:
     return {"f32": 4 * dim, "bf16": 2 * dim, "fp8": dim + 4, "fp4": dim // 2 + dim // 16}[dtype]
 
 
+def _per_seq(cfg, d):
+    """(query positions, entries visible to each query, sequence of each query)."""
+    qpos = d["q_pos"].tolist()
+    cu_q = d["cu_q"].tolist()
+    seq = [b for b in range(cfg.batch) for _ in range(cu_q[b + 1] - cu_q[b])]
+    return qpos, [(t + 1) // cfg.ratio for t in qpos], seq
+
+
 def algorithmic_bytes(cfg, d) -> dict:
-    """Bytes the method must move in one step (no scratch, no re-reads), per stage."""
+    """Bytes the method must move in one step (no scratch, no re-reads), per stage.  Keys and
+    rows shared by several queries of a sequence count once: per sequence the indexer keys of
+    its latest query, and at most the entries it has (or the sum of its queries' top-k) plus the
+    window positions its queries span."""
     B, H, D, W = cfg.batch, cfg.n_heads, cfg.dim, cfg.window
     total_q = d["q_pos"].shape[0]
-    qpos = d["q_pos"].tolist()
-    n_vis = [(t + 1) // cfg.ratio for t in qpos]
+    qpos, n_vis, seq = _per_seq(cfg, d)
+    n_seq = [max([n for n, b2 in zip(n_vis, seq) if b2 == b], default=0) for b in range(B)]
     kvrow = row_bytes(cfg.kv_dtype, D)
     idx_row = row_bytes(cfg.idx_dtype, 128)
     rawb = 2 if cfg.raw_dtype == "bf16" else 4
@@ -60,12 +72,33 @@ def algorithmic_bytes(cfg, d) -> dict:
         out["compress_idx"] = e * (Wc * 128 * rawb + Wc * 4 + idx_row) + new * 2 * 128 * rawb
     if "index" in cfg.stages:
         qb = 2 if cfg.idx_q_dtype == "bf16" else 4
-        out["index_score"] = sum(n_vis) * idx_row + total_q * cfg.idx_heads * (128 * qb + 4)
+        out["index_score"] = sum(n_seq) * idx_row + total_q * cfg.idx_heads * (128 * qb + 4)
         out["index_select"] = total_q * cfg.k * 4
     if "attn" in cfg.stages:
-        rows = sum((min(cfg.k, n) if "index" in cfg.stages else n) + min(W, t + 1) for n, t in zip(n_vis, qpos))
+        rows = 0
+        for b in range(B):
+            qs = [(n, t) for n, t, b2 in zip(n_vis, qpos, seq) if b2 == b]
+            if not qs:
+                continue
+            sel = sum(min(cfg.k, n) for n, _ in qs) if "index" in cfg.stages else sum(n for n, _ in qs)
+            t_lo, t_hi = min(t for _, t in qs), max(t for _, t in qs)
+            rows += min(n_seq[b], sel) + (t_hi - max(0, t_lo - W + 1) + 1)
         qb = 2 if cfg.q_dtype == "bf16" else 4
         out["attn"] = rows * kvrow + total_q * H * (D * qb + D * 4 + 4)
+    return out
+
+
+def algorithmic_flops(cfg, d) -> dict:
+    """Multiply-add work of the two contractions (2 flops each): the indexer's q.k over every
+    (query, visible entry, indexer head) and attention's QK and PV over every (query, head, row)."""
+    qpos, n_vis, _ = _per_seq(cfg, d)
+    out = {}
+    if "index" in cfg.stages:
+        out["index_score"] = 2 * cfg.idx_heads * 128 * sum(n_vis)
+    if "attn" in cfg.stages:
+        rows = sum((min(cfg.k, n) if "index" in cfg.stages else n) + min(cfg.window, t + 1)
+                   for n, t in zip(n_vis, qpos))
+        out["attn"] = 4 * cfg.n_heads * cfg.dim * rows
     return out
 
 
@@ -85,10 +118,12 @@ def score_kernel_sha1() -> str:
     return hashlib.sha1(text[a:b].encode()).hexdigest()
 
 
-def counters_traffic():
+def counters_traffic(cfg):
     """HBM bytes per index-score launch from the committed rocprofv3 counter summary, or None
-    when there is none or it was taken from a different version of the kernel source."""
-    if not os.path.exists(COUNTERS_FILE):
+    when there is none, it was taken from a different version of the kernel source, or the
+    workload is not the one it was taken on (the 1M c4a fp8 decode)."""
+    from workloads import configs
+    if cfg.name != configs.HEADLINE.name or not os.path.exists(COUNTERS_FILE):
         return None
     kv = {}
     for line in open(COUNTERS_FILE):
@@ -427,6 +462,8 @@ def main() -> int:
 
     ab = algorithmic_bytes(cfg, d)
     step_bytes = sum(ab.values())
+    fl = algorithmic_flops(cfg, d)
+    step_flops = sum(fl.values())
     total_q = d["q_pos"].shape[0]
     # the headline: the K steps replayed from the HIP graph (the pages deploy with full CUDA
     # graphs); the eager issue of the same K steps is reported beside it
@@ -451,6 +488,8 @@ def main() -> int:
         "hbm_gbs": round(step_bytes / (ms_head / 1e3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms_head / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": step_bytes,
+        "algorithmic_flops_per_step": step_flops,
+        "mfma_frac": round(step_flops / (ms_head / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "stages_us": stages,
         "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 5),
         "ms_per_step_two_stream": None if ms_two is None else round(ms_two, 5),
@@ -465,15 +504,26 @@ def main() -> int:
     }
     if has_index:
         launch_bytes = score_launch_bytes(step, ab)
+        launch_flops = fl["index_score"]
         achieved = launch_bytes / (score_ms / 1e3) / 1e9
-        result["roofline"] = {
-            "kernel": "index_score_mfma" + (" (with the compressor workgroups)" if step.fused else ""),
-            "bound": "hbm", "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": counters_traffic(), "launch_us": round(score_ms * 1e3, 2),
-            "algorithmic_bytes_per_launch": launch_bytes,
-        }
-        if not args.no_stream_probe:
+        kname = "index_score_mfma" + (" (with the compressor workgroups)" if step.fused else "")
+        if launch_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > launch_bytes / (HBM_PEAK_GBS * 1e9):
+            # many queries per sequence share each key: the bf16 contraction bounds the kernel
+            tf = launch_flops / (score_ms / 1e3) / 1e12
+            result["roofline"] = {
+                "kernel": kname, "bound": "mfma", "achieved": round(tf, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "launch_us": round(score_ms * 1e3, 2),
+                "algorithmic_flops_per_launch": launch_flops, "algorithmic_bytes_per_launch": launch_bytes,
+            }
+        else:
+            result["roofline"] = {
+                "kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": counters_traffic(cfg), "launch_us": round(score_ms * 1e3, 2),
+                "algorithmic_bytes_per_launch": launch_bytes,
+            }
+        if not args.no_stream_probe and result["roofline"]["bound"] == "hbm":
             sr = stream_read_gbs()
             result["roofline"]["stream_read_gbs"] = round(sr, 1)
             result["roofline"]["frac_of_stream_read"] = round(achieved / sr, 4)

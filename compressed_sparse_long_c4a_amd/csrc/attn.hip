@@ -35,7 +35,9 @@
 //   partial (m, l, O) per head leaves the workgroup.
 // Kernel 2 (attn_merge), grid (4-head group, query), one wave per head: combines the splits
 //   by their softmax statistics, normalises, applies R_t^{-1} to the last rope_dims dims
-//   (angles formed and reduced in float64) and writes out / lse.
+//   (angles formed and reduced in float64) and writes out / lse.  When every query's rows fit
+//   one split (prefill chunks: many queries, few rows each) and only float32 output is wanted,
+//   kernel 1 finishes the rows itself with the same operations and kernel 2 is not launched.
 #include <type_traits>
 
 #include "common.h"
@@ -66,7 +68,64 @@ struct Args {
   float* part_ml;   // [total_q][splits][hgp][2]  (m in log2 units, l)
   int xcd_map;      // 1-D grid with the head groups of a (split, query) on one XCD
   int units;        // splits * total_q
+  // single split (splits == 1, float32 output only): the workgroup writes the finished rows
+  int direct, rope_dims;
+  float* out;       // [total_q][n_heads][DIM]
+  float* lse;       // [total_q][n_heads] or NULL
+  RopeTable rope;
 };
+
+// The workgroup's 16 head rows leave as split partials (O relative to 2^M, and (M, L) per
+// head) for attn_merge, or -- when the query's rows are one split and only float32 output is
+// wanted -- finished: O / L, R_t^{-1} on the last rope_dims dims, and the lse, with the same
+// operations attn_merge applies to a single split (its weight 2^(M - M) is exactly 1), so both
+// routes give the same bits.  mb: the merged rows in LDS (published); thread h < 16 passes
+// head h's (M, L) in (Mh, Lh); hml: LDS for them.  Called by every thread.
+template <int DIM, int NT>
+__device__ __forceinline__ void store_head_rows(const Args& a, int s, int hg, int qi,
+                                                const float (*mb)[DIM + 4], float (*hml)[2],
+                                                float Mh, float Lh) {
+  const int tid = threadIdx.x;
+  if (a.direct) {
+    if (tid < 16) {
+      hml[tid][0] = Mh;
+      hml[tid][1] = Lh;
+    }
+    __syncthreads();
+    const int t = a.q_pos[qi];
+    const int rope0 = DIM - a.rope_dims;
+    for (int i = tid; i < 16 * DIM / 4; i += NT) {
+      const int h = i / (DIM / 4), d = 4 * (i - h * (DIM / 4));
+      const int hq = 16 * hg + h;
+      if (hq >= a.n_heads) continue;
+      const float L = hml[h][1];
+      const float inv = L > 0.f ? 1.0f / L : 0.f;
+      const float4 v = *(const float4*)&mb[h][d];
+      float4 r = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+      if (d >= rope0) {  // pairs (d, d+1) and (d+2, d+3) by -t theta_i
+        float c0, s0, c1, s1;
+        rope_cos_sin(-(double)t, a.rope.theta[(d - rope0) / 2], c0, s0);
+        rope_cos_sin(-(double)t, a.rope.theta[(d - rope0) / 2 + 1], c1, s1);
+        r = make_float4(r.x * c0 - r.y * s0, r.x * s0 + r.y * c0, r.z * c1 - r.w * s1, r.z * s1 + r.w * c1);
+      }
+      *(float4*)(a.out + ((int64_t)qi * a.n_heads + hq) * DIM + d) = r;
+    }
+    if (a.lse && tid < 16 && 16 * hg + tid < a.n_heads) {
+      const float M = hml[tid][0], L = hml[tid][1];
+      a.lse[(int64_t)qi * a.n_heads + 16 * hg + tid] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
+  const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg;
+  for (int i = tid; i < 16 * DIM / 4; i += NT) {
+    const int h = i / (DIM / 4), d = 4 * (i - h * (DIM / 4));
+    *(float4*)(a.part_o + (pbase + h) * DIM + d) = *(const float4*)&mb[h][d];
+  }
+  if (tid < 16) {
+    a.part_ml[(pbase + tid) * 2 + 0] = Mh;
+    a.part_ml[(pbase + tid) * 2 + 1] = Lh;
+  }
+}
 
 // Workgroup coordinates (split, head group, query).  With the XCD map the grid is 1-D:
 // consecutive workgroup ids go to the eight XCDs in turn, so the head groups of one (split,
@@ -164,6 +223,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial(Args a) {
   __shared__ __attribute__((aligned(16))) char tile_sh[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
   __shared__ f32x4 sx_sh[2][kRG][4][64];  // partial S^T of each quarter: [step parity][row group]
   __shared__ float ml_sh[kRG][16][2];
+  __shared__ float hml_sh[16][2];  // per head (M, L) of the workgroup
 
   int s, hg, qi;
   if (!wg_coords(a, s, hg, qi)) return;
@@ -467,23 +527,16 @@ __global__ __launch_bounds__(kThreads) void attn_partial(Args a) {
     }
     __syncthreads();
   }
-  const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg;
-  for (int i = tid; i < 16 * DIM / 4; i += kThreads) {
-    const int h = i / (DIM / 4), d = 4 * (i - h * (DIM / 4));
-    *(float4*)(a.part_o + (pbase + h) * DIM + d) = *(const float4*)&mb[h][d];
-  }
+  float Mh = -INFINITY, L = 0.f;
   if (tid < 16) {
     const int h = tid;
-    float Mh = -INFINITY;
 #pragma unroll
     for (int g = 0; g < kRG; ++g) Mh = fmaxf(Mh, ml_sh[g][h][0]);
-    float L = 0.f;
 #pragma unroll
     for (int g = 0; g < kRG; ++g)
       if (ml_sh[g][h][0] != -INFINITY) L += exp2f(ml_sh[g][h][0] - Mh) * ml_sh[g][h][1];
-    a.part_ml[(pbase + h) * 2 + 0] = Mh;
-    a.part_ml[(pbase + h) * 2 + 1] = L;
   }
+  store_head_rows<DIM, kThreads>(a, s, hg, qi, mb, hml_sh, Mh, L);
 }
 
 // ---- fp8 rows with bf16 queries.  A row group's four waves take one 64-row chunk per step:
@@ -510,6 +563,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_fp8(Args a) {
   __shared__ uint4 p_sh[kRG][4][64];         // P of each QK tile, lane-major {4 hi, 4 lo} bf16
   __shared__ float mx_sh[kRG][4][16];        // per-head maximum logit of each QK tile
   __shared__ float ml_sh[kRG][4][16][2];     // (m, l) of every wave, for the final merge
+  __shared__ float hml_sh[16][2];            // per head (M, L) of the workgroup
 
   const int s = blockIdx.x, hg = blockIdx.y, qi = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -747,26 +801,19 @@ __global__ __launch_bounds__(kThreads) void attn_partial_fp8(Args a) {
     }
     __syncthreads();
   }
-  const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg;
-  for (int i = tid; i < 16 * DIM / 4; i += kThreads) {
-    const int h = i / (DIM / 4), d = 4 * (i - h * (DIM / 4));
-    *(float4*)(a.part_o + (pbase + h) * DIM + d) = *(const float4*)&mb[h][d];
-  }
+  float Mh = -INFINITY, L = 0.f;
   if (tid < 16) {
     const int h = tid;
-    float Mh = -INFINITY;
 #pragma unroll
     for (int g = 0; g < kRG; ++g) Mh = fmaxf(Mh, ml_sh[g][0][h][0]);
-    float L = 0.f;
 #pragma unroll
     for (int g = 0; g < kRG; ++g) {
       const float mg = ml_sh[g][0][h][0];
       if (mg != -INFINITY)
         L += exp2f(mg - Mh) * (ml_sh[g][0][h][1] + ml_sh[g][1][h][1] + ml_sh[g][2][h][1] + ml_sh[g][3][h][1]);
     }
-    a.part_ml[(pbase + h) * 2 + 0] = Mh;
-    a.part_ml[(pbase + h) * 2 + 1] = L;
   }
+  store_head_rows<DIM, kThreads>(a, s, hg, qi, mb, hml_sh, Mh, L);
 }
 
 struct MergeArgs {
@@ -971,6 +1018,12 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, const AttnPlan& p, void* work
   const size_t slots = (size_t)L.total_q * p.splits * p.head_groups * 16;
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + ((slots * dim * sizeof(float) + 255) & ~(size_t)255));
+  // one split and float32 output only: the partial kernel writes the finished rows itself
+  a.direct = p.splits == 1 && L.out != nullptr && L.out_fp8 == nullptr;
+  a.rope_dims = L.rope_dims;
+  a.out = L.out;
+  a.lse = L.lse;
+  a.rope = make_rope_table(L.rope_base, L.rope_dims);
   const dim3 grid(p.splits, p.head_groups, L.total_q);
   a.units = p.splits * L.total_q;
   // the generic kernel (bf16 / f32 rows, or f32 queries) takes the XCD-grouped 1-D grid; the
@@ -983,14 +1036,14 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, const AttnPlan& p, void* work
     default: launch_q<CSA_F32>(a, L.q_dtype, dim, grid_xcd, stream); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.direct) return e;
   MergeArgs m{};
   m.n_heads = L.n_heads;
   m.splits = p.splits;
   m.hgp = a.hgp;
   m.dim = dim;
   m.rope_dims = L.rope_dims;
-  m.rope = make_rope_table(L.rope_base, L.rope_dims);
+  m.rope = a.rope;
   m.q_pos = L.q_pos;
   m.part_o = a.part_o;
   m.part_ml = a.part_ml;

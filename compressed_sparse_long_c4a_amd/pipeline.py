@@ -56,8 +56,13 @@ class Step:
         self.lse = None
         self.side = None  # second stream for the overlapped schedule (created on first use)
         # fast(): the step's compressors inside the index-score launch (csa_compress_index_score;
-        # the indexer-key job is the last of _jobs); run() keeps them a launch of their own
-        self.fused = "compress_idx" in cfg.stages and "index" in cfg.stages
+        # the indexer-key job is the last of _jobs) where that call takes its single launch: bf16
+        # indexer queries, at most 64 indexer heads, ratio 4 and at most 4,096 (new entry, query)
+        # pairs (decode).  Otherwise, and always in run(), the compressors are a launch of their own.
+        new_entries = sum(L // 4 - (L - cfg.new_of(b)) // 4 for b, L in enumerate(cfg.ctx_after))
+        self.fused = ("compress_idx" in cfg.stages and "index" in cfg.stages and cfg.ratio == 4
+                      and cfg.idx_q_dtype == "bf16" and cfg.idx_heads <= 64
+                      and new_entries * total_q <= 4096)
         self._bound = {}  # id(g) -> pre-marshalled C calls of the step (see fast())
 
     def compress(self, g=None):

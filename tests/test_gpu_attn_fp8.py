@@ -28,6 +28,13 @@ CASES = [
     # bf16 caches, c128a (every causal entry), window 128
     D(C.C128A_1M_B8, name="attn_fp8out_c128a_bf16", ctx_after=(70000, 300, 129, 1),
       stages=("attn",)),
+    # many queries with few rows each: one split per query, so csa_sparse_attn_decode finishes
+    # the rows in the partial kernel while the fp8 entry point merges; the float32 rows of the
+    # two must agree bit for bit (fp8 rows, then bf16 rows)
+    D(C.C4A_1M_B4_FP8, name="attn_fp8out_one_split_fp8", ctx_after=(40000, 39999, 9000, 300),
+      new_tokens=64, q_per_seq=64, n_heads=16, k=256, stages=("attn",)),
+    D(C.C4A_PREFILL_64K, name="attn_fp8out_one_split_bf16", ctx_after=(2048 + 256,), new_tokens=256,
+      q_per_seq=256, k=128, stages=("attn",)),
 ]
 
 

@@ -20,6 +20,10 @@ CASES = {
     # entries and window rows, some in a block the step opens)
     "c4a_fp8_multi_query": dataclasses.replace(P.SMALL_DECODE, name="c4a_fp8_multi_query", new_tokens=4,
                                                q_per_seq=4, n_heads=16),
+    # fp8 caches, a 64-token chunk per sequence: each query's rows are one split, finished by
+    # the partial kernel without the merge
+    "c4a_fp8_chunk": dataclasses.replace(P.SMALL_DECODE, name="c4a_fp8_chunk", new_tokens=64, q_per_seq=64,
+                                         n_heads=16),
 }
 
 
