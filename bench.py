@@ -414,10 +414,10 @@ def main() -> int:
     names = [s for s in ("compress", "index_score", "index_select", "attn")
              if (s in cfg.stages) or (s.startswith("index") and has_index)
              or (s == "compress" and "compress_idx" in cfg.stages)]
-    if step.fused:
+    if step.via_score:
         names.remove("compress")
     run_stage = {"compress": step.compress_all,
-                 "index_score": step.compress_index_score if step.fused else step.index_score,
+                 "index_score": step.compress_index_score if step.via_score else step.index_score,
                  "index_select": step.index_select, "attn": lambda g: step.attn(g, with_lse=False)}
     evs = {s: [] for s in names}
     for i in range(min(K, 100)):

@@ -89,6 +89,7 @@ _SIGNATURES = {
                                         _I, _F, _F, _I, _P, _P, _P, _P, _P, _SZ]),
     "csa_compress_index_score": (_I, [_P, _I, _P, _P, _I, _I, ctypes.POINTER(_CJob), _I, _P, _P, _I,
                                       _I, _P, _I, _I, _P, _CP, _I, _P, _SZ]),
+    "csa_compress_index_score_launches": (_I, [_I, ctypes.POINTER(_CJob), _I, _I, _I, _I, _I]),
     "csa_read_probe": (_I, [_P, _P, _SZ, _P]),
     "csa_read_probe_sink_words": (_I, []),
 }
@@ -376,6 +377,16 @@ def compress_index_score(ctx_lens: torch.Tensor, cu_new: torch.Tensor, total_new
         cu_q.data_ptr(), q_pos.data_ptr(), total_q, max_context, q_idx.data_ptr(), dtype_code(q_idx.dtype),
         heads, head_w.data_ptr(), _cref(idx_cache), k, workspace.data_ptr(), workspace.numel())
     _check(st, "csa_compress_index_score")
+
+
+def compress_index_score_launches(jobs: list[CompressJob], idx_job: int, total_new: int, total_q: int,
+                                  q_dtype: torch.dtype, heads: int) -> int:
+    """Kernel launches compress_index_score makes for these arguments (1: the compressors run
+    inside the score launch); the library decides, nothing is launched."""
+    n = lib().csa_compress_index_score_launches(len(jobs), compress_jobs_array(jobs), idx_job, total_new,
+                                                total_q, dtype_code(q_dtype), heads)
+    _check(min(n, 0), "csa_compress_index_score_launches")
+    return n
 
 
 def index_select(cu_q, q_pos, k: int, max_context: int, workspace: torch.Tensor,

@@ -191,6 +191,28 @@ int csa_index_topk(csa_stream_t stream, int batch, const int32_t* cu_q, const in
   return hip_status(csa::launch_index_select(L, topk_idx, topk_score, ws, (hipStream_t)stream));
 }
 
+// One launch for csa_compress_index_score when the entry scoring stays small: every new indexer
+// key is scored by its compressor workgroup for each query of its sequence (bf16 queries, at
+// most 64 indexer heads, ratio-4 jobs, at most 4,096 (new entry, query) pairs).
+static bool single_launch(int num_jobs, const csa_compress_job* jobs, int idx_job, int64_t work,
+                          int total_q, int q_dtype, int n_heads_idx) {
+  bool fuse = work > 0 && total_q > 0 && q_dtype == CSA_BF16 && n_heads_idx <= 64 &&
+              (int64_t)jobs[idx_job].total_entries * total_q <= 4096;
+  for (int i = 0; i < num_jobs; ++i) fuse = fuse && jobs[i].ratio == 4;
+  return fuse;
+}
+
+int csa_compress_index_score_launches(int num_jobs, const csa_compress_job* jobs, int idx_job,
+                                      int total_new, int total_q, int q_dtype, int n_heads_idx) {
+  if (num_jobs < 1 || num_jobs > csa::kMaxCompressJobs || !jobs || idx_job < 0 ||
+      idx_job >= num_jobs || total_new < 0 || total_q < 0)
+    return CSA_EINVAL;
+  int64_t work = 0;
+  for (int i = 0; i < num_jobs; ++i) work += (int64_t)jobs[i].total_entries + total_new;
+  if (single_launch(num_jobs, jobs, idx_job, work, total_q, q_dtype, n_heads_idx)) return 1;
+  return (work > 0 ? 1 : 0) + (total_q > 0 ? 1 : 0);
+}
+
 int csa_compress_index_score(csa_stream_t stream, int batch, const int32_t* ctx_lens,
                              const int32_t* cu_new, int total_new, int num_jobs,
                              const csa_compress_job* jobs, int idx_job, const int32_t* cu_q,
@@ -213,11 +235,7 @@ int csa_compress_index_score(csa_stream_t stream, int batch, const int32_t* ctx_
     return CSA_EINVAL;
   const hipStream_t s = (hipStream_t)stream;
   if (total_q == 0) return work == 0 ? CSA_OK : hip_status(csa::launch_compress(CL, s));
-  // one launch when the entry scoring stays small: every new indexer key is scored by its
-  // compressor workgroup for each query of its sequence
-  bool fuse = work > 0 && q_dtype == CSA_BF16 && n_heads_idx <= 64 &&
-              (int64_t)ij.total_entries * total_q <= 4096;
-  for (int i = 0; i < num_jobs; ++i) fuse = fuse && jobs[i].ratio == 4;
+  const bool fuse = single_launch(num_jobs, jobs, idx_job, work, total_q, q_dtype, n_heads_idx);
   csa::IndexLaunch L{batch, cu_q, q_pos, total_q, max_context, q_idx, q_dtype, n_heads_idx,
                      head_w, idx_cache, k};
   const csa::IndexWorkspace ws = csa::index_workspace_carve(workspace, total_q, max_context, k);

@@ -220,9 +220,12 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
     int64_t prow_g = 0;  // row of entry ln of tile lg: one scale load covers the four tiles
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int tile = min(16 * gi + 4 * u + wv, ntiles - 1);
-      const int eloc = min(tile * 16 + ln, nold_loc - 1);  // (this step's entries are not read)
-      const int blk = __builtin_amdgcn_readlane(my_blk, min(4 * gi + u, nblk - 1));
+      // the tile (wave-uniform) is clamped to the last one holding an old entry, so both its
+      // block and the entry (clamped to the last old one) lie before this step's entries: the
+      // rows the compressor workgroups of a fused launch write are never read
+      const int tile = min(min(16 * gi + 4 * u + wv, ntiles - 1), (nold_loc - 1) >> 4);
+      const int eloc = min(tile * 16 + ln, nold_loc - 1);
+      const int blk = __builtin_amdgcn_readlane(my_blk, tile >> 2);
       const int64_t prow = ((int64_t)blk << 6) + (eloc & 63);
       prow_g = lg == u ? prow : prow_g;
       // load i reads one 64-byte half line of each of the tile's 16 rows: lane group lg takes

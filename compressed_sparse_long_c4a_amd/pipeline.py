@@ -12,7 +12,8 @@ import torch
 import ctypes
 
 from . import (OK, CompressJob, CsaError, PagedCache, compress_insert, compress_insert_many,
-               compress_index_score, compress_jobs_array, dtype_code, index_score, index_select,
+               compress_index_score, compress_index_score_launches, compress_jobs_array, dtype_code,
+               index_score, index_select,
                index_workspace_size, lib,
                sparse_attn_decode, sparse_attn_workspace_size)
 
@@ -55,15 +56,17 @@ class Step:
         self.out = torch.empty((total_q, H, D), dtype=torch.float32, device=dev)
         self.lse = None
         self.side = None  # second stream for the overlapped schedule (created on first use)
-        # fast(): the step's compressors inside the index-score launch (csa_compress_index_score;
-        # the indexer-key job is the last of _jobs) where that call takes its single launch: bf16
-        # indexer queries, at most 64 indexer heads, ratio 4 and at most 4,096 (new entry, query)
-        # pairs (decode).  Otherwise, and always in run(), the compressors are a launch of their own.
-        new_entries = sum(L // 4 - (L - cfg.new_of(b)) // 4 for b, L in enumerate(cfg.ctx_after))
-        self.fused = ("compress_idx" in cfg.stages and "index" in cfg.stages and cfg.ratio == 4
-                      and cfg.idx_q_dtype == "bf16" and cfg.idx_heads <= 64
-                      and new_entries * total_q <= 4096)
-        self._bound = {}  # id(g) -> pre-marshalled C calls of the step (see fast())
+        # fast(): with an indexer-key compressor and an index stage, the step's compressors go
+        # through csa_compress_index_score (the indexer-key job is the last of _jobs), which runs
+        # them inside the index-score launch or as a launch of their own; the library decides and
+        # `fused` records its answer (one launch).  run() always launches the compressors first.
+        self.via_score = "compress_idx" in cfg.stages and "index" in cfg.stages
+        self.fused = False
+        if self.via_score:
+            jobs = self._jobs(g)
+            self.fused = compress_index_score_launches(jobs, len(jobs) - 1, g["new_raw"].shape[0], total_q,
+                                                       g["q_idx"].dtype, g["q_idx"].shape[1]) == 1
+        self._bound = {}  # id(g) -> (g, pre-marshalled C calls of the step, refs) (see fast())
 
     def compress(self, g=None):
         g = g or self.g
@@ -167,13 +170,13 @@ class Step:
         B = g["ctx_lens"].shape[0] if "ctx_lens" in g else g["cu_q"].shape[0] - 1
         jobs = self._jobs(g)
         total_q = g["q_pos"].shape[0]
-        fused = self.fused and bool(jobs)
+        fused = self.via_score and bool(jobs)
         if jobs and not fused:  # every compressor of the step in one launch
             arr = compress_jobs_array(jobs)
             refs.extend([jobs, arr])
             calls.append(("compress", L.csa_compress_insert_many, (
                 B, g["ctx_lens"].data_ptr(), g["cu_new"].data_ptr(), g["new_raw"].shape[0], len(jobs), arr)))
-        if "index" in c.stages and fused:  # the compressors inside the score launch
+        if "index" in c.stages and fused:  # the compressors with the score (one or two launches)
             arr = compress_jobs_array(jobs)
             refs.extend([jobs, arr])
             calls.append(("index_score", L.csa_compress_index_score, (
@@ -207,10 +210,12 @@ class Step:
         optional (before, after) torch events recorded around the index-score launch."""
         g = g or self.g
         key = id(g)
-        if key not in self._bound:
-            self._bound[key] = self._bind(g)
+        # the entry holds g itself, so the tensors whose pointers it marshalled stay alive and an
+        # id reused by another dict after g is gone can never match
+        if key not in self._bound or self._bound[key][0] is not g:
+            self._bound[key] = (g,) + self._bind(g)
         stream = torch.cuda.current_stream().cuda_stream
-        for name, fn, args in self._bound[key][0]:
+        for name, fn, args in self._bound[key][1]:
             if score_events is not None and name == "index_score":
                 score_events[0].record()
             st = fn(stream, *args)

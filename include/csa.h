@@ -360,6 +360,17 @@ int csa_compress_index_score(csa_stream_t stream, int batch, const int32_t* ctx_
                              size_t workspace_bytes);
 
 /*
+ * csa_compress_index_score_launches -- how many kernel launches csa_compress_index_score makes
+ * for these arguments (host-only, reads no device memory): 1 when the compressors run inside
+ * the score launch, 2 when the compressor launch precedes the score launch, 1 or 0 when there
+ * are no queries or nothing to compress.  total_new and the jobs' total_entries are the
+ * counts the call would receive.  Returns CSA_EINVAL for a missing job array, idx_job out of
+ * range or negative counts.
+ */
+int csa_compress_index_score_launches(int num_jobs, const csa_compress_job* jobs, int idx_job,
+                                      int total_new, int total_q, int q_dtype, int n_heads_idx);
+
+/*
  * csa_read_probe -- a measurement utility, not a step of the method: reads `bytes` bytes of the
  * device buffer `buf` once each with 16-byte loads and writes one word per workgroup to `sink`
  * (the XOR of the words it read, so no load can be dropped).  Timed on a buffer larger than

@@ -50,19 +50,3 @@ def topk(s: np.ndarray, k: int) -> np.ndarray:
     kk = min(k, n)
     out[:kk] = order[:kk]
     return out
-
-
-def index_topk(idx_cache: PagedCache, cu_q, q_pos, q_idx, head_w, k: int):
-    """Top-k ids and their scores for every query (rows of q_idx [total_q, H, d])."""
-    total_q = len(q_pos)
-    ids = np.full((total_q, k), -1, dtype=np.int64)
-    sc = np.zeros((total_q, k))
-    all_scores = []
-    for b in range(len(cu_q) - 1):
-        for i in range(int(cu_q[b]), int(cu_q[b + 1])):
-            s = query_scores(idx_cache, b, int(q_pos[i]), q_idx[i], head_w[i])
-            sel = topk(s, k)
-            ids[i] = sel
-            sc[i, sel >= 0] = s[sel[sel >= 0]]
-            all_scores.append(s)
-    return ids, sc, all_scores

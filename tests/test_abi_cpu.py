@@ -224,3 +224,29 @@ def test_compress_index_score_validation(csa):
     assert call((csa._CJob * 2)(main, ij_other), 2, 1) == csa.EINVAL
     assert call(jobs, 2, 1, ws_bytes=16) == csa.EWORKSPACE
     assert call(jobs, 0, 0) == csa.EINVAL            # no job
+
+
+def test_compress_index_score_launch_count(csa):
+    """The library's own choice between one launch (compressors inside the score launch) and
+    two (compressor, then score): host-only, nothing is launched."""
+    L = csa.lib()
+    P = ctypes.pointer
+    st = csa._CCache(1, None, csa.BF16, 576, 256, 10, 1, 8)
+    kv = csa._CCache(1, 1, csa.FP8_E4M3, 576, 64, 10, 1, 8)
+    idx = csa._CCache(4, 5, csa.FP8_E4M3, 128, 64, 10, 6, 8)
+
+    def jobs(entries, ratio=4):
+        main = csa._CJob(ratio, 1, csa.BF16, 1, entries, 1, None, 1e-6, 1e4, 64, P(st), P(kv), None)
+        ij = csa._CJob(4, 1, csa.BF16, 1, entries, 1, None, 1e-6, 1e4, 64, P(st), P(idx), None)
+        return (csa._CJob * 2)(main, ij)
+
+    n = L.csa_compress_index_score_launches
+    assert n(2, jobs(1), 1, 4, 4, csa.BF16, 64) == 1          # decode: one launch
+    assert n(2, jobs(1), 1, 4, 4, csa.F32, 64) == 2           # float32 queries
+    assert n(2, jobs(1), 1, 4, 4, csa.BF16, 65) == 2          # more than 64 indexer heads
+    assert n(2, jobs(1024), 1, 4096, 4096, csa.BF16, 64) == 2  # prefill chunk: 4M (entry, query) pairs
+    assert n(2, jobs(1, ratio=128), 1, 4, 4, csa.BF16, 64) == 2
+    assert n(2, jobs(0), 1, 0, 4, csa.BF16, 64) == 1          # nothing to compress: the score only
+    assert n(2, jobs(1), 1, 4, 0, csa.BF16, 64) == 1          # no queries: the compressor only
+    assert n(2, jobs(1), 2, 4, 4, csa.BF16, 64) == csa.EINVAL
+    assert n(2, None, 1, 4, 4, csa.BF16, 64) == csa.EINVAL
