@@ -327,8 +327,8 @@ static int sparse_attn(csa_stream_t stream, int batch, const int32_t* cu_q, cons
       csa::attn_plan(total_q, n_heads, ratio, has_topk, has_topk ? k : 0, max_context, window,
                      csa::attn_rows_cap(kv->dtype, q_dtype));
   if (p.max_rows > csa::kAttnMaxRows) return CSA_ENOTSUP;
-  if (!workspace || workspace_bytes < csa::attn_workspace_bytes(total_q, n_heads, kv->dim, p))
-    return CSA_EWORKSPACE;
+  const size_t need = csa::attn_workspace_bytes(total_q, n_heads, kv->dim, p);
+  if (!workspace || workspace_bytes < need) return CSA_EWORKSPACE;
   csa::AttnLaunch L{batch, cu_q, q_pos, total_q, max_context, q, q_dtype, n_heads, kv, ratio,
                     topk_idx, has_topk ? k : 0, swa, window, softmax_scale, rope_base, rope_dims,
                     out, lse, out_fp8, out_scales};

@@ -44,11 +44,11 @@
 #include "launch.h"
 
 namespace csa {
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kMaxSplits = 256;
 constexpr int kRowsPerSplit = kAttnRowsCapGeneric;  // most rows a workgroup handles (addresses staged in LDS)
 constexpr int kRowsPerSplitF8 = kAttnRowsCapFp8;     // the same for attn_partial_fp8
 constexpr int kRG = 2;               // row groups per workgroup (of four quarter waves each)
@@ -66,7 +66,6 @@ struct Args {
   float sm_scale2;  // softmax_scale * log2(e)
   float* part_o;    // [total_q][splits][hgp][DIM]
   float* part_ml;   // [total_q][splits][hgp][2]  (m in log2 units, l)
-  int xcd_map;      // 1-D grid with the head groups of a (split, query) on one XCD
   int units;        // splits * total_q
   // single split (splits == 1, float32 output only): the workgroup writes the finished rows
   int direct, rope_dims;
@@ -127,17 +126,11 @@ __device__ __forceinline__ void store_head_rows(const Args& a, int s, int hg, in
   }
 }
 
-// Workgroup coordinates (split, head group, query).  With the XCD map the grid is 1-D:
-// consecutive workgroup ids go to the eight XCDs in turn, so the head groups of one (split,
-// query) get ids eight apart -- they run on the same XCD at about the same time and read the
-// split's rows once from HBM and then from that XCD's L2.  Ids past the last unit exit.
+// Workgroup coordinates (split, head group, query) on the 1-D grid: consecutive workgroup ids
+// go to the eight XCDs in turn, so the head groups of one (split, query) get ids eight apart --
+// they run on the same XCD at about the same time and read the split's rows once from HBM and
+// then from that XCD's L2.  Ids past the last unit exit.
 __device__ __forceinline__ bool wg_coords(const Args& a, int& s, int& hg, int& qi) {
-  if (!a.xcd_map) {
-    s = blockIdx.x;
-    hg = blockIdx.y;
-    qi = blockIdx.z;
-    return true;
-  }
   const int id = blockIdx.x, x = id & 7, slot = id >> 3;
   const int G = a.hgp / 16;
   const int u = 8 * (slot / G) + x;
@@ -539,151 +532,170 @@ __global__ __launch_bounds__(kThreads) void attn_partial(Args a) {
   store_head_rows<DIM, kThreads>(a, s, hg, qi, mb, hml_sh, Mh, L);
 }
 
-// ---- fp8 rows with bf16 queries.  A row group's four waves take one 64-row chunk per step:
-// wave dq computes S^T for one 16-row tile over the full row width (no partial sums to
-// exchange), the per-head block maximum and then P are exchanged through LDS, and every wave
-// accumulates O^T over all 64 rows for its own quarter of the dimensions.  The waves stage the
-// fp8 codes they loaded in LDS; PV reads them back transposed with ds_read_b64_tr_b8 (a 16-lane
-// group reads an 8-row x 16-byte block and lane l receives column l of the 8 rows), which is
-// exactly the A operand of V^T with K = 32 rows: the MFMA rows of the two QK tiles of a 32-row
-// half are interleaved (tile h holds rows 8 (r / 4) + 4 h + r % 4) so that after the softmax
-// lane (head j, group g) holds P of rows 8 g .. 8 g + 7 -- the B operand -- with no movement.
-// P is applied as bf16 hi and lo parts in two MFMAs.
-constexpr int kChunk = 64;  // rows of a row group per step (four 16-row QK tiles)
+// ---- fp8 rows with bf16 queries.  The workgroup's eight waves take one 128-row step at a
+// time: wave w computes S^T for one 16-row tile of the step over the full row width, the
+// per-head step maximum and then P are exchanged through LDS, and every wave accumulates O^T
+// over the step's 128 rows for its own eighth of the dimensions (five or four 16-dim tiles of
+// 576), so the partial output leaves the workgroup from registers, with no merge inside it.
+// Rows gathered from random blocks arrive after a long latency, so each wave keeps kRing steps
+// of its rows in flight in registers, and every load of the prologue and of the ring is issued
+// unconditionally (clamped, or pointed at one cached row when there is nothing left to load):
+// with no branch around them, the wait counters wait for exactly the loads a value needs and
+// the next steps' rows stay in flight meanwhile.  The dependent trips are: (query position,
+// sequence, list entries, query heads) -> block table -> (row scales, then rows).
+// The waves stage the fp8 codes they loaded in LDS; PV reads them back transposed with
+// ds_read_b64_tr_b8 (a 16-lane group reads an 8-row x 16-byte block and lane l receives column
+// l of the 8 rows), which is exactly the A operand of V^T with K = 32 rows: the MFMA rows of
+// the two QK tiles of a 32-row block are interleaved (tile h holds rows 8 (r / 4) + 4 h + r % 4)
+// so that after the softmax lane (head j, group g) holds P of rows 8 g .. 8 g + 7 -- the B
+// operand -- once the two waves' halves are put together.  P is applied as bf16 hi and lo
+// parts in two MFMAs.
+constexpr int kF8Waves = 8;
+constexpr int kF8Threads = 64 * kF8Waves;
+constexpr int kStepF8 = 16 * kF8Waves;  // rows per step: one 16-row QK tile per wave
+constexpr int kRing = 2;                // register tiles per wave (steps in flight)
+static_assert(kRowsPerSplitF8 % kF8Threads == 0 && kRowsPerSplitF8 % kStepF8 == 0, "fp8 split size");
 template <int DIM>
-__global__ __launch_bounds__(kThreads) void attn_partial_fp8(Args a) {
-  constexpr int NKS = DIM / 32;        // k-steps of a full row
-  constexpr int MQ = (NKS + 3) / 4;    // k-steps of the largest quarter
-  constexpr int VROW = DIM + 16;       // LDS bytes per staged row
+__global__ __launch_bounds__(kF8Threads) void attn_partial_fp8(Args a) {
+  constexpr int NSEG = DIM / 64;        // 64-byte segments of a row (two k-steps each)
+  constexpr int NDT = DIM / 16;         // 16-dim output tiles
+  constexpr int DTW = (NDT + kF8Waves - 1) / kF8Waves;  // most output tiles of one wave
+  constexpr int VROW = DIM + 16;        // LDS bytes per staged row
   __shared__ int64_t off_sh[kRowsPerSplitF8];
   __shared__ float scale_sh[kRowsPerSplitF8];  // row scale; 0 marks padding
-  constexpr int V_BYTES = kRG * kChunk * VROW;
-  constexpr int MERGE_BYTES = 16 * (DIM + 4) * 4;
-  __shared__ __attribute__((aligned(16))) char v_sh[V_BYTES > MERGE_BYTES ? V_BYTES : MERGE_BYTES];
-  __shared__ uint4 p_sh[kRG][4][64];         // P of each QK tile, lane-major {4 hi, 4 lo} bf16
-  __shared__ float mx_sh[kRG][4][16];        // per-head maximum logit of each QK tile
-  __shared__ float ml_sh[kRG][4][16][2];     // (m, l) of every wave, for the final merge
-  __shared__ float hml_sh[16][2];            // per head (M, L) of the workgroup
+  __shared__ __attribute__((aligned(16))) char v_sh[kStepF8 * VROW];
+  __shared__ uint4 p_sh[kF8Waves][64];         // P of each QK tile, lane-major {4 hi, 4 lo} bf16
+  __shared__ float mx_sh[kF8Waves][16];        // per-head maximum logit of each QK tile
+  __shared__ float l_sh[kF8Waves][16];         // per-head sum of P of each wave's rows
 
-  const int s = blockIdx.x, hg = blockIdx.y, qi = blockIdx.z;
+  int s, hg, qi;
+  if (!wg_coords(a, s, hg, qi)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, lg = lane >> 4;
-  // wave (dq, rg): waves 2 dq + rg, so a SIMD holds waves of a long and a short quarter
-  const int dq = wv >> 1, rg = wv & 1;
-  const int nkq = NKS / 4 + (dq < NKS % 4 ? 1 : 0);   // k-steps of quarter dq
-  const int k0 = dq * (NKS / 4) + min(dq, NKS % 4);    // its first k-step
+  const int ndt = NDT / kF8Waves + (wv < NDT % kF8Waves ? 1 : 0);  // this wave's output tiles
+  const int dt0 = wv * (NDT / kF8Waves) + min(wv, NDT % kF8Waves);  // its first
   const int H = a.n_heads;
   const char* kvbase = (const char*)a.kv.rows;
   const int r_begin = s * a.rows_per_split;
 
-  // ---- loads that need nothing else: query position, sequence, list entries, Q^T
-  const int t = a.q_pos[qi];
-  const int b = seq_of_wave(a.cu_q, a.batch, qi);
-  constexpr int RPT = kRowsPerSplitF8 / kThreads;
+  // ---- trip 1 (all unconditional): list entries, query heads, sequence start, position
+  constexpr int RPT = kRowsPerSplitF8 / kF8Threads;
   int ent[RPT];
 #pragma unroll
   for (int u = 0; u < RPT; ++u) {
-    const int pos = r_begin + min(tid + kThreads * u, a.rows_per_split - 1);
+    const int pos = r_begin + min(tid + kF8Threads * u, a.rows_per_split - 1);
     ent[u] = a.has_topk ? a.topk[(int64_t)qi * a.k + min(pos, a.k - 1)] : pos;
   }
-  // the workgroup's 16 query heads are read once, 16 bytes per thread and pass, and staged in
-  // LDS (in the row buffer, which the first step fills only after every wave's first QK)
   constexpr int QS = DIM + 8;                  // bf16 per staged query row (padded)
-  constexpr int QV = 16 * DIM / 8;             // 16-byte pieces of the tile
-  constexpr int QP = (QV + kThreads - 1) / kThreads;
+  constexpr int QV = 16 * DIM / 8;             // 16-byte pieces of the 16 heads
+  constexpr int QP = (QV + kF8Threads - 1) / kF8Threads;
   static_assert(16 * QS * 2 <= (int)sizeof(v_sh), "query tile fits the row buffer");
   uint4 qv[QP];
 #pragma unroll
   for (int p = 0; p < QP; ++p) {
-    const int i = p * kThreads + tid;
+    const int i = min(p * kF8Threads + tid, QV - 1);
     const int h = i / (DIM / 8), c = i - h * (DIM / 8);
-    qv[p] = i < QV && 16 * hg + h < H ? *(const uint4*)((const uint16_t*)a.q + ((int64_t)qi * H + 16 * hg + h) * DIM + 8 * c)
-                                     : make_uint4(0, 0, 0, 0);
+    qv[p] = *(const uint4*)((const uint16_t*)a.q + ((int64_t)qi * H + min(16 * hg + h, H - 1)) * DIM + 8 * c);
   }
+  const int cu_v = seq_load(a.cu_q, a.batch);
+  const int t = a.q_pos[qi];
+  const int b = seq_pick(a.cu_q, a.batch, qi, cu_v);
 
   const int n_vis = min((t + 1) / a.ratio, a.n_max);
   const int n_c = a.has_topk ? a.k : n_vis;
   const int n_w = min(a.window, t + 1);
   const int n_rows = n_c + n_w;
   const int nrows = (n_w > 0 || n_vis > 0) ? max(0, min(a.rows_per_split, n_rows - r_begin)) : 0;
-  // padded to whole steps; rows_per_split is a multiple of kRG * kChunk
-  const int nrows_p = (nrows + kRG * kChunk - 1) / (kRG * kChunk) * (kRG * kChunk);
+  // padded to whole steps; rows_per_split is a multiple of kStepF8
+  const int nrows_p = (nrows + kStepF8 - 1) / kStepF8 * kStepF8;
+  const int steps = nrows_p / kStepF8;
 
-  // ---- resolve the split's rows once: offset and scale; padding rows -> a safe row with
-  // scale 0
-  if (nrows > 0) {
-    const int64_t swa_off = (int64_t)((uintptr_t)a.swa.rows - (uintptr_t)a.kv.rows);
-    const int64_t safe = n_w > 0 ? swa_off + phys_row(a.swa, b, t) * DIM
-                                 : phys_row(a.kv, b, max(n_vis - 1, 0)) * DIM;
-    int64_t prow[RPT];
-    bool is_kv[RPT], ok[RPT];
+  // ---- trip 2: the block table gives each staged row's address (the kv or the window cache,
+  // picked by pointer, one load either way)
+  const int64_t swa_off = (int64_t)((uintptr_t)a.swa.rows - (uintptr_t)a.kv.rows);
+  int64_t roff[RPT], prow[RPT];  // row: byte offset from the main cache's row base, index
+  bool use[RPT], is_kv[RPT];
 #pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-      const int i = tid + kThreads * u;
-      const int pos = r_begin + min(i, nrows - 1);
-      is_kv[u] = pos < n_c;
-      ok[u] = i < nrows && (!is_kv[u] || (ent[u] >= 0 && ent[u] < n_vis));
-      prow[u] = is_kv[u] ? (ok[u] ? phys_row(a.kv, b, ent[u]) : 0)
-                         : phys_row(a.swa, b, t - n_w + 1 + (pos - n_c));
-    }
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-      const int i = tid + kThreads * u;
-      if (i < nrows_p) {
-        const int64_t base = is_kv[u] ? 0 : swa_off;
-        const float sc = ok[u] ? (is_kv[u] ? a.kv.scales : a.swa.scales)[prow[u]] : 0.f;
-        off_sh[i] = ok[u] ? base + prow[u] * DIM : safe;
-        scale_sh[i] = sc;
-      }
-    }
+  for (int u = 0; u < RPT; ++u) {
+    const int i = tid + kF8Threads * u;
+    const int pos = r_begin + min(i, max(nrows - 1, 0));
+    is_kv[u] = pos < n_c;
+    use[u] = i < nrows && (!is_kv[u] || (ent[u] >= 0 && ent[u] < n_vis));
+    // logical row in its cache: an entry id, or a window position; clamped into the table
+    const int64_t lrow = is_kv[u] ? (int64_t)min(max(ent[u], 0), max(n_vis - 1, 0))
+                                  : (int64_t)max(t - n_w + 1 + (pos - n_c), 0);
+    // (each field picked on its own: a selected struct would be read per lane from memory)
+    const int32_t* bt = is_kv[u] ? a.kv.bt : a.swa.bt;
+    const int stride = is_kv[u] ? a.kv.bt_stride : a.swa.bt_stride;
+    const int shift = is_kv[u] ? a.kv.rpb_shift : a.swa.rpb_shift;
+    const int32_t blk = bt[(int64_t)b * stride + (int32_t)(lrow >> shift)];
+    prow[u] = ((int64_t)blk << shift) + (lrow & ((1 << shift) - 1));
+    roff[u] = (is_kv[u] ? 0 : swa_off) + prow[u] * DIM;
   }
-
-  {
-    uint16_t* q_sh = (uint16_t*)v_sh;
 #pragma unroll
-    for (int p = 0; p < QP; ++p) {
-      const int i = p * kThreads + tid;
-      const int h = i / (DIM / 8), c = i - h * (DIM / 8);
-      if (i < QV) *(uint4*)&q_sh[h * QS + 8 * c] = qv[p];
-    }
+  for (int p = 0; p < QP; ++p) {  // the query tile into LDS (its loads are done by now)
+    const int i = p * kF8Threads + tid;
+    const int h = i / (DIM / 8), c = i - h * (DIM / 8);
+    const uint4 v = 16 * hg + h < H ? qv[p] : make_uint4(0, 0, 0, 0);
+    if (i < QV) *(uint4*)&((uint16_t*)v_sh)[h * QS + 8 * c] = v;  // (a compile-time bound)
   }
-  f32x4 o[2 * MQ];  // O^T of quarter dq (dim tile 16 d .. +15 x 16 heads), over the group's rows
+  // ---- trip 3a: the row scales (issued before the rows, so waiting for them never waits
+  // for a row); padding and rejected entries read the first scale and get 0
+  float sc[RPT];
 #pragma unroll
-  for (int dt = 0; dt < 2 * MQ; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_run = 0.f;  // per head: reference exponent (log2 units), this
-                                         // wave's share of the sum of P
-  __syncthreads();
+  for (int u = 0; u < RPT; ++u) {
+    const float* sp = is_kv[u] ? a.kv.scales : a.swa.scales;
+    sc[u] = sp[use[u] ? prow[u] : 0];
+  }
+  // the first used row of the split stands in for padding rows (finite data, scale 0)
+  const int64_t safe_off = __shfl(roff[0], 0);  // (thread 0 holds the split's first row)
+  // (slots past the split's rows are written too, and never read: no branch, no wait)
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) off_sh[tid + kF8Threads * u] = use[u] ? roff[u] : safe_off;
+  barrier_lds();  // offsets and the query tile (the scale loads stay in flight)
   // QK runs over the dimensions in the order the rows are loaded: lane group lg of 64-byte
   // segment m holds dims 64 m + 16 lg .. +15 (one 16-byte load), k-step 2 m + e takes the half
   // e of them.  Q^T, the B operand, follows the same order: lane (head ln, group lg) holds
   // q[h][64 m + 16 lg + 8 e + 0..7] for k-step 2 m + e.
-  bf16x8 qb[NKS];
+  bf16x8 qb[2 * NSEG];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
+  for (int ks = 0; ks < 2 * NSEG; ++ks) {
     const int d0 = 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1);
     qb[ks] = __builtin_bit_cast(bf16x8, *(const uint4*)((const uint16_t*)v_sh + ln * QS + d0));
   }
-
-  const int steps = nrows_p / (kRG * kChunk);
-  const int kb = dq >> 1, hh = dq & 1;  // this wave's QK tile: half kb, interleave hh
-  const int my_row = 32 * kb + 8 * (ln >> 2) + 4 * hh + (ln & 3);  // chunk row of QK row ln
-  const int srow0 = 32 * kb + 8 * lg + 4 * hh;                       // chunk rows of P lanes
-  char* vrow_w = v_sh + (rg * kChunk + my_row) * VROW + 16 * lg;
-  constexpr int NSEG = DIM / 64;  // 64-byte segments of a row
+  // this wave's QK tile: 32-row block kb of the step, interleave hh
+  const int kb = wv >> 1, hh = wv & 1;
+  const int my_row = 32 * kb + 8 * (ln >> 2) + 4 * hh + (ln & 3);  // step row of QK row ln
+  const int srow0 = 32 * kb + 8 * lg + 4 * hh;                      // step rows of P lanes
+  char* vrow_w = v_sh + my_row * VROW + 16 * lg;
   struct Tile { uint4 d[NSEG]; };
-  // Row loads are unconditional (clamped to the last step; with no step at all, row 0 of the
-  // cache).
-  auto load_block = [&](int i, Tile& tl) {
-    const int c = rg + kRG * max(0, min(i, steps - 1));
-    const int64_t off = steps > 0 ? off_sh[kChunk * c + my_row] : 0;
-    const char* row = kvbase + off + 16 * lg;
+  // Loads of step i's rows; a step past the last (or none at all) reads the first row of the
+  // main cache instead, the same bytes for every wave, so the load is there for the wait
+  // counters but costs no memory traffic.
+  auto load_step = [&](int i, Tile& tl) {
+    const int64_t o = off_sh[kStepF8 * max(min(i, steps - 1), 0) + my_row];
+    const char* row = kvbase + (i < steps ? o : 0) + 16 * lg;
 #pragma unroll
-    for (int m = 0; m < NSEG; ++m) tl.d[m] = *(const uint4*)(row + 64 * m);
+    for (int m = 0; m < NSEG; ++m) tl.d[m] = load_global16(row + 64 * m);
   };
+  // ---- trip 3b: the rows of the first kRing steps
+  Tile ring[kRing];
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) load_step(r, ring[r]);
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) scale_sh[tid + kF8Threads * u] = use[u] ? sc[u] : 0.f;
+  barrier_lds();  // the scales; every wave has read its Q^T (the row buffer is free)
 
-  auto step = [&](int i, Tile& tl) {
-    const int r0 = kChunk * (rg + kRG * i);
+  f32x4 o[DTW];  // O^T of this wave's dims (tile 16 (dt0 + dt) .. +15 x 16 heads)
+#pragma unroll
+  for (int dt = 0; dt < DTW; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_run = 0.f;  // per head: reference exponent (log2 units), this
+                                         // wave's share of the sum of P
+
+  // One step over the tile in `tl`, which is refilled with step `next` (or the stand-in row).
+  auto step = [&](int i, Tile& tl, int next) {
+    const int r0 = kStepF8 * i;
     // S^T of this wave's 16 rows over the full width, two accumulation chains
     f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -702,16 +714,17 @@ __global__ __launch_bounds__(kThreads) void attn_partial_fp8(Args a) {
       mloc = fmaxf(mloc, z[j]);
     }
     mloc = rows_reduce(mloc, [](float x, float y) { return fmaxf(x, y); });
-    if (lg == 0) mx_sh[rg][dq][ln] = mloc;
-    barrier_lds();  // #1: the four tiles' maxima; every wave is past the previous step's PV
-    // stage this wave's rows (fp8 codes) for PV; the tile is then free for the next chunk,
-    // whose loads overlap this step's softmax and PV
+    if (lg == 0) mx_sh[wv][ln] = mloc;
+    barrier_lds();  // #1: the tiles' maxima; every wave is past the previous step's PV
+    // stage this wave's rows (fp8 codes) for PV; the registers then take a later step's rows
 #pragma unroll
     for (int m = 0; m < NSEG; ++m) *(uint4*)(vrow_w + 64 * m) = tl.d[m];
-    load_block(i + 1, tl);
-    const float mblk = fmaxf(fmaxf(mx_sh[rg][0][ln], mx_sh[rg][1][ln]), fmaxf(mx_sh[rg][2][ln], mx_sh[rg][3][ln]));
-    // the row group's reference moves only when a block's maximum exceeds it by more than
-    // kSlack (always when it has none yet); the four waves take the same decision
+    load_step(next, tl);
+    float mblk = mx_sh[0][ln];
+#pragma unroll
+    for (int w = 1; w < kF8Waves; ++w) mblk = fmaxf(mblk, mx_sh[w][ln]);
+    // the reference moves only when a step's maximum exceeds it by more than kSlack (always
+    // when it has none yet); every wave takes the same decision
     const bool move = mblk > m_ref + kSlack;
     if (__ballot(move)) {
       const float m_new = move ? mblk : m_ref;
@@ -719,9 +732,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_fp8(Args a) {
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 2 * MQ; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < DTW; ++dt) o[dt] *= alpha;
     }
-    uint4 pw;
     {
       float pvv[4], psum = 0.f;
 #pragma unroll
@@ -738,82 +750,85 @@ __global__ __launch_bounds__(kThreads) void attn_partial_fp8(Args a) {
         hl[j] = hi;
         hl[4 + j] = (__bf16)(pvv[j] - (float)hi);
       }
-      pw = __builtin_bit_cast(uint4, hl);
+      p_sh[wv][lane] = __builtin_bit_cast(uint4, hl);
     }
-    p_sh[rg][dq][lane] = pw;
-    barrier_lds();  // #2: P of the four tiles and the staged rows
-    // O^T += V^T . P^T over the chunk, one 32-row half at a time (P_hi and P_lo MFMAs)
+    barrier_lds();  // #2: P of the tiles and the staged rows
+    // O^T += V^T . P^T over the step, one 32-row block at a time (P_hi and P_lo MFMAs)
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, p_sh[rg][2 * kh][lane]);
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, p_sh[rg][2 * kh + 1][lane]);
+    for (int kh = 0; kh < kF8Waves / 2; ++kh) {
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, p_sh[2 * kh][lane]);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, p_sh[2 * kh + 1][lane]);
       const bf16x8 phi = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
       const bf16x8 plo = {pa[4], pa[5], pa[6], pa[7], pb[4], pb[5], pb[6], pb[7]};
-      const char* vt = v_sh + (rg * kChunk + 32 * kh + 8 * lg + (ln >> 1)) * VROW + 32 * k0 + 8 * (ln & 1);
+      const char* vt = v_sh + (32 * kh + 8 * lg + (ln >> 1)) * VROW + 16 * dt0 + 8 * (ln & 1);
 #pragma unroll
-      for (int dt = 0; dt < 2 * MQ; ++dt) {
-        // (a short quarter's two extra tiles re-read its last tile: O^T tiles never written out)
-        const int dtc = dt < 2 * nkq ? dt : 2 * nkq - 1;
-        typedef int v2i __attribute__((ext_vector_type(2)));
-        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i*)(vt + 16 * dtc));
-        const bf16x8 va = fp8x8_to_bf16x8((uint32_t)raw[0], (uint32_t)raw[1]);
-        o[dt] = mfma16x16x32(va, phi, o[dt]);
-        o[dt] = mfma16x16x32(va, plo, o[dt]);
+      for (int dt = 0; dt < DTW; ++dt) {
+        if (dt < ndt) {  // (wave-uniform)
+          typedef int v2i __attribute__((ext_vector_type(2)));
+          const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) v2i*)(vt + 16 * dt));
+          const bf16x8 va = fp8x8_to_bf16x8((uint32_t)raw[0], (uint32_t)raw[1]);
+          o[dt] = mfma16x16x32(va, phi, o[dt]);
+          o[dt] = mfma16x16x32(va, plo, o[dt]);
+        }
       }
     }
   };
 
   {
-    Tile t0;
-    load_block(0, t0);
-    for (int i = 0; i < steps; ++i) step(i, t0);
+    int i = 0;
+    for (; i + kRing <= steps; i += kRing) {
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) step(i + r, ring[r], i + r + kRing);
+    }
+#pragma unroll
+    for (int r = 0; r < kRing - 1; ++r)
+      if (i + r < steps) step(i + r, ring[r], steps);  // (uniform across the workgroup)
   }
 
-  // ---- merge: per head, the row group's l is the sum over its four waves; then the two row
-  // groups are combined with weights 2^(m_g - M)
-  const float l_tot = rows_reduce(l_run, [](float x, float y) { return x + y; });
-  if (lg == 0) {
-    ml_sh[rg][dq][ln][0] = m_ref;
-    ml_sh[rg][dq][ln][1] = l_tot;
-  }
-  __syncthreads();  // also: every wave is done with the staged rows (the merge buffer aliases)
-  float M = -INFINITY;
+  // ---- per head: the sum of P over the waves' rows (m_ref is the same in every wave)
+  const float l_w = rows_reduce(l_run, [](float x, float y) { return x + y; });
+  if (lg == 0) l_sh[wv][ln] = l_w;
+  __syncthreads();
+  float L = 0.f;
 #pragma unroll
-  for (int g = 0; g < kRG; ++g) M = fmaxf(M, ml_sh[g][0][ln][0]);
-  const float f = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - M);
-  float (*mb)[DIM + 4] = reinterpret_cast<float (*)[DIM + 4]>(v_sh);
-  float* dst = &mb[ln][32 * k0 + 4 * lg];
+  for (int w = 0; w < kF8Waves; ++w) L += l_sh[w][ln];
+  const int hq = 16 * hg + ln;  // lane (head ln, group lg): dims 16 (dt0 + dt) + 4 lg .. +3
+  if (a.direct) {  // one split: the finished rows, as attn_merge would write them
+    if (hq < H) {
+      const float inv = L > 0.f ? 1.0f / L : 0.f;
+      const int rope0 = DIM - a.rope_dims;
+      float* dst = a.out + ((int64_t)qi * H + hq) * DIM;
 #pragma unroll
-  for (int round = 0; round < kRG; ++round) {
-    if (rg == round) {
-#pragma unroll
-      for (int dt = 0; dt < 2 * MQ; ++dt) {
-        if (dt < 2 * nkq) {
-          float4 v = make_float4(f * o[dt][0], f * o[dt][1], f * o[dt][2], f * o[dt][3]);
-          if (round > 0) {
-            const float4 w = *(const float4*)(dst + 16 * dt);
-            v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
-          }
-          *(float4*)(dst + 16 * dt) = v;
+      for (int dt = 0; dt < DTW; ++dt) {
+        if (dt >= ndt) continue;
+        const int d = 16 * (dt0 + dt) + 4 * lg;
+        float4 r = make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+        if (d >= rope0) {  // pairs (d, d+1) and (d+2, d+3) by -t theta_i
+          float c0, s0, c1, s1;
+          rope_cos_sin(-(double)t, a.rope.theta[(d - rope0) / 2], c0, s0);
+          rope_cos_sin(-(double)t, a.rope.theta[(d - rope0) / 2 + 1], c1, s1);
+          r = make_float4(r.x * c0 - r.y * s0, r.x * s0 + r.y * c0, r.z * c1 - r.w * s1, r.z * s1 + r.w * c1);
         }
+        *(float4*)(dst + d) = r;
       }
+      if (a.lse && wv == 0 && lg == 0)
+        a.lse[(int64_t)qi * H + hq] = L > 0.f ? (m_ref + log2f(L)) * kLn2 : -INFINITY;
     }
-    __syncthreads();
+    return;
   }
-  float Mh = -INFINITY, L = 0.f;
-  if (tid < 16) {
-    const int h = tid;
+  const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg + ln;
+  float* dst = a.part_o + pbase * DIM;
 #pragma unroll
-    for (int g = 0; g < kRG; ++g) Mh = fmaxf(Mh, ml_sh[g][0][h][0]);
-#pragma unroll
-    for (int g = 0; g < kRG; ++g) {
-      const float mg = ml_sh[g][0][h][0];
-      if (mg != -INFINITY)
-        L += exp2f(mg - Mh) * (ml_sh[g][0][h][1] + ml_sh[g][1][h][1] + ml_sh[g][2][h][1] + ml_sh[g][3][h][1]);
-    }
+  for (int dt = 0; dt < DTW; ++dt) {
+    if (dt >= ndt) continue;
+    const int d = 16 * (dt0 + dt) + 4 * lg;
+    *(float4*)(dst + d) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
   }
-  store_head_rows<DIM, kThreads>(a, s, hg, qi, mb, hml_sh, Mh, L);
+  if (wv == 0 && lg == 0) {
+    a.part_ml[pbase * 2 + 0] = m_ref;
+    a.part_ml[pbase * 2 + 1] = L;
+  }
 }
 
 struct MergeArgs {
@@ -957,8 +972,8 @@ void launch_q(const Args& args, int qdt, int dim, dim3 grid, hipStream_t stream)
 template <>
 void launch_q<CSA_FP8_E4M3>(const Args& args, int qdt, int dim, dim3 grid, hipStream_t stream) {
   if (qdt == CSA_BF16) {
-    if (dim == 576) hipLaunchKernelGGL((attn_partial_fp8<576>), grid, dim3(kThreads), 0, stream, args);
-    else hipLaunchKernelGGL((attn_partial_fp8<512>), grid, dim3(kThreads), 0, stream, args);
+    if (dim == 576) hipLaunchKernelGGL((attn_partial_fp8<576>), grid, dim3(kF8Threads), 0, stream, args);
+    else hipLaunchKernelGGL((attn_partial_fp8<512>), grid, dim3(kF8Threads), 0, stream, args);
   } else {
     // (fp8 rows with f32 queries: the generic kernel on the XCD-grouped grid)
     const dim3 g1((unsigned)(8 * (int64_t)(args.hgp / 16) * ((args.units + 7) / 8)));
@@ -977,10 +992,11 @@ AttnPlan attn_plan(int total_q, int n_heads, int ratio, int has_topk, int k, int
   const int64_t blocks32 = std::max<int64_t>(1, (p.max_rows + 31) / 32);
   const int64_t units = (int64_t)total_q * p.head_groups;
   // aim at one workgroup per compute unit (256 CUs); a split is a whole number of 128-row
-  // steps (the fp8 kernel's step: two row groups of 64 rows)
-  int64_t bpw = std::max<int64_t>(4, (blocks32 * units + 255) / 256);
-  bpw = std::min<int64_t>((std::min(bpw, blocks32) + 3) / 4 * 4, rows_cap / 32);
-  // callers keep max_rows <= kMaxSplits * kAttnRowsCapFp8 (kAttnMaxRows), so splits <= kMaxSplits
+  // steps (the fp8-row kernel's step; the generic kernel's is 32 rows)
+  const int64_t sb = 4;  // 32-row blocks per step
+  int64_t bpw = std::max<int64_t>(sb, (blocks32 * units + 255) / 256);
+  bpw = std::min<int64_t>((std::min(bpw, blocks32) + sb - 1) / sb * sb, rows_cap / 32);
+  // (max_rows <= kAttnMaxRows keeps splits <= 512 and the partial workspace finite)
   const int64_t splits = (blocks32 + bpw - 1) / bpw;
   p.splits = (int)splits;
   p.rows_per_split = (int)(bpw * 32);
@@ -1024,14 +1040,11 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, const AttnPlan& p, void* work
   a.out = L.out;
   a.lse = L.lse;
   a.rope = make_rope_table(L.rope_base, L.rope_dims);
-  const dim3 grid(p.splits, p.head_groups, L.total_q);
   a.units = p.splits * L.total_q;
-  // the generic kernel (bf16 / f32 rows, or f32 queries) takes the XCD-grouped 1-D grid; the
-  // fp8-row kernel with bf16 queries keeps the 3-D grid
-  a.xcd_map = !(L.kv->dtype == CSA_FP8_E4M3 && L.q_dtype == CSA_BF16);
+  // 1-D grid with the head groups of one split on one XCD (wg_coords)
   const dim3 grid_xcd((unsigned)(8 * (int64_t)p.head_groups * ((a.units + 7) / 8)));
   switch (L.kv->dtype) {
-    case CSA_FP8_E4M3: launch_q<CSA_FP8_E4M3>(a, L.q_dtype, dim, grid, stream); break;
+    case CSA_FP8_E4M3: launch_q<CSA_FP8_E4M3>(a, L.q_dtype, dim, grid_xcd, stream); break;
     case CSA_BF16: launch_q<CSA_BF16>(a, L.q_dtype, dim, grid_xcd, stream); break;
     default: launch_q<CSA_F32>(a, L.q_dtype, dim, grid_xcd, stream); break;
   }

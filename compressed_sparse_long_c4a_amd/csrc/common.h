@@ -81,13 +81,20 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int batch, int i) {
 }
 
 // Same as seq_of with one round trip for batch <= 64: every lane of the calling wave loads
-// one prefix sum and a ballot finds the last sequence starting at or before i.
-__device__ __forceinline__ int seq_of_wave(const int32_t* cu, int batch, int i) {
+// one prefix sum (unconditionally, so the load needs no branch and never waits alone) and a
+// ballot finds the last sequence starting at or before i.  Split in two so that a kernel can
+// issue the load with its other first loads: seq_load, then seq_pick on its value.
+__device__ __forceinline__ int seq_load(const int32_t* cu, int batch) {
+  return cu[min((int)(threadIdx.x & 63), batch - 1)];
+}
+__device__ __forceinline__ int seq_pick(const int32_t* cu, int batch, int i, int loaded) {
   if (batch > 64) return seq_of(cu, batch, i);
   const int lane = threadIdx.x & 63;
-  const bool le = lane < batch && cu[lane] <= i;
-  const unsigned long long m = __ballot(le);
+  const unsigned long long m = __ballot(lane < batch && loaded <= i);
   return m ? 63 - __clzll(m) : 0;
+}
+__device__ __forceinline__ int seq_of_wave(const int32_t* cu, int batch, int i) {
+  return seq_pick(cu, batch, i, seq_load(cu, batch));
 }
 
 // ---------------------------------------------------------------- formats
@@ -303,6 +310,15 @@ __device__ __forceinline__ void rope_cos_sin(double position, double theta, floa
   const double x = position * theta;
   const double r = x - two_pi * rint(x * (1.0 / two_pi));
   sincosf((float)r, &s, &c);
+}
+
+// A load through a global-memory address (device memory): emitted as a global load, never a
+// flat one.  Flat loads also count against the LDS wait counter, so an LDS-only wait (as in
+// barrier_lds) would wait for them too.
+__device__ __forceinline__ uint4 load_global16(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)p;
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {

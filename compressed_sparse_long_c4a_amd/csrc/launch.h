@@ -135,4 +135,5 @@ struct AttnLaunch {
 hipError_t launch_sparse_attn(const AttnLaunch& a, const AttnPlan& p, void* workspace,
                               hipStream_t stream);
 
+
 }  // namespace csa

@@ -250,3 +250,4 @@ def test_compress_index_score_launch_count(csa):
     assert n(2, jobs(1), 1, 4, 0, csa.BF16, 64) == 1          # no queries: the compressor only
     assert n(2, jobs(1), 2, 4, 4, csa.BF16, 64) == csa.EINVAL
     assert n(2, None, 1, 4, 4, csa.BF16, 64) == csa.EINVAL
+
