@@ -85,6 +85,8 @@ _SIGNATURES = {
     "csa_sparse_attn_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "csa_sparse_attn_decode": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _CP, _I, _P, _I, _CP, _I,
                                     _F, _F, _I, _P, _P, _P, _SZ]),
+    "csa_sparse_attn_decode_noalloc": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _CP, _I, _P, _I, _CP,
+                                            _I, _F, _F, _I, _P, _P]),
     "csa_sparse_attn_decode_fp8": (_I, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _CP, _I, _P, _I, _CP,
                                         _I, _F, _F, _I, _P, _P, _P, _P, _P, _SZ]),
     "csa_compress_index_score": (_I, [_P, _I, _P, _P, _I, _I, ctypes.POINTER(_CJob), _I, _P, _P, _I,

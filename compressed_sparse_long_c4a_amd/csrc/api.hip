@@ -300,13 +300,14 @@ int csa_q_norm_rope_swa(csa_stream_t stream, int total_q, const int32_t* q_pos, 
   return hip_status(csa::launch_q_norm_rope_swa(L, (hipStream_t)stream));
 }
 
-// Shared by the float32 and the fp8 output entry points.
+// Shared by the float32, fp8 output and no-allocation entry points (static_scratch: the
+// library's own device array instead of the caller's workspace).
 static int sparse_attn(csa_stream_t stream, int batch, const int32_t* cu_q, const int32_t* q_pos,
                        int total_q, int max_context, const void* q, int q_dtype, int n_heads,
                        const csa_cache* kv, int ratio, const int32_t* topk_idx, int k,
                        const csa_cache* swa, int window, float softmax_scale, float rope_base,
                        int rope_dims, float* out, float* lse, uint8_t* out_fp8, float* out_scales,
-                       void* workspace, size_t workspace_bytes) {
+                       void* workspace, size_t workspace_bytes, bool static_scratch = false) {
   if (ratio != 4 && ratio != 128) return CSA_EINVAL;
   if (batch <= 0 || total_q < 0 || !cu_q) return CSA_EINVAL;
   if (total_q > 0 && (!q_pos || !q)) return CSA_EINVAL;  // zero-length arrays may be NULL
@@ -328,6 +329,13 @@ static int sparse_attn(csa_stream_t stream, int batch, const int32_t* cu_q, cons
                      csa::attn_rows_cap(kv->dtype, q_dtype));
   if (p.max_rows > csa::kAttnMaxRows) return CSA_ENOTSUP;
   const size_t need = csa::attn_workspace_bytes(total_q, n_heads, kv->dim, p);
+  if (static_scratch) {  // the no-allocation entry point
+    if (need > csa::kAttnStaticScratchBytes) return CSA_EWORKSPACE;
+    hipError_t e = hipSuccess;
+    workspace = csa::attn_static_scratch(&e);
+    if (!workspace) return CSA_EHIP;
+    workspace_bytes = csa::kAttnStaticScratchBytes;
+  }
   if (!workspace || workspace_bytes < need) return CSA_EWORKSPACE;
   csa::AttnLaunch L{batch, cu_q, q_pos, total_q, max_context, q, q_dtype, n_heads, kv, ratio,
                     topk_idx, has_topk ? k : 0, swa, window, softmax_scale, rope_base, rope_dims,
@@ -345,6 +353,18 @@ int csa_sparse_attn_decode(csa_stream_t stream, int batch, const int32_t* cu_q,
   return sparse_attn(stream, batch, cu_q, q_pos, total_q, max_context, q, q_dtype, n_heads, kv,
                      ratio, topk_idx, k, swa, window, softmax_scale, rope_base, rope_dims, out,
                      lse, nullptr, nullptr, workspace, workspace_bytes);
+}
+
+int csa_sparse_attn_decode_noalloc(csa_stream_t stream, int batch, const int32_t* cu_q,
+                                   const int32_t* q_pos, int total_q, int max_context,
+                                   const void* q, int q_dtype, int n_heads,
+                                   const csa_cache* kv, int ratio, const int32_t* topk_idx, int k,
+                                   const csa_cache* swa, int window, float softmax_scale,
+                                   float rope_base, int rope_dims, float* out, float* lse) {
+  if (total_q > 0 && !out) return CSA_EINVAL;
+  return sparse_attn(stream, batch, cu_q, q_pos, total_q, max_context, q, q_dtype, n_heads, kv,
+                     ratio, topk_idx, k, swa, window, softmax_scale, rope_base, rope_dims, out,
+                     lse, nullptr, nullptr, nullptr, 0, true);
 }
 
 int csa_sparse_attn_decode_fp8(csa_stream_t stream, int batch, const int32_t* cu_q,

@@ -38,12 +38,39 @@
 //   (angles formed and reduced in float64) and writes out / lse.  When every query's rows fit
 //   one split (prefill chunks: many queries, few rows each) and only float32 output is wanted,
 //   kernel 1 finishes the rows itself with the same operations and kernel 2 is not launched.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
 #include "launch.h"
 
 namespace csa {
+
+// Scratch of csa_sparse_attn_decode_noalloc: the split partials live in this array instead of a
+// caller workspace.  Each device holds its own copy for the life of the process; host code uses
+// only the device address resolved by attn_static_scratch, never the array's name.
+static __device__ __align__(256) unsigned char scratch[kAttnStaticScratchBytes];
+
+void* attn_static_scratch(hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // (with device `dev` current)
+    if (*err != hipSuccess) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
 
 namespace {
 

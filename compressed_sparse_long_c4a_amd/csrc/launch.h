@@ -135,5 +135,10 @@ struct AttnLaunch {
 hipError_t launch_sparse_attn(const AttnLaunch& a, const AttnPlan& p, void* workspace,
                               hipStream_t stream);
 
+// csa_sparse_attn_decode_noalloc: the largest workspace it serves from the library's own
+// device array, and that array's address on the current device (resolved once per device;
+// NULL with *err set if the lookup fails).
+constexpr size_t kAttnStaticScratchBytes = (size_t)16 << 20;
+void* attn_static_scratch(hipError_t* err);
 
 }  // namespace csa

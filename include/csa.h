@@ -311,6 +311,25 @@ int csa_sparse_attn_decode(csa_stream_t stream, int batch, const int32_t* cu_q,
                            void* workspace, size_t workspace_bytes);
 
 /*
+ * csa_sparse_attn_decode_noalloc -- csa_sparse_attn_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same kernels and results.  Its
+ * scratch (the split partials) is a device array inside the library, one per GPU, held until
+ * the process ends; the call allocates and frees nothing.  Limit: the workspace the call would
+ * need (csa_sparse_attn_workspace_size for its arguments) must not exceed 16 MiB
+ * (16,777,216 bytes), else CSA_EWORKSPACE and nothing is launched.  Every call on a GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different host threads) race and give wrong results; calls in
+ * one stream are ordered and safe.  No part of the array needs to start at zero.  Returns
+ * CSA_EHIP if the array's device address cannot be resolved on the current device.
+ */
+int csa_sparse_attn_decode_noalloc(csa_stream_t stream, int batch, const int32_t* cu_q,
+                                   const int32_t* q_pos, int total_q, int max_context,
+                                   const void* q, int q_dtype, int n_heads,
+                                   const csa_cache* kv, int ratio, const int32_t* topk_idx, int k,
+                                   const csa_cache* swa, int window, float softmax_scale,
+                                   float rope_base, int rope_dims, float* out, float* lse);
+
+/*
  * csa_sparse_attn_decode_fp8 -- csa_sparse_attn_decode with the output row quantised to fp8 in
  * the same launch as the inverse RoPE ([vLLM-V4] section 3 part 2, second fusion: inverse RoPE
  * + fp8 quantisation, the input of the output projection's fp8 matrix products).  The pages do

@@ -251,3 +251,20 @@ def test_compress_index_score_launch_count(csa):
     assert n(2, jobs(1), 2, 4, 4, csa.BF16, 64) == csa.EINVAL
     assert n(2, None, 1, 4, 4, csa.BF16, 64) == csa.EINVAL
 
+
+def test_noalloc_attention_refuses_scratch_beyond_its_array(csa):
+    """csa_sparse_attn_decode_noalloc serves at most 16 MiB of split partials from the library's
+    own array; a larger request returns CSA_EWORKSPACE before any HIP call (fake pointers)."""
+    L = csa.lib()
+    P = ctypes.pointer
+    kv = csa._CCache(1, 1, csa.FP8_E4M3, 576, 64, 10, 1, 8)
+    swa = csa._CCache(2, 2, csa.FP8_E4M3, 576, 256, 10, 1, 8)
+    # 256 queries x 128 heads x 2,176 rows: far more split partials than 16 MiB
+    need = L.csa_sparse_attn_workspace_size(256, 128, 576, 4, 1, 2048, 1 << 20, 128)
+    assert need > 16 << 20
+    st = L.csa_sparse_attn_decode_noalloc(None, 1, 1, 1, 256, 1 << 20, 1, csa.BF16, 128, P(kv), 4, 1, 2048,
+                                          P(swa), 128, 0.04, 1e4, 64, 1, None)
+    assert st == csa.EWORKSPACE
+    # and the usual argument checks come first
+    assert L.csa_sparse_attn_decode_noalloc(None, 1, 1, 1, 4, 1 << 20, 1, csa.BF16, 128, P(kv), 4, 1, 2048,
+                                            P(swa), 128, 0.04, 1e4, 64, None, None) == csa.EINVAL
