@@ -214,10 +214,14 @@ struct EntryScorer {
   const uint16_t* q;  // [total_q][n_heads][128] bf16
   const float* w;     // [total_q][n_heads]
   float* scores;      // [total_q][n_cap]
+  uint2* new_cand;    // [total_q][kNewCand]: (key, id) of the k-th entry the call inserts
 };
+constexpr int kNewCand = 64;  // new entries per query listed as ready-made candidates
 
 // Thread (head tid / 4, quarter tid % 4) takes 32 dims; the quad's sum is the head's product.
-__device__ void score_new_entry(const EntryScorer& es, int b, int j, const float* key, float* red_sh) {
+// slot: the entry's index among the entries the call inserts for sequence b.
+__device__ void score_new_entry(const EntryScorer& es, int b, int j, int slot, const float* key,
+                                float* red_sh) {
   const int tid = threadIdx.x, h = tid >> 2, qd = tid & 3;
   const int i0 = es.cu_q[b], i1 = es.cu_q[b + 1];
   for (int i = i0; i < i1; ++i) {
@@ -242,7 +246,10 @@ __device__ void score_new_entry(const EntryScorer& es, int b, int j, const float
     dot += dpp<kDppQuadXor2>(dot);
     const float c = (qd == 0 && h < es.n_heads) ? es.w[(int64_t)i * es.n_heads + h] * fmaxf(dot, 0.f) : 0.f;
     const float sum = block_sum256(c, red_sh);
-    if (tid == 0) es.scores[(int64_t)i * es.n_cap + j] = sum;
+    if (tid == 0) {
+      es.scores[(int64_t)i * es.n_cap + j] = sum;
+      if (slot < kNewCand) es.new_cand[(int64_t)i * kNewCand + slot] = make_uint2(f2key(sum), (uint32_t)j);
+    }
   }
 }
 
@@ -368,7 +375,7 @@ __device__ void compress_task(const CompressArgs& a, const Job& J, int local, Se
     if (es != nullptr && score_job) {
       store_row<true>(J.out, orow, v_sh, dim, red_sh);
       __syncthreads();  // the stored key, decoded, in v_sh
-      score_new_entry(*es, b, (int)j, v_sh, red_sh);
+      score_new_entry(*es, b, (int)j, (int)(e - e0), v_sh, red_sh);
     } else {
       store_row(J.out, orow, v_sh, dim, red_sh);
     }

@@ -7,21 +7,23 @@
 // [vLLM-V4] section 2: as fp4, 64 bytes of two-a-byte codes plus one scale per 16 values.
 // Score (reading of the DSA indexer): s_j = sum_h w_h * relu(q_h . k_j).
 //
-// Three kernels:
+// Two kernels:
 //  1. score  -- grid (chunk of 2048 entries, query).  The contraction q . k_j is dense
 //     (64 heads x 128 dims per key), so it runs on MFMA: A = the query's heads (registers),
 //     B = 16 keys per tile streamed from HBM (fp8 or fp4 codes widened exactly to bf16, an fp4
 //     block scale applied in the widening).  The head sum, relu and the fp8 row scale are
-//     applied to the MFMA output in registers.  Each workgroup also writes a lower bound on
-//     the kc-th largest score of its chunk.
-//  2. filter -- grid (chunk, query).  tau_lo = min over the full chunks of their bounds is a
-//     lower bound on the k-th largest score (each full chunk holds kc keys above its bound,
-//     and chunks * kc >= k), so every selected entry has score >= tau_lo.  Survivors are
-//     compacted, in entry order, into a chunk-sparse candidate list.
-//  3. select -- one workgroup per query: gathers the candidate lists densely into LDS (one
-//     coalesced piece per chunk), finds the exact k-th largest key by 11-bit radix passes over
-//     the candidates' own key range, then writes the winners in ascending entry order with one
-//     prefix scan, resolving exact ties towards lower entry ids.
+//     applied to the MFMA output in registers.  Each workgroup then emits its chunk's
+//     candidates: a lower bound B_c of the chunk's kc2-th largest score (one histogram over the
+//     chunk's key range) and, in entry order, every entry scoring at least B_c.  kc2 = 2 kc + 8
+//     with kc = ceil(k' / full chunks), so for any chunk to hold more of the winners than its
+//     candidates its count of winners would have to exceed twice its share by 8.
+//  2. select -- one workgroup per query: gathers the candidate lists densely into LDS (one
+//     coalesced piece per chunk, plus the entries the call's compressor inserted), finds the
+//     k'-th largest candidate key tau by 11-bit radix passes over the candidates' own key range,
+//     and writes the winners in ascending entry order with one prefix scan, resolving exact ties
+//     towards lower entry ids.  The result is exact when tau >= B_c for every chunk: then every
+//     entry scoring at least tau is a candidate.  Otherwise (scores clustered far beyond the
+//     chunks' shares) the same selection runs over every stored score of the query.
 #include "common.h"
 #include "compress_dev.h"
 #include "launch.h"
@@ -42,7 +44,9 @@ struct ScoreArgs {
   const float* w;
   DevCache cache;
   float* scores;
-  uint32_t* bounds;
+  uint2* cand;          // [total_q][n_cap]: the chunk's candidates from its first slot on
+  int4* cand_info;      // [total_q][chunks]: candidate count, least and largest key, bound B_c
+  int32_t* new_from;    // [total_q]: first entry id the call's compressor inserts (else n)
   // With the compressor in the same launch (MFMA kernel only): grid rows y < comp_rows run its
   // comp_wgs workgroups; ctx_lens[b] / 4 entries of sequence b existed before the step, the
   // rest are inserted (and scored) by the compressor, so the score workgroups neither read nor
@@ -110,13 +114,23 @@ __device__ __forceinline__ int bit_len(uint32_t v) { return v ? 32 - __clz((int)
 // +0); fmaxf would add a canonicalising max per value.
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// Lower bound of the kc-th largest of the C scores in sc_sh: one 256-bin histogram over the
-// chunk's own key range [kmin, kmax]; the bound is the lower edge of the bin that holds the
+// Per-chunk candidate quota: kc2 = 2 kc + 8, kc = ceil(k' / full chunks); 0 when the select
+// takes every entry (k' = n).
+__device__ __forceinline__ int chunk_quota(int k, int n) {
+  const int kprime = min(k, n);
+  if (kprime >= n) return 0;
+  const int m_full = max(n / C, 1);
+  const int kc = (kprime + m_full - 1) / m_full;
+  return min(C, 2 * kc + 8);
+}
+
+// Lower bound of the kc-th largest of the first nval scores in sc_sh (nval > kc): one 256-bin
+// histogram over their own key range; the bound is the lower edge of the bin that holds the
 // kc-th largest key.
-__device__ uint32_t chunk_bound(const float* sc_sh, int kc, uint32_t* hist, int* misc, uint32_t* red) {
+__device__ uint32_t chunk_bound(const float* sc_sh, int nval, int kc, uint32_t* hist, int* misc, uint32_t* red) {
   const int tid = threadIdx.x;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int i = tid; i < C; i += 256) {
+  for (int i = tid; i < nval; i += 256) {
     const uint32_t key = f2key(sc_sh[i]);
     lo = min(lo, key);
     hi = max(hi, key);
@@ -126,7 +140,7 @@ __device__ uint32_t chunk_bound(const float* sc_sh, int kc, uint32_t* hist, int*
   const int shift = max(0, bit_len(hi - lo) - 8);
   hist[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < C; i += 256) atomicAdd(&hist[((f2key(sc_sh[i]) - lo) >> shift) & 255u], 1u);
+  for (int i = tid; i < nval; i += 256) atomicAdd(&hist[((f2key(sc_sh[i]) - lo) >> shift) & 255u], 1u);
   __syncthreads();
   if (tid < kWave) pick_bin_wave0(hist, kc, misc);
   __syncthreads();
@@ -135,17 +149,43 @@ __device__ uint32_t chunk_bound(const float* sc_sh, int kc, uint32_t* hist, int*
   return bound;
 }
 
-// Tail of the float32 score kernel: write the chunk's bound when the chunk is full (the MFMA
-// kernel reduces the same bound from its registers).
-__device__ void finish_chunk(const ScoreArgs& a, int qi, int chunk, int n, int nloc,
-                             const float* sc_sh, uint32_t* hist, int* misc, uint32_t* red) {
-  const int kprime = min(a.k, n);
-  const int m_full = n / C;
-  if (nloc == C && kprime < n && m_full > 0) {
-    const int kc = (kprime + m_full - 1) / m_full;
-    uint32_t bound = 0;
-    if (kc <= C) bound = chunk_bound(sc_sh, kc, hist, misc, red);
-    if (threadIdx.x == 0) a.bounds[(int64_t)qi * a.chunks + chunk] = bound;
+// The chunk's candidates: every entry e < nval (the entries this workgroup scored) with key >=
+// bound, in entry order, from the chunk's first slot of the candidate list; its count, key
+// range and bound into cand_info.  Thread t takes entries 8 t .. 8 t + 7.  sh: >= 13 ints.
+__device__ void emit_chunk(const ScoreArgs& a, int qi, int chunk, int nval, uint32_t bound,
+                           const float* sc_sh, int* sh) {
+  static_assert(C == 256 * 8, "eight entries per thread");
+  const int base = threadIdx.x * 8;
+  const float4 v0 = *(const float4*)&sc_sh[base], v1 = *(const float4*)&sc_sh[base + 4];
+  const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t key[8];
+  int cnt = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    key[i] = f2key(v[i]);
+    const bool take = base + i < nval && key[i] >= bound;
+    cnt += take ? 1 : 0;
+    kmin = take ? min(kmin, key[i]) : kmin;
+    kmax = take ? max(kmax, key[i]) : kmax;
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if ((threadIdx.x & 63) == 0) {
+    sh[5 + (threadIdx.x >> 6)] = (int)kmin;
+    sh[9 + (threadIdx.x >> 6)] = (int)kmax;
+  }
+  int total;
+  int off = block_exscan256(cnt, sh, &total);  // (its barriers also publish the key ranges)
+  const int64_t j0 = (int64_t)chunk * C;
+  uint2* dst = a.cand + (int64_t)qi * a.n_cap + j0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (base + i < nval && key[i] >= bound) dst[off++] = make_uint2(key[i], (uint32_t)(j0 + base + i));
+  if (threadIdx.x == 0) {
+    const uint32_t lo = min(min((uint32_t)sh[5], (uint32_t)sh[6]), min((uint32_t)sh[7], (uint32_t)sh[8]));
+    const uint32_t hi = max(max((uint32_t)sh[9], (uint32_t)sh[10]), max((uint32_t)sh[11], (uint32_t)sh[12]));
+    a.cand_info[(int64_t)qi * a.chunks + chunk] = make_int4(total, (int)lo, (int)hi, (int)bound);
   }
 }
 
@@ -330,12 +370,13 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
   // repeat its last entry), so the chunk's key range is reduced from registers, and the same
   // barrier that completes sc_sh publishes the per-wave ranges.
   static_assert(C / 256 == 8, "eight groups per chunk");
-  // this step's entries (fused launch) get key 0, which no score reaches: left out of the bound
-  if (nold_loc < nloc) {
+  // this step's entries (fused launch) and entries past a partial chunk's end get key 0, which
+  // no score reaches: left out of the bound
+  if (nold_loc < C) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int eloc = (16 * i + 4 * lg + wv) * 16 + ln;
-      if (eloc >= nold_loc && eloc < nloc) lane_keys[i] = 0u;
+      if (eloc >= nold_loc) lane_keys[i] = 0u;
     }
   }
   uint32_t klo = 0xFFFFFFFFu, khi = 0u;  // over the scored entries
@@ -363,38 +404,31 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
     for (int e = threadIdx.x; e < C; e += 256)
       if (e < nold_loc || e >= nloc) dst[e] = any_old ? sc_sh[e] : 0.f;
   }
-  // the bound (full chunks): one 256-bin histogram over the chunk's own key range; the bound
-  // is the lower edge of the bin that holds the kc-th largest key
-  const int kprime = min(a.k, n);
-  const int m_full = n / C;
-  if (nloc == C && kprime < n && m_full > 0) {
-    const int kc = (kprime + m_full - 1) / m_full;
-    if (kc > C) {
-      if (threadIdx.x == 0) a.bounds[(int64_t)qi * a.chunks + chunk] = 0u;
-      return;
-    }
+  if (chunk == 0 && threadIdx.x == 0) a.new_from[qi] = min(nold, n);
+  // the candidates: a lower bound of the kc2-th largest scored entry (one 256-bin histogram over
+  // the scored entries' key range, from the keys the lanes hold) and every scored entry at or
+  // above it; a chunk with at most kc2 scored entries gives them all
+  const int kc2 = chunk_quota(a.k, n);
+  if (kc2 == 0) return;  // the select takes every entry
+  uint32_t bound = 0u;
+  if (nold_loc > kc2) {
     const uint32_t lo = min(min(red[0], red[1]), min(red[2], red[3]));
     const uint32_t hi = max(max(red2[0], red2[1]), max(red2[2], red2[3]));
-    if (nold_loc < kc) {  // fewer than kc scored entries (the rest are this step's): bound 0
-      if (threadIdx.x == 0) a.bounds[(int64_t)qi * a.chunks + chunk] = 0u;
-      return;
-    }
-    // the kc-th largest of the scored entries is a lower bound of the chunk's kc-th largest
     const int shift = max(0, bit_len(hi - lo) - 8);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (lane_keys[i]) atomicAdd(&hist[((lane_keys[i] - lo) >> shift) & 255u], 1u);
     __syncthreads();
-    if (wv == 0) {
-      pick_bin_wave0(hist, kc, misc);  // (the crossing lane writes misc[0])
-      if (lane == 0) a.bounds[(int64_t)qi * a.chunks + chunk] = lo + ((uint32_t)misc[0] << shift);
-    }
+    if (wv == 0) pick_bin_wave0(hist, kc2, misc);  // (the crossing lane writes misc[0])
+    __syncthreads();
+    bound = lo + ((uint32_t)misc[0] << shift);
   }
+  emit_chunk(a, qi, chunk, nold_loc, bound, sc_sh, (int*)hist);
 }
 
 // ---- float32 queries (any key dtype): plain per-entry dot products.
 __global__ __launch_bounds__(256) void index_score_f32(ScoreArgs a) {
-  __shared__ float sc_sh[C];
+  __shared__ __attribute__((aligned(16))) float sc_sh[C];
   __shared__ float q_sh[64 * 128];
   __shared__ float w_sh[64];
   __shared__ uint32_t hist[256];
@@ -446,92 +480,27 @@ __global__ __launch_bounds__(256) void index_score_f32(ScoreArgs a) {
   __syncthreads();
   for (int eloc = threadIdx.x; eloc < nloc; eloc += 256)
     a.scores[(int64_t)qi * a.n_cap + j0 + eloc] = sc_sh[eloc];
-  finish_chunk(a, qi, chunk, n, nloc, sc_sh, hist, misc, red);
+  if (chunk == 0 && threadIdx.x == 0) a.new_from[qi] = n;  // (no compressor in this launch)
+  const int kc2 = chunk_quota(a.k, n);
+  if (kc2 == 0) return;  // the select takes every entry
+  const uint32_t bound = nloc > kc2 ? chunk_bound(sc_sh, nloc, kc2, hist, misc, red) : 0u;
+  emit_chunk(a, qi, chunk, nloc, bound, sc_sh, (int*)hist);
 }
 
-// ---- filter: compact the chunk's entries with key >= tau_lo, in entry order.
+// ---- select: exact k'-th largest among the candidates, winners in ascending entry order.
 struct SelArgs {
   int batch, k, chunks, n_max;
   int64_t n_cap;
   const int32_t* q_pos;
   const float* scores;
-  const uint32_t* bounds;
-  uint2* cand;
-  int4* cand_info;  // per chunk: candidate count, least and largest candidate key
+  const uint2* cand;
+  const int4* cand_info;   // per chunk: candidate count, least and largest key, bound B_c
+  const int32_t* new_from; // per query: first entry id the call's compressor inserted (else n)
+  const uint2* new_cand;   // per query: (key, id) of the first kNewCand of those entries
   int32_t* topk_idx;
   float* topk_score;
 };
 
-__device__ uint32_t query_tau_lo(const SelArgs& a, int qi, int n, uint32_t* red) {
-  const int kprime = min(a.k, n);
-  const int m_full = n / C;
-  if (m_full == 0) return 0u;
-  const int kc = (kprime + m_full - 1) / m_full;
-  if (kc > C) return 0u;
-  uint32_t mn = 0xFFFFFFFFu;
-  for (int c = threadIdx.x; c < m_full; c += 256) mn = min(mn, a.bounds[(int64_t)qi * a.chunks + c]);
-  mn = wave_min_u32(mn);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mn;
-  __syncthreads();
-  return min(min(red[0], red[1]), min(red[2], red[3]));
-}
-
-__global__ __launch_bounds__(256) void index_filter(SelArgs a) {
-  __shared__ uint32_t red[4], kmin_sh[4], kmax_sh[4];
-  __shared__ int scan_sh[8];
-  const int chunk = blockIdx.x, qi = blockIdx.y;
-  const int n = query_entries(a.q_pos, qi, a.n_max);
-  const int64_t j0 = (int64_t)chunk * C;
-  if (j0 >= n) return;
-  const int kprime = min(a.k, n);
-  if (kprime == n) return;  // select takes every candidate directly
-  const int nloc = (int)min((int64_t)C, n - j0);
-  static_assert(C == 256 * 8, "the filter gives each of its 256 threads 8 entries of a chunk");
-  const int base = threadIdx.x * 8;
-  uint32_t key[8];
-  int cnt = 0;
-  // the chunk's scores are loaded before the bounds: both trips overlap
-  const float* sc = a.scores + (int64_t)qi * a.n_cap + j0;
-  if (base + 8 <= nloc) {
-    const float4 v0 = *(const float4*)(sc + base), v1 = *(const float4*)(sc + base + 4);
-    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) key[i] = f2key(v[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) key[i] = (base + i < nloc) ? f2key(sc[base + i]) : 0u;
-  }
-  const uint32_t tau = query_tau_lo(a, qi, n, red);
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;  // the chunk's candidate key range, for the select
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const bool c = base + i < nloc && key[i] >= tau;
-    cnt += c ? 1 : 0;
-    kmin = c ? min(kmin, key[i]) : kmin;
-    kmax = c ? max(kmax, key[i]) : kmax;
-  }
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  if ((threadIdx.x & 63) == 0) {
-    kmin_sh[threadIdx.x >> 6] = kmin;
-    kmax_sh[threadIdx.x >> 6] = kmax;
-  }
-  int total;
-  int off = block_exscan256(cnt, scan_sh, &total);  // (its barriers also publish kmin/kmax_sh)
-  uint2* dst = a.cand + (int64_t)qi * a.n_cap + j0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (base + i < nloc && key[i] >= tau) dst[off++] = make_uint2(key[i], (uint32_t)(j0 + base + i));
-  }
-  if (threadIdx.x == 0) {
-    const uint32_t lo = min(min(kmin_sh[0], kmin_sh[1]), min(kmin_sh[2], kmin_sh[3]));
-    const uint32_t hi = max(max(kmax_sh[0], kmax_sh[1]), max(kmax_sh[2], kmax_sh[3]));
-    a.cand_info[(int64_t)qi * a.chunks + chunk] = make_int4(total, (int)lo, (int)hi, 0);
-  }
-}
-
-// ---- select: exact k-th largest among the candidates, winners in ascending entry order.
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kDigitBits = 11;              // radix digit: 2048 bins, two per thread
@@ -559,29 +528,49 @@ __device__ __forceinline__ int2 sel_exscan2(int v0, int v1, int* sh, int* tot) {
   return make_int2(b0 + i0 - v0, b1 + i1 - v1);
 }
 
-// Candidate g of the query (dense index over the chunk-sparse list).
-template <bool IN_LDS>
-__device__ __forceinline__ uint2 cand_at(const uint2* cand_sh, const uint2* gcand, const int* off_sh,
-                                         int nchunks, int g) {
-  if (IN_LDS) return cand_sh[g];
-  int lo = 0, hi = nchunks - 1;  // last chunk c with off_sh[c] <= g
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off_sh[mid] <= g) lo = mid; else hi = mid - 1;
+// Candidate g (dense index, entry order) of the query, from one of three places:
+//   CandLds    -- gathered into LDS;
+//   CandChunks -- the chunk-sparse lists in the workspace (off_sh: chunk offsets), followed by
+//                 the entries the call's compressor inserted (their scores);
+//   CandScores -- every entry of the query, from its stored score (the fallback).
+struct CandLds {
+  const uint2* sh;
+  __device__ uint2 operator()(int g) const { return sh[g]; }
+};
+struct CandChunks {
+  const uint2* gcand;
+  const int* off_sh;
+  int nchunks;
+  const float* sc;
+  int new_from;
+  __device__ uint2 operator()(int g) const {
+    const int m_chunks = off_sh[nchunks];
+    if (g >= m_chunks) {
+      const int j = new_from + (g - m_chunks);
+      return make_uint2(f2key(sc[j]), (uint32_t)j);
+    }
+    int lo = 0, hi = nchunks - 1;  // last chunk c with off_sh[c] <= g
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off_sh[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    return gcand[(int64_t)lo * C + (g - off_sh[lo])];
   }
-  return gcand[(int64_t)lo * C + (g - off_sh[lo])];
-}
+};
+struct CandScores {
+  const float* sc;
+  __device__ uint2 operator()(int g) const { return make_uint2(f2key(sc[g]), (uint32_t)g); }
+};
 
 // The kprime-th largest key among the m candidates (all in [lo, hi]) and how many keys equal to
 // it are selected: a most-significant-digit radix select on d = key - lo, 11 bits per pass (keys
 // decided by a higher digit drop out of later passes).  With `have`, hist already holds the
 // first pass's histogram (built while the candidates were gathered).  Once the bin that holds the answer has
 // at most 64 keys, one wave ranks them directly instead of further passes.
-template <bool IN_LDS>
-__device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, bool have,
-                             const uint2* cand_sh, const uint2* gcand, const int* off_sh,
-                             int nchunks, uint32_t* hist, int* misc, int* scan_sh,
-                             uint32_t* small_sh, uint32_t& tau, int& ties_needed) {
+template <class Cand>
+__device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, bool have, Cand cand,
+                             uint32_t* hist, int* misc, int* scan_sh, uint32_t* small_sh,
+                             uint32_t& tau, int& ties_needed) {
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t prefix = 0;  // decided high digits of d
   int need = kprime;
@@ -596,7 +585,7 @@ __device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, bool h
       if (tid == 0) misc[2] = 0;
       __syncthreads();
       for (int g = tid; g < m; g += kSelThreads) {
-        const uint32_t d = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x - lo;
+        const uint32_t d = cand(g).x - lo;
         if (top >= 32 || (d >> top) == (prefix >> top)) atomicAdd(&hist[(d >> shift) & (kBins - 1)], 1u);
       }
     }
@@ -621,7 +610,7 @@ __device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, bool h
     if (top > 0 && in_bin <= 64) {
       // collect the bin's keys (any order) and rank them in one wave
       for (int g = tid; g < m; g += kSelThreads) {
-        const uint32_t key = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x;
+        const uint32_t key = cand(g).x;
         if (((key - lo) >> top) == (prefix >> top)) {
           const int slot = atomicAdd(&misc[2], 1);
           if (slot < 64) small_sh[slot] = key;  // (at most in_bin <= 64 keys match)
@@ -654,19 +643,18 @@ __device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, bool h
   ties_needed = need;  // how many keys equal to tau are selected
 }
 
-// Winners in ascending entry order: the candidates are stored in entry order, so one scan of
-// (keys above tau, keys equal to tau) per thread-contiguous range places every winner; ties
-// go to the lowest entries.
-template <bool IN_LDS>
-__device__ void write_winners(const SelArgs& a, int qi, int m, uint32_t tau, int ties_needed,
-                              const uint2* cand_sh, const uint2* gcand, const int* off_sh,
-                              int nchunks, int* scan_sh) {
+// Winners in ascending entry order: the candidates are in entry order, so one scan of (keys
+// above tau, keys equal to tau) per thread-contiguous range places every winner; ties go to the
+// lowest entries.
+template <class Cand>
+__device__ void write_winners(const SelArgs& a, int qi, int m, uint32_t tau, int ties_needed, Cand cand,
+                              int* scan_sh) {
   const int tid = threadIdx.x;
   const int per = (m + kSelThreads - 1) / kSelThreads;
   const int g0 = min(m, tid * per), g1 = min(m, g0 + per);
   int gt = 0, eq = 0;
   for (int g = g0; g < g1; ++g) {
-    const uint32_t key = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g).x;
+    const uint32_t key = cand(g).x;
     gt += key > tau;
     eq += key == tau;
   }
@@ -677,7 +665,7 @@ __device__ void write_winners(const SelArgs& a, int qi, int m, uint32_t tau, int
   int32_t* out = a.topk_idx + (int64_t)qi * a.k;
   float* outs = a.topk_score ? a.topk_score + (int64_t)qi * a.k : nullptr;
   for (int g = g0; g < g1; ++g) {
-    const uint2 c = cand_at<IN_LDS>(cand_sh, gcand, off_sh, nchunks, g);
+    const uint2 c = cand(g);
     bool take = c.x > tau;
     if (c.x == tau) { take = tr < ties_needed; ++tr; }
     if (take) {
@@ -697,7 +685,8 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
   __shared__ uint32_t small_sh[64];
   __shared__ int misc[4];
   __shared__ int scan_sh[2 * kSelWaves];
-  __shared__ uint32_t red[2 * kSelWaves];
+  __shared__ uint32_t red[3 * kSelWaves];
+  __shared__ uint2 tail_sh[kNewCand];  // the first entries the call's compressor inserted
   const int qi = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int n = query_entries(a.q_pos, qi, a.n_max);
@@ -721,36 +710,76 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
   const uint2* gcand = a.cand + (int64_t)qi * a.n_cap;
   hist[tid] = 0;  // (published by the barriers of the count scan below)
   hist[tid + kSelThreads] = 0;
-  // one trip: the per-chunk candidate counts (one chunk per thread) and, speculatively, the
-  // first 64 slots of every chunk's list (wave w reads chunks w, w + 16, ..., up to 8 of them;
-  // slots past a list's end hold stale data of this query's slice and are discarded)
+  // (the loads above and below need nothing but the query index and the workspace geometry,
+  // so they all go out in one trip; n only decides which of them are used)
+  // per chunk (one per thread): candidate count, key range and bound
+  const int4 inf = a.cand_info[(int64_t)qi * a.chunks + min(tid, a.chunks - 1)];
+  // speculatively, the first 64 slots of every chunk's list (a chunk's quota is ~2.5 times its
+  // share of the winners, so its list rarely holds more): wave w reads chunks w, w + 16, ..., up
+  // to 8 of them (slots past a list's end are discarded)
   constexpr int kPieces = 8;
   uint2 v[kPieces];
 #pragma unroll
   for (int u = 0; u < kPieces; ++u) {
-    const int c = min(w + u * kSelWaves, nchunks - 1);
+    const int c = min(w + u * kSelWaves, a.chunks - 1);
     v[u] = gcand[(int64_t)c * C + lane];
   }
-  // and, in the same trip, each chunk's candidate count and key range (from the filter)
-  const int4 inf = tid < nchunks ? a.cand_info[(int64_t)qi * a.chunks + tid] : make_int4(0, -1, 0, 0);
-  const int cnt = min(max(inf.x, 0), C);
-  uint32_t lo = wave_min_u32((uint32_t)inf.y), hi = wave_max_u32((uint32_t)inf.z);
+  // the entries the call's compressor inserted: where they start, and the first 64 of them
+  const int nf = min(max(a.new_from[qi], 0), n);
+  const uint2 nc = a.new_cand[(int64_t)qi * kNewCand + lane];
+  if (w == 0) tail_sh[lane] = nc;  // (published by the scan's barriers)
+  const bool has = tid < nchunks;
+  const int cnt = has ? min(max(inf.x, 0), C) : 0;
+  uint32_t lo = wave_min_u32(has && cnt ? (uint32_t)inf.y : 0xFFFFFFFFu);
+  uint32_t hi = wave_max_u32(has && cnt ? (uint32_t)inf.z : 0u);
+  const uint32_t bmax = wave_max_u32(has ? (uint32_t)inf.w : 0u);
   if (lane == 0) {
     red[w] = lo;
     red[kSelWaves + w] = hi;
+    red[2 * kSelWaves + w] = bmax;
   }
   int tot2[2];
   off_sh[tid] = sel_exscan2(cnt, 0, scan_sh, tot2).x;  // (its barriers also publish red)
-  const int m = tot2[0];
+  const int m_chunks = tot2[0];
+  const int n_new = n - nf;
+  const int m = m_chunks + n_new;
+  uint32_t maxb = 0u;
 #pragma unroll
   for (int i = 0; i < kSelWaves; ++i) {
     lo = min(lo, red[i]);
     hi = max(hi, red[kSelWaves + i]);
+    maxb = max(maxb, red[2 * kSelWaves + i]);
   }
-  if (tid == 0) off_sh[nchunks] = m;
+  // new entry r: listed (r < 64) or its stored score
+  auto new_entry = [&](int r) -> uint2 {
+    const int j = nf + r;
+    return r < kNewCand ? tail_sh[r] : make_uint2(f2key(sc[j]), (uint32_t)j);
+  };
+  if (n_new > 0) {  // their keys widen the range
+    for (int r = tid; r < n_new; r += kSelThreads) {
+      const uint32_t key = new_entry(r).x;
+      lo = min(lo, key);
+      hi = max(hi, key);
+    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    __syncthreads();
+    if (lane == 0) {
+      red[w] = lo;
+      red[kSelWaves + w] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSelWaves; ++i) {
+      lo = min(lo, red[i]);
+      hi = max(hi, red[kSelWaves + i]);
+    }
+  }
+  if (tid == 0) off_sh[nchunks] = m_chunks;
   __syncthreads();
   uint32_t tau;
   int ties_needed;
+  const CandChunks in_ws{gcand, off_sh, nchunks, sc, nf};
   if (m <= kSelCap) {
     // the gather also builds the first radix pass's histogram (bins of the candidates' range)
     const int shift0 = max(0, bit_len(hi - lo) - kDigitBits);
@@ -770,15 +799,28 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
       const int j0 = c < w + kPieces * kSelWaves ? 64 : 0;
       for (int j = j0 + lane; j < len; j += 64) put(off_sh[c] + j, gcand[(int64_t)c * C + j]);
     }
+    // the new entries, after every chunk's candidates (their ids are the largest)
+    for (int r = tid; r < n_new; r += kSelThreads) put(m_chunks + r, new_entry(r));
     __syncthreads();
-    radix_select<true>(m, kprime, lo, hi, true, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh,
-                       small_sh, tau, ties_needed);
-    write_winners<true>(a, qi, m, tau, ties_needed, cand_sh, gcand, off_sh, nchunks, scan_sh);
+    const CandLds in_lds{cand_sh};
+    radix_select(m, kprime, lo, hi, true, in_lds, hist, misc, scan_sh, small_sh, tau, ties_needed);
+    if (tau >= maxb) {
+      write_winners(a, qi, m, tau, ties_needed, in_lds, scan_sh);
+      return;
+    }
   } else {
-    radix_select<false>(m, kprime, lo, hi, false, cand_sh, gcand, off_sh, nchunks, hist, misc, scan_sh,
-                        small_sh, tau, ties_needed);
-    write_winners<false>(a, qi, m, tau, ties_needed, cand_sh, gcand, off_sh, nchunks, scan_sh);
+    radix_select(m, kprime, lo, hi, false, in_ws, hist, misc, scan_sh, small_sh, tau, ties_needed);
+    if (tau >= maxb) {
+      write_winners(a, qi, m, tau, ties_needed, in_ws, scan_sh);
+      return;
+    }
   }
+  // Some chunk's bound lies above the candidates' k'-th largest key, so entries of that chunk
+  // scoring between the two may be missing: select over every stored score of the query.
+  const CandScores all{sc};
+  __syncthreads();
+  radix_select(n, kprime, 0u, 0xFFFFFFFFu, false, all, hist, misc, scan_sh, small_sh, tau, ties_needed);
+  write_winners(a, qi, n, tau, ties_needed, all, scan_sh);
 }
 
 ScoreArgs make_score_args(const IndexLaunch& a, const IndexWorkspace& ws) {
@@ -795,7 +837,9 @@ ScoreArgs make_score_args(const IndexLaunch& a, const IndexWorkspace& ws) {
   s.w = a.head_w;
   s.cache = to_dev(a.idx_cache);
   s.scores = ws.scores;
-  s.bounds = ws.bounds;
+  s.cand = ws.cand;
+  s.cand_info = ws.cand_info;
+  s.new_from = ws.new_from;
   return s;
 }
 
@@ -819,7 +863,8 @@ size_t index_workspace_bytes(int total_q, int max_context, int k) {
   size_t bytes = 0;
   auto add = [&](size_t b) { bytes += (b + 255) & ~(size_t)255; };
   add((size_t)total_q * n_cap * sizeof(float));
-  add((size_t)total_q * chunks * sizeof(uint32_t));
+  add((size_t)total_q * sizeof(int32_t));
+  add((size_t)total_q * kNewCand * sizeof(uint2));
   add((size_t)total_q * n_cap * sizeof(uint2));
   add((size_t)total_q * chunks * sizeof(int4));
   return bytes;
@@ -834,7 +879,8 @@ IndexWorkspace index_workspace_carve(void* ws, int total_q, int max_context, int
   char* p = (char*)ws;
   auto take = [&](size_t b) { char* r = p; p += (b + 255) & ~(size_t)255; return (void*)r; };
   w.scores = (float*)take((size_t)total_q * w.n_cap * sizeof(float));
-  w.bounds = (uint32_t*)take((size_t)total_q * w.chunks * sizeof(uint32_t));
+  w.new_from = (int32_t*)take((size_t)total_q * sizeof(int32_t));
+  w.new_cand = (uint2*)take((size_t)total_q * kNewCand * sizeof(uint2));
   w.cand = (uint2*)take((size_t)total_q * w.n_cap * sizeof(uint2));
   w.cand_info = (int4*)take((size_t)total_q * w.chunks * sizeof(int4));
   return w;
@@ -849,7 +895,7 @@ hipError_t launch_compress_index_score(const IndexLaunch& a, const IndexWorkspac
   s.comp_rows = (blocks + ws.chunks - 1) / ws.chunks;
   s.ctx_lens = c.ctx_lens;
   s.scorer = EntryScorer{score_job, a.n_heads, a.max_context / 4, ws.n_cap, a.cu_q, a.q_pos,
-                         (const uint16_t*)a.q_idx, a.head_w, ws.scores};
+                         (const uint16_t*)a.q_idx, a.head_w, ws.scores, ws.new_cand};
   // the compressor's rows come first, so its workgroups are dispatched before the score's
   const dim3 grid(ws.chunks, a.total_q + s.comp_rows);
   const int ht = (a.n_heads + 15) / 16;
@@ -883,14 +929,12 @@ hipError_t launch_index_select(const IndexLaunch& a, int32_t* topk_idx, float* t
   s.n_cap = ws.n_cap;
   s.q_pos = a.q_pos;
   s.scores = ws.scores;
-  s.bounds = ws.bounds;
   s.cand = ws.cand;
   s.cand_info = ws.cand_info;
+  s.new_from = ws.new_from;
+  s.new_cand = ws.new_cand;
   s.topk_idx = topk_idx;
   s.topk_score = topk_score;
-  hipLaunchKernelGGL(index_filter, dim3(ws.chunks, a.total_q), dim3(256), 0, stream, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(index_select, dim3(a.total_q), dim3(kSelThreads), 0, stream, s);
   return hipGetLastError();
 }

@@ -63,9 +63,10 @@ constexpr int kIndexChunk = 2048;
 
 struct IndexWorkspace {
   float* scores;       // [total_q][n_cap]
-  uint32_t* bounds;    // [total_q][chunks]   key lower bound of each full chunk
+  int32_t* new_from;   // [total_q]           first entry id the call's compressor inserted
+  uint2* new_cand;     // [total_q][64]       (key, id) of the entries the call's compressor inserted
   uint2* cand;         // [total_q][n_cap]    (key, entry) candidates, chunk-sparse
-  int4* cand_info;     // [total_q][chunks]   candidate count, least and largest candidate key
+  int4* cand_info;     // [total_q][chunks]   candidate count, least and largest key, bound
   int chunks;          // per query
   int64_t n_cap;       // chunks * kIndexChunk
 };

@@ -83,6 +83,27 @@ def test_large_selections(gpu, ctx, k):
     assert not rep["fail"], rep["fail"][:10]
 
 
+def _cluster_winners(d):
+    """Scale the first 4,096 indexer keys of every sequence by 8 (their fp8 row scales), so
+    nearly all of the top k lie in the first two 2,048-entry chunks: far more than those chunks'
+    candidate quotas."""
+    rows, scales, bt = d["idx"]
+    for b in range(bt.shape[0]):
+        for lb in range(64):  # 64 entries per logical block: blocks 0..63 hold entries 0..4095
+            scales[int(bt[b, lb])] *= 8.0
+
+
+@pytest.mark.gpu
+def test_clustered_winners_take_the_full_scan(gpu):
+    """When the winners crowd into a few chunks, the candidates' k'-th largest key falls below
+    those chunks' bounds, so the select kernel must run its exact fallback over every stored
+    score; the result must still be the oracle's top-k (fused compressor launch included)."""
+    cfg = D(C.C4A_1M_B4_FP8, name="c4a_clustered_winners", ctx_after=(200000, 199999, 60000), k=1024)
+    print(f"case {cfg.name}", flush=True)
+    rep = P.run_step_parity(cfg, verbose=True, prep=_cluster_winners, fast=True)
+    assert not rep["fail"], rep["fail"][:10]
+
+
 @pytest.mark.gpu
 def test_max_k(gpu):
     """k = 65536, the largest the ABI accepts, over a 300K-token context (75,000 entries): the
