@@ -7,10 +7,14 @@ scale, fp8 indexer keys (64 heads x 128), 128 query heads of 576, top-k 2048, wi
 A step is the whole hot path: compress the new token (main KV + window row, and indexer
 key), index scores + exact top-k, sparse K=V attention + inverse RoPE.  Inputs are resident
 in HBM before timing; steps rotate over several copies of the caches so that repeated steps
-cannot be served from the 256 MB Infinity Cache.  The headline time is the K steps replayed
-from a HIP graph (one step per cache replica in the graph), as the pages deploy with full
-graphs; the same K steps issued eagerly are timed too (ms_per_step_eager), and that eager
-loop is where the dominant kernel's launches are timed with HIP events.
+cannot be served from the 256 MB Infinity Cache.  The headline time is the median of 5 timed
+trials of K steps replayed from a HIP graph (one step per cache replica in the graph), as the
+pages deploy with full graphs; the same K steps issued eagerly are timed too
+(ms_per_step_eager), and so is the pages' two-stream schedule, eagerly and from a graph.  The
+dominant kernel (the index score launch) is timed with HIP events around 20 of its launches
+back to back in a graph, which is what the kernel trace's average duration measures; the
+events around each launch inside the eager loop also hold the command processor's dispatch
+(launch_us_in_step).
 
 Prints one JSON line.  --gpus N > 1 is not supported (one GPU only).
 """
@@ -31,8 +35,9 @@ sys.path.insert(0, ROOT)
 METRIC = "c4a sparse decode query-tokens/s and achieved HBM GB/s at 1M context"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "index_score_mfma_c4a_1m_b4_counters.txt")
-INDEX_SRC = os.path.join(ROOT, "compressed_sparse_long_c4a_amd", "csrc", "index.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_step_c4a_1m_b4_fp8_counters.txt")
+CSRC = os.path.join(ROOT, "compressed_sparse_long_c4a_amd", "csrc")
+TRIALS = 5  # timed trials of K steps; the median is reported
 
 
 def row_bytes(dtype: str, dim: int) -> int:
@@ -109,34 +114,36 @@ def score_launch_bytes(step, ab: dict) -> int:
     return ab["index_score"] + extra
 
 
-def score_kernel_sha1() -> str:
-    """SHA-1 of the score kernel's source text (from its section comment to the next kernel's),
-    so the counter figures go stale when that kernel changes and only then."""
-    text = open(INDEX_SRC).read()
-    a = text.index("// ---- MFMA score kernel")
-    b = text.index("// ---- float32 queries")
-    return hashlib.sha1(text[a:b].encode()).hexdigest()
+def kernels_sha1() -> str:
+    """SHA-1 over the text of every kernel source (csrc/*.hip and *.h), so the committed counter
+    figures go stale as soon as any kernel changes."""
+    h = hashlib.sha1()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
 
 
-def counters_traffic(cfg):
-    """HBM bytes per index-score launch from the committed rocprofv3 counter summary, or None
-    when there is none, it was taken from a different version of the kernel source, or the
-    workload is not the one it was taken on (the 1M c4a fp8 decode)."""
+def counters(cfg):
+    """HBM bytes per launch of the score kernel and per step (all of the step's kernels), from
+    the committed rocprofv3 counter summary: (score_bytes, step_bytes), or (None, None) when
+    there is none, it was taken from different kernel sources, or the workload is not the one it
+    was taken on (the 1M c4a fp8 decode)."""
     from workloads import configs
     if cfg.name != configs.HEADLINE.name or not os.path.exists(COUNTERS_FILE):
-        return None
+        return None, None
     kv = {}
     for line in open(COUNTERS_FILE):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    src_hash = score_kernel_sha1()
-    if kv.get("source_sha1") != src_hash:
-        return None
+    if kv.get("source_sha1") != kernels_sha1():
+        return None, None
     try:
-        return float(kv["traffic_bytes_per_launch"])
+        return float(kv["score_traffic_bytes_per_launch"]), float(kv["step_traffic_bytes"])
     except (KeyError, ValueError):
-        return None
+        return None, None
 
 
 def time_launches(fn, reps: int = 50, replays: int = 5) -> float:
@@ -240,8 +247,8 @@ def attn_fp8_rows(cfg, step, g) -> dict:
 def fp4_indexer_rows(cfg, d, reps, steps: int) -> dict:
     """The same step with the indexer key cache in fp4 (two E2M1 codes a byte, one E8M0 scale
     per 16 values: 72-byte keys instead of 132), every other input shared with the timed step:
-    the eager step time and the score kernel's launch time from HIP events, as for the
-    roofline of the fp8 step."""
+    the step time replayed from a graph and the score kernel's launch time (20 launches back
+    to back), as for the fp8 step."""
     import dataclasses
     import torch
     from compressed_sparse_long_c4a_amd import PagedCache, pipeline
@@ -260,15 +267,11 @@ def fp4_indexer_rows(cfg, d, reps, steps: int) -> dict:
     for g in g4:
         step.fast(g)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(steps):
-        step.fast(g4[i % len(g4)], ev[i])
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
-    score_us = statistics.mean(x.elapsed_time(y) for x, y in ev) * 1e3
+    graph = graph_of(lambda g: step.fast(g), g4)
+    ms = statistics.median(time_graph(graph, max(1, steps // len(g4)))) / len(g4)
+    del graph
+    launch = (lambda g: step.compress_index_score(g)) if step.via_score else (lambda g: step.index_score(g))
+    score_us = back_to_back_ms(launch, g4) * 1e3
     nbytes = score_launch_bytes(step, algorithmic_bytes(cfg4, d))
     total_q = d["q_pos"].shape[0]
     return {"workload": cfg4.name, "kernel": "index_score_mfma (fp4 keys)",
@@ -310,24 +313,87 @@ def clone_caches(g: dict) -> dict:
     return r
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, d) -> dict:
-    from threadpoolctl import threadpool_info
+    """The float64 oracle running the same step (every query: compress, the full indexer scans,
+    top-k, attention, inverse RoPE) on the host: the median of 3 runs with numpy's threads on
+    every core this process may use, and one run on a single thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from tests import oracle_step as O
     caches = O.prepare(d)
-    # the whole step, repeated until at least 10 s of host time have been spent (at most 8
-    # times; a repeat rewrites the same cache rows)
-    reps, dt = 0, 0.0
-    while reps < 8 and (reps == 0 or dt < 10.0):
-        t0 = time.perf_counter()
-        O.run_oracle(cfg, d, caches=caches)
-        dt += time.perf_counter() - t0
-        reps += 1
     total_q = d["q_pos"].shape[0]
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": reps * total_q / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole step of the same workload ({total_q} queries: compress, index "
-                      f"scores and top-k, attention, inverse RoPE) on the float64 oracle, run "
-                      f"{reps} times in {dt:.1f} s"}
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+
+    def one(threads=None):
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            O.run_oracle(cfg, d, caches=caches)   # (a repeat rewrites the same cache rows)
+            return time.perf_counter() - t0
+    with threadpool_limits(limits=cores):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    runs = [one(cores) for _ in range(3)]
+    single = one(1)
+    med = statistics.median(runs)
+    return {"value": total_q / med, "unit": "query-tokens/s", "cores": used, "kind": "oracle",
+            "cpu": cpu_model(), "nproc": cores,
+            "single_thread_value": total_q / single,
+            "sample": f"the whole step of the same workload ({total_q} queries: compress, index scores "
+                      f"and top-k, attention, inverse RoPE) on the float64 oracle: median of 3 runs "
+                      f"({', '.join(f'{r:.2f}' for r in runs)} s) with {used} BLAS threads, and one "
+                      f"run on one thread ({single:.2f} s)"}
+
+
+def graph_of(fn, reps):
+    """A HIP graph holding fn(g) once for every input dict g of reps (warmed up on a side stream)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for g in reps:
+            fn(g)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for g in reps:
+            fn(g)
+    graph.replay()
+    torch.cuda.synchronize()
+    return graph
+
+
+def back_to_back_ms(launch, reps, n: int = 20) -> float:
+    """Milliseconds per call of launch(g): n calls back to back in one HIP graph, g rotating over
+    the cache replicas reps, median of the timed trials."""
+    import torch
+    graph = graph_of(lambda _g: [launch(reps[i % len(reps)]) for i in range(n)], reps[:1])
+    ms = statistics.median(time_graph(graph, 10)) / n
+    del graph
+    torch.cuda.synchronize()
+    return ms
+
+
+def time_graph(graph, replays: int, trials: int = TRIALS) -> list:
+    """Milliseconds per replay of `graph` in each of `trials` timed runs of `replays` replays."""
+    import torch
+    out = []
+    for _ in range(trials):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(replays):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / replays)
+    return out
 
 
 def main() -> int:
@@ -343,8 +409,6 @@ def main() -> int:
                     help="skip the separate timings of the rows beyond the step")
     ap.add_argument("--no-stream-probe", action="store_true",
                     help="skip the 2 GiB read that measures the achievable read bandwidth")
-    ap.add_argument("--two-stream", action="store_true",
-                    help="also time the schedule with the main-KV compress on a second stream")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device-to-device copy (a reference for byte counters)")
     args = ap.parse_args()
@@ -381,31 +445,63 @@ def main() -> int:
         step.run(reps[i % len(reps)], with_lse=False)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     has_index = "index" in cfg.stages
     for g in reps:                       # marshal the C calls of every replica once
         step.fast(g)
     torch.cuda.synchronize()
+    # the K steps issued eagerly, one launch at a time (events around every score launch)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(K):
         step.fast(reps[i % len(reps)], ev[i] if has_index else None)
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
-    score_ms = statistics.mean(a.elapsed_time(b) for a, b in ev) if has_index else None
-    print(f"# timed {K} steps: {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    score_ms_in_step = statistics.mean(a.elapsed_time(b) for a, b in ev) if has_index else None
+    print(f"# timed {K} eager steps: {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
-    # the pages' two-stream schedule (main-KV compress beside the indexer), for comparison
+    # the same K steps replayed from a HIP graph that holds one step per cache replica, timed in
+    # TRIALS trials; the median trial is the headline
+    graph_ms, graph_trials = None, None
+    if not args.no_graph:
+        try:
+            graph = graph_of(lambda g: step.fast(g), reps)
+            graph_trials = [t / len(reps) for t in time_graph(graph, max(1, K // len(reps)))]
+            graph_ms = statistics.median(graph_trials)
+            del graph
+        except Exception as exc:  # graph capture is reported, never required
+            print(f"# graph variant unavailable: {exc}", file=sys.stderr)
+
+    # the dominant kernel's launch time: the step's own score launch (with the compressor
+    # workgroups when it has them), 20 times back to back in a graph, rotating over the cache
+    # replicas as the steps do (so the keys come from HBM, not the infinity cache), events
+    # around the replays
+    score_ms = None
+    if has_index:
+        launch = (lambda g: step.compress_index_score(g)) if step.via_score else (lambda g: step.index_score(g))
+        score_ms = back_to_back_ms(launch, reps)
+
+    # the pages' two-stream schedule (main-KV compressor and window rows on a second stream,
+    # beside the indexer), issued eagerly and replayed from a graph
     ms_two = None
-    if args.two_stream and has_index and "compress" in cfg.stages:
+    if has_index and "compress" in cfg.stages:
+        step.run_overlapped(reps[0], with_lse=False)
+        torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(K):
             step.run_overlapped(reps[i % len(reps)], with_lse=False)
         b.record()
         torch.cuda.synchronize()
-        ms_two = a.elapsed_time(b) / K
+        ms_two = {"eager": round(a.elapsed_time(b) / K, 5), "graph": None}
+        if not args.no_graph:
+            try:
+                g2 = graph_of(lambda g: step.run_overlapped(g, with_lse=False), reps)
+                ms_two["graph"] = round(statistics.median(time_graph(g2, max(1, K // len(reps)))) / len(reps), 5)
+                del g2
+            except Exception as exc:
+                print(f"# two-stream graph unavailable: {exc}", file=sys.stderr)
 
     # per-stage breakdown (separate pass, events around every stage)
     stages = {}
@@ -432,34 +528,6 @@ def main() -> int:
     for s in names:
         stages[s] = round(statistics.median(a.elapsed_time(b) for a, b in evs[s]) * 1e3, 2)
 
-    # the same step captured in a HIP graph (one step per cache replica), replayed
-    graph_ms = None
-    if not args.no_graph:
-        try:
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            run = lambda g, with_lse: step.fast(g)
-            with torch.cuda.stream(s):
-                for g in reps:
-                    run(g, with_lse=False)
-            torch.cuda.current_stream().wait_stream(s)
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                for g in reps:
-                    run(g, with_lse=False)
-            graph.replay()
-            torch.cuda.synchronize()
-            reps_n = max(1, K // len(reps))
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(reps_n):
-                graph.replay()
-            b.record()
-            torch.cuda.synchronize()
-            graph_ms = a.elapsed_time(b) / (reps_n * len(reps))
-        except Exception as exc:  # graph capture is reported, never required
-            print(f"# graph variant unavailable: {exc}", file=sys.stderr)
-
     ab = algorithmic_bytes(cfg, d)
     step_bytes = sum(ab.values())
     fl = algorithmic_flops(cfg, d)
@@ -467,8 +535,9 @@ def main() -> int:
     total_q = d["q_pos"].shape[0]
     # the headline: the K steps replayed from the HIP graph (the pages deploy with full CUDA
     # graphs); the eager issue of the same K steps is reported beside it
-    graph_head = graph_ms is not None and K % len(reps) == 0
+    graph_head = graph_ms is not None
     ms_head = graph_ms if graph_head else ms_step
+    score_traffic, step_traffic = counters(cfg)
     value = total_q / (ms_head / 1e3)
     result = {
         "metric": METRIC,
@@ -492,7 +561,9 @@ def main() -> int:
         "mfma_frac": round(step_flops / (ms_head / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "stages_us": stages,
         "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 5),
-        "ms_per_step_two_stream": None if ms_two is None else round(ms_two, 5),
+        "ms_per_step_graph_trials": None if graph_trials is None else [round(t, 5) for t in graph_trials],
+        "ms_per_step_two_stream": ms_two,
+        "step_traffic_bytes": step_traffic,
         "config": {
             "workload": cfg.name, "ratio": cfg.ratio, "batch": cfg.batch,
             "context": list(cfg.ctx_after), "new_tokens": cfg.new_tokens,
@@ -514,13 +585,15 @@ def main() -> int:
                 "kernel": kname, "bound": "mfma", "achieved": round(tf, 1),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": None, "launch_us": round(score_ms * 1e3, 2),
+                "launch_us_in_step": round(score_ms_in_step * 1e3, 2),
                 "algorithmic_flops_per_launch": launch_flops, "algorithmic_bytes_per_launch": launch_bytes,
             }
         else:
             result["roofline"] = {
                 "kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": counters_traffic(cfg), "launch_us": round(score_ms * 1e3, 2),
+                "traffic": score_traffic, "launch_us": round(score_ms * 1e3, 2),
+                "launch_us_in_step": round(score_ms_in_step * 1e3, 2),
                 "algorithmic_bytes_per_launch": launch_bytes,
             }
         if not args.no_stream_probe and result["roofline"]["bound"] == "hbm":
