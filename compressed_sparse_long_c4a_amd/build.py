@@ -32,8 +32,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libcsa)")
 
 
-def build(verbose: bool = False, src_dir: str | None = None, out: str | None = None) -> str:
-    """Compile every .hip source of csrc/ (or src_dir) and link one shared library (LIB or out)."""
+def build(verbose: bool = False, src_dir: str | None = None, out: str | None = None,
+          extra_flags: list[str] | None = None, link_flags: list[str] | None = None) -> str:
+    """Compile every .hip source of csrc/ (or src_dir) and link one shared library (LIB or out).
+    extra_flags / link_flags: additional hipcc options for every compile / for the link."""
     src_dir = src_dir or os.path.join(PKG, "csrc")
     out = out or LIB
     srcs = sorted(glob.glob(os.path.join(src_dir, "*.hip")))
@@ -41,8 +43,8 @@ def build(verbose: bool = False, src_dir: str | None = None, out: str | None = N
     with tempfile.TemporaryDirectory(prefix="csa_build_") as tmpdir:
         def compile_one(src: str) -> str:
             obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
-            cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *inc, "-c", src,
-                   "-o", obj]
+            cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *(extra_flags or []),
+                   *inc, "-c", src, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             subprocess.run(cmd, check=True)
@@ -51,7 +53,7 @@ def build(verbose: bool = False, src_dir: str | None = None, out: str | None = N
         with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
             objs = list(ex.map(compile_one, srcs))
         tmp = out + ".tmp"
-        cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
+        cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *(link_flags or []), *objs, "-o", tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
