@@ -20,9 +20,14 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-# Per-source extra hipcc flags.  index.hip: MFMA accumulators in ordinary VGPRs, so the score
-# epilogue (relu, head weights) reads them without one v_accvgpr_read per value.
-FILE_FLAGS: dict[str, list[str]] = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra hipcc flags: MFMA accumulators in ordinary VGPRs.  index.hip: the score
+# epilogue (relu, head weights) reads them without one v_accvgpr_read per value.  attn.hip: the
+# one-wave-per-SIMD bf16 kernel scales its output accumulators in place when the softmax
+# reference moves (with them in AGPRs every value is copied out and back, and the copies of
+# all 144 at once made the register allocator spill); the other attention kernels run at two
+# waves per SIMD and use no AGPRs either way.
+FILE_FLAGS: dict[str, list[str]] = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                                    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:

@@ -6,6 +6,9 @@
 // inverse RoPE: with v_n = k_n = R_n k the output must be multiplied by R_m^{-1}, leaving
 // R_{n-m}.  [vLLM-V4] appendix, exact k values: c128a attends to every entry (top-k = 8192).
 //
+// Three partial kernels, one per row / query format: attn_partial_w (bf16 rows, bf16 queries)
+// and attn_partial_fp8 (fp8 rows, bf16 queries) are described where they are defined; the
+// generic one covers float32 rows or queries:
 // Kernel 1 (attn_partial), grid (row split, 16-head group, query).  The addresses (and fp8
 //   scales) of the split's rows are resolved once into LDS.  The workgroup's waves are
 //   (dq, ri): dq picks a quarter of the row's dimensions (32-dim k-steps, 5/5/4/4 of 18 for
@@ -110,7 +113,17 @@ struct Args {
 template <int DIM, int NT>
 __device__ __forceinline__ void store_head_rows(const Args& a, int s, int hg, int qi,
                                                 const float (*mb)[DIM + 4], float (*hml)[2],
-                                                float Mh, float Lh) {
+                                                float Mh, float Lh,
+                                                const float (*mb2)[DIM + 4] = nullptr) {
+  // (mb2, when given, holds a second part of the same rows: the stored rows are mb + mb2)
+  auto row4 = [&](int h, int d) {
+    float4 v = *(const float4*)&mb[h][d];
+    if (mb2) {
+      const float4 w = *(const float4*)&mb2[h][d];
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    return v;
+  };
   const int tid = threadIdx.x;
   if (a.direct) {
     if (tid < 16) {
@@ -126,7 +139,7 @@ __device__ __forceinline__ void store_head_rows(const Args& a, int s, int hg, in
       if (hq >= a.n_heads) continue;
       const float L = hml[h][1];
       const float inv = L > 0.f ? 1.0f / L : 0.f;
-      const float4 v = *(const float4*)&mb[h][d];
+      const float4 v = row4(h, d);
       float4 r = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
       if (d >= rope0) {  // pairs (d, d+1) and (d+2, d+3) by -t theta_i
         float c0, s0, c1, s1;
@@ -145,7 +158,7 @@ __device__ __forceinline__ void store_head_rows(const Args& a, int s, int hg, in
   const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg;
   for (int i = tid; i < 16 * DIM / 4; i += NT) {
     const int h = i / (DIM / 4), d = 4 * (i - h * (DIM / 4));
-    *(float4*)(a.part_o + (pbase + h) * DIM + d) = *(const float4*)&mb[h][d];
+    *(float4*)(a.part_o + (pbase + h) * DIM + d) = row4(h, d);
   }
   if (tid < 16) {
     a.part_ml[(pbase + tid) * 2 + 0] = Mh;
@@ -858,6 +871,327 @@ __global__ __launch_bounds__(kF8Threads) void attn_partial_fp8(Args a) {
   }
 }
 
+// ---- bf16 rows with bf16 queries.  Four waves, one per SIMD, and nothing shared between them
+// inside the row loop: wave w takes the 16-row tiles w, w + 4, w + 8, ... of the split for the
+// workgroup's 16 heads and, per tile, computes S^T over the full row width (Q^T held in
+// registers as the B operand), runs its own online softmax, and accumulates O^T over every
+// dimension.  Two measured gfx950 costs shape it:
+// * loaded straight into the MFMA operand layout, every load instruction would read 64 bytes of
+//   each of 16 rows, a pattern the vector L1 serves at ~15 bytes per clock per compute unit;
+//   the rows arrive instead by LDS DMA (global_load_lds_dwordx4), each instruction moving whole
+//   128-byte lines of 8 rows (~40 bytes per clock including the operand reads back), into two
+//   slots per wave, the next tile's DMA in flight while one is computed;
+// * PV needs the rows transposed (V^T: a lane holds four rows of one dimension); a transposing
+//   LDS read costs ~25 clocks per KB of the compute unit's LDS and a b128 LDS write ~16, so
+//   the matrix cores transpose instead: an MFMA of a 16 x 32 operand block with an identity B
+//   operand leaves A[4 g .. 4 g + 3][j] in lane (j, g) -- exactly the V^T operand layout -- as
+//   float32 values that convert back to bf16 exactly; two such MFMAs per 32-dim k-step.
+// A tile thus costs 18 QK + 36 transpose + 36 PV MFMAs.  With one wave per SIMD a wave holds
+// Q^T and the whole O^T of its heads; the waves' (m, l, O) are merged through LDS at the end and
+// one partial row per head leaves from registers.
+constexpr int kWWaves = 4;
+constexpr int kWThreads = 64 * kWWaves;
+static_assert(kRowsPerSplit % kWThreads == 0 && kRowsPerSplit % (16 * kWWaves) == 0, "split size");
+template <int DIM>
+__global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
+  constexpr int NKS = DIM / 32;         // k-steps of a row
+  constexpr int NDT = DIM / 16;         // 16-dim output tiles
+  constexpr int MROW = DIM + 4;         // floats per row of the two merge buffers
+  constexpr int RB = 2 * DIM, NL = RB / 128;  // bytes and 128-byte lines of a row
+  constexpr int SLOT = 16 * RB + 128;         // LDS bytes of a tile slot
+  static_assert(RB % 128 == 0 && 2 * 16 * MROW * 4 <= 2 * kWWaves * SLOT, "slots hold the merge buffers");
+  // each staged row as one word: physical row index, bit 31 = a window row (the window cache),
+  // bit 30 = padding or a rejected entry (masked; the word still names a loadable row)
+  __shared__ uint32_t row_sh[kRowsPerSplit];
+  // two tile slots per wave (the rows arrive here by LDS DMA); the final merge reuses the space
+  __shared__ __attribute__((aligned(16))) char slot_sh[2 * kWWaves * SLOT];
+  __shared__ float hml_sh[16][2];  // per head (M, L) of the workgroup (single-split rows)
+  __shared__ float ml_sh[kWWaves][16][2];
+
+  int s, hg, qi;
+  if (!wg_coords(a, s, hg, qi)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15, lg = lane >> 4;
+  const int H = a.n_heads;
+  const char* kvbase = (const char*)a.kv.rows;
+  const int r_begin = s * a.rows_per_split;
+
+  // ---- trip 1 (all unconditional): list entries, Q^T, sequence start, position
+  constexpr int RPT = kRowsPerSplit / kWThreads;
+  int ent[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int pos = r_begin + min(tid + kWThreads * u, a.rows_per_split - 1);
+    ent[u] = a.has_topk ? a.topk[(int64_t)qi * a.k + min(pos, a.k - 1)] : pos;
+  }
+  // Q^T as the B operand: lane (head ln, group lg) holds q[h][32 ks + 8 lg .. +7] (heads past
+  // the last repeat it; their rows are never stored)
+  bf16x8 qb[NKS];
+  {
+    const int h = min(16 * hg + ln, H - 1);
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)qi * H + h) * DIM + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, load_global16(qrow + 32 * ks));
+  }
+  // Q^T lives in the accumulation registers (the MFMA reads its B operand from either file):
+  // the ordinary registers then hold O^T and leave room for the PV operands in flight
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qb[ks]));
+  const int cu_v = seq_load(a.cu_q, a.batch);
+  const int t = a.q_pos[qi];
+  const int b = seq_pick(a.cu_q, a.batch, qi, cu_v);
+
+  const int n_vis = min((t + 1) / a.ratio, a.n_max);
+  const int n_c = a.has_topk ? a.k : n_vis;
+  const int n_w = min(a.window, t + 1);
+  const int n_rows = n_c + n_w;
+  const int nrows = (n_w > 0 || n_vis > 0) ? max(0, min(a.rows_per_split, n_rows - r_begin)) : 0;
+  const int ntiles = (nrows + 15) / 16;
+
+  // ---- trip 2: the block table gives each staged row's address (the kv or the window cache,
+  // picked by pointer, one load either way)
+  uint32_t rw[RPT];
+  bool use[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int i = tid + kWThreads * u;
+    const int pos = r_begin + min(i, max(nrows - 1, 0));
+    const bool is_kv = pos < n_c;
+    use[u] = i < nrows && (!is_kv || (ent[u] >= 0 && ent[u] < n_vis));
+    const int64_t lrow = is_kv ? (int64_t)min(max(ent[u], 0), max(n_vis - 1, 0))
+                               : (int64_t)max(t - n_w + 1 + (pos - n_c), 0);
+    const int32_t* bt = is_kv ? a.kv.bt : a.swa.bt;
+    const int stride = is_kv ? a.kv.bt_stride : a.swa.bt_stride;
+    const int shift = is_kv ? a.kv.rpb_shift : a.swa.rpb_shift;
+    const int32_t blk = bt[(int64_t)b * stride + (int32_t)(lrow >> shift)];
+    const uint32_t prow = ((uint32_t)blk << shift) + (uint32_t)(lrow & ((1 << shift) - 1));
+    rw[u] = prow | (is_kv ? 0u : 0x80000000u);
+  }
+  // the first row of the split stands in for padding rows (finite data, masked)
+  const uint32_t safe = (uint32_t)__shfl((int)rw[0], 0) | 0x40000000u;
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) row_sh[tid + kWThreads * u] = use[u] ? rw[u] : safe;
+  barrier_lds();
+
+  const int ntw = ntiles > wv ? (ntiles - wv + kWWaves - 1) / kWWaves : 0;  // this wave's tiles
+  // identity B operands of the transposing MFMAs: B[k][n] = 1 where k = n (I_lo: dims 0-15 of
+  // a k-step) or k = n + 16 (I_hi: dims 16-31); lane (n, g) holds B[8 g .. 8 g + 7][n]
+  bf16x8 id_lo, id_hi;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    id_lo[e] = (__bf16)(8 * lg + e == ln ? 1.0f : 0.0f);
+    id_hi[e] = (__bf16)(8 * lg + e == ln + 16 ? 1.0f : 0.0f);
+  }
+  // 16 rows as lane (row ln, group lg) holds them: dims 32 ks + 8 lg .. +7 for every k-step
+  struct Tile { uint4 d[NKS]; };
+  // The rows come through LDS: loaded straight into the operand layout every load instruction
+  // would touch 64 bytes of each of 16 rows, a pattern the vector L1 serves at ~15 bytes per
+  // clock per compute unit; LDS DMA instructions that each move whole 128-byte lines of 8 rows,
+  // read back with ds_read_b128, run at ~40.  Instruction (rg, c) of the wave's tile j moves
+  // line c of rows 8 rg .. 8 rg + 7: lane l fetches row 8 rg + l / 8, 16-byte piece
+  // (l % 8) ^ (l / 8) of the line, which the DMA writes at 16 l -- piece p of row r lands at
+  // piece p ^ (r % 8) of the row's 128-byte place, so the operand reads fall on distinct banks.
+  // Past the wave's last tile (or with none at all) the first row of the main cache is moved.
+  lds_char* slots = (lds_char*)slot_sh + 2 * wv * SLOT;  // tile j goes to slot j % 2
+  const char* swabase = (const char*)a.swa.rows;
+  auto dma_tile = [&](int j) __attribute__((always_inline)) {
+    const int tile = wv + kWWaves * max(min(j, ntw - 1), 0);
+    lds_char* slot = slots + (j & 1) * SLOT;
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      const uint32_t w = row_sh[16 * tile + 8 * rg + (lane >> 3)];
+      const char* base = (w & 0x80000000u) ? swabase : kvbase;
+      const char* row = (j < ntw ? base + (int64_t)(w & 0x3FFFFFFFu) * RB : kvbase) + 16 * ((lane & 7) ^ (lane >> 3));
+#pragma unroll
+      for (int c = 0; c < NL; ++c)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(row + 128 * c),
+                                         (__attribute__((address_space(3))) void*)(slot + (rg * NL + c) * 1024),
+                                         16, 0, 0);
+    }
+  };
+  auto read_tile = [&](int j, Tile& tl) __attribute__((always_inline)) {
+    const lds_char* slot = slots + (j & 1) * SLOT;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int byte = 64 * ks + 16 * lg;  // of row ln
+      const int p = (byte >> 4) & 7;
+      const int off = ((ln >> 3) * NL + (byte >> 7)) * 1024 + (ln & 7) * 128 + ((p ^ (ln & 7)) << 4);
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(slot + off);
+      tl.d[ks] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  };
+
+  f32x4 o[NDT];  // O^T: dim tile 16 dt .. +15 x 16 heads
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_run = 0.f;  // per head: reference exponent (log2 units), sum of P
+
+  // QK, softmax and P (bf16 hi + lo) of the wave's tile j, rows in tl.  The transposes of the
+  // first kLead k-steps are issued first, so the matrix cores run them during the softmax.
+  constexpr int kLead = 3;
+  auto transposes = [&](const Tile& tl, int ks, f32x4 (&t)[2]) __attribute__((always_inline)) {
+    const bf16x8 rk = __builtin_bit_cast(bf16x8, tl.d[ks]);
+    t[0] = mfma16x16x32(rk, id_lo, f32x4{0.f, 0.f, 0.f, 0.f});
+    t[1] = mfma16x16x32(rk, id_hi, f32x4{0.f, 0.f, 0.f, 0.f});
+  };
+  auto qk_softmax = [&](int j, const Tile& tl, f32x4 (&tq)[kLead][2]) __attribute__((always_inline)) -> bf16x8 {
+    const int row0 = 16 * (wv + kWWaves * j);
+    f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      acc2[ks & 1] = mfma16x16x32(__builtin_bit_cast(bf16x8, tl.d[ks]), qb[ks], acc2[ks & 1]);
+    const f32x4 sacc = acc2[0] + acc2[1];
+#pragma unroll
+    for (int ks = 0; ks < kLead; ++ks) transposes(tl, ks, tq[ks]);
+    const uint4 rw4 = *(const uint4*)&row_sh[row0 + 4 * lg];
+    const uint32_t rws[4] = {rw4.x, rw4.y, rw4.z, rw4.w};
+    float z[4];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      z[jj] = (rws[jj] & 0x40000000u) ? -INFINITY : sacc[jj] * a.sm_scale2;
+      mloc = fmaxf(mloc, z[jj]);
+    }
+    mloc = rows_reduce(mloc, [](float x, float y) { return fmaxf(x, y); });
+    // the reference moves only when a tile's maximum exceeds it by more than kSlack
+    const bool move = mloc > m_ref + kSlack;
+    if (__ballot(move)) {
+      const float m_new = move ? mloc : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    }
+    bf16x8 pb;  // k-slots 0-3: P_hi of rows 4 lg + j, 4-7: P_lo of the same rows
+    float psum = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float p = z[jj] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[jj] - m_ref);
+      psum += p;
+      const __bf16 hi = (__bf16)p;
+      pb[jj] = hi;
+      pb[4 + jj] = (__bf16)(p - (float)hi);
+    }
+    l_run += psum;
+    return pb;
+  };
+  // O^T += [V^T | V^T] . [P_hi ; P_lo]; V^T of dims 32 ks .. +15 and 32 ks + 16 .. +31 from the
+  // transposing MFMAs (lane (dim n, group g): rows 4 g .. 4 g + 3, exact in bf16), issued kLead
+  // k-steps ahead of their use, so the conversions (VALU) of one k-step run while the matrix
+  // cores work on later ones: per k-step two transposes, eight VALU, two PV MFMAs.
+  auto pv = [&](const Tile& tl, f32x4 (&tq)[kLead][2], const bf16x8& pb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const f32x4 t0 = tq[ks % kLead][0], t1 = tq[ks % kLead][1];
+      if (ks + kLead < NKS) transposes(tl, ks + kLead, tq[ks % kLead]);
+      bf16x8 vlo, vhi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vlo[e] = vlo[4 + e] = (__bf16)t0[e];
+        vhi[e] = vhi[4 + e] = (__bf16)t1[e];
+      }
+      o[2 * ks] = mfma16x16x32(vlo, pb, o[2 * ks]);
+      o[2 * ks + 1] = mfma16x16x32(vhi, pb, o[2 * ks + 1]);
+      if (ks + kLead < NKS) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+  };
+
+  // The wave's own wait counts order its DMA and its LDS reads (no other load of this wave is in
+  // flight in the loop): with tile j + 1's DMA issued after tile j's, tile j has landed once at
+  // most that many loads are outstanding, and its slot may take tile j + 2 once the operand
+  // reads are back (lgkmcnt 0).
+  constexpr int kVmcnt0 = 0x0F70, kLgkmcnt0 = 0xC07F;
+  constexpr int kVmcntTile = 0x0F70 | ((2 * NL) & 15) | (((2 * NL) >> 4) << 14);  // vmcnt(2 NL)
+  dma_tile(0);
+  dma_tile(1);
+  for (int j = 0; j < ntw; ++j) {
+    Tile cur;
+    __builtin_amdgcn_s_waitcnt(kVmcntTile);
+    read_tile(j, cur);
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+    dma_tile(j + 2);
+    f32x4 tq[kLead][2];
+    const bf16x8 pb = qk_softmax(j, cur, tq);
+    pv(cur, tq, pb);
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);  // (the DMAs past the end) before the slots are reused
+
+  // ---- merge the waves: per head M = max_w m_w, f_w = 2^(m_w - M); waves 2 and 3 put f O in
+  // LDS, waves 0 and 1 add theirs to it in registers, wave 1 passes its sum to wave 0, and wave 0
+  // stores (f0 O0 + f2 O2) + (f1 O1 + f3 O3) from registers
+  const float l_w = rows_reduce(l_run, [](float x, float y) { return x + y; });
+  if (lg == 0) {
+    ml_sh[wv][ln][0] = m_ref;
+    ml_sh[wv][ln][1] = l_w;
+  }
+  __syncthreads();  // also: every wave is done with its slot (the merge buffers alias them)
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWWaves; ++w) M = fmaxf(M, ml_sh[w][ln][0]);
+  const float f = m_ref == -INFINITY ? 0.f : exp2f(m_ref - M);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] *= f;
+  float (*mb)[MROW] = reinterpret_cast<float (*)[MROW]>(slot_sh);  // rows 0-15: A, 16-31: B
+  float* my = &mb[16 * (wv & 1) + ln][4 * lg];
+  // o += the 16 x DIM rows at src (this lane's part), six tiles of loads in flight at a time
+  auto add_from = [&](const float* src) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < NDT; c += 6) {
+      float4 v[6];
+#pragma unroll
+      for (int e = 0; e < 6; ++e)
+        if (c + e < NDT) v[e] = *(const float4*)(src + 16 * (c + e));
+#pragma unroll
+      for (int e = 0; e < 6; ++e)
+        if (c + e < NDT) o[c + e] += f32x4{v[e].x, v[e].y, v[e].z, v[e].w};
+    }
+  };
+  if (wv >= 2) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *(float4*)(my + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  }
+  __syncthreads();
+  if (wv < 2) add_from(my);
+  if (wv == 1) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *(float4*)(my + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  }
+  __syncthreads();
+  if (wv == 0) add_from(&mb[16 + ln][4 * lg]);
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWWaves; ++w)
+    if (ml_sh[w][ln][0] != -INFINITY) L += exp2f(ml_sh[w][ln][0] - M) * ml_sh[w][ln][1];
+  if (a.direct) {
+    // one split: the finished rows (normalised, R_t^{-1}, lse) by every thread through LDS, with
+    // the operations attn_merge applies to a single split
+    if (wv == 0) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *(float4*)(my + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    }
+    __syncthreads();
+    store_head_rows<DIM, kWThreads>(a, s, hg, qi, mb, hml_sh, M, L);
+    return;
+  }
+  if (wv != 0) return;
+  // lane (head ln, group lg) holds dims 16 dt + 4 lg .. +3 of the split's partial row
+  const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg + ln;
+  float* dst = a.part_o + pbase * DIM;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+    *(float4*)(dst + 16 * dt + 4 * lg) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  if (lg == 0) {
+    a.part_ml[pbase * 2 + 0] = M;
+    a.part_ml[pbase * 2 + 1] = L;
+  }
+}
+
 struct MergeArgs {
   int n_heads, splits, hgp, dim, rope_dims;
   const int32_t* q_pos;
@@ -994,6 +1328,16 @@ template <int DT>
 void launch_q(const Args& args, int qdt, int dim, dim3 grid, hipStream_t stream) {
   if (qdt == CSA_BF16) launch_dim<DT, CSA_BF16>(args, dim, grid, stream);
   else launch_dim<DT, CSA_F32>(args, dim, grid, stream);
+}
+
+template <>
+void launch_q<CSA_BF16>(const Args& args, int qdt, int dim, dim3 grid, hipStream_t stream) {
+  if (qdt == CSA_BF16) {
+    if (dim == 576) hipLaunchKernelGGL((attn_partial_w<576>), grid, dim3(kWThreads), 0, stream, args);
+    else hipLaunchKernelGGL((attn_partial_w<512>), grid, dim3(kWThreads), 0, stream, args);
+  } else {
+    launch_dim<CSA_BF16, CSA_F32>(args, dim, grid, stream);
+  }
 }
 
 template <>
