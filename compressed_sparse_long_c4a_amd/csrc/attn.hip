@@ -181,6 +181,47 @@ __device__ __forceinline__ bool wg_coords(const Args& a, int& s, int& hg, int& q
   return true;
 }
 
+// The same for workgroups of four head groups (head-group quad hq).
+__device__ __forceinline__ bool wg_coords_hq(const Args& a, int& s, int& hq, int& qi) {
+  const int id = blockIdx.x, x = id & 7, slot = id >> 3;
+  const int G = a.hgp / 64;
+  const int u = 8 * (slot / G) + x;
+  if (u >= a.units) return false;
+  hq = slot - G * (slot / G);
+  s = u % a.splits;
+  qi = u / a.splits;
+  return true;
+}
+
+// One wave writes its 16 head rows (in wb, LDS, written by this wave) finished: O / L, R_t^{-1}
+// on the last rope_dims dims, the lse -- the operations attn_merge applies to a single split.
+// Lane (head ln, any group) passes head ln's (M, L).
+template <int DIM>
+__device__ __forceinline__ void store_head_rows_wave(const Args& a, int hg, int qi, const float (*wb)[DIM + 4],
+                                                     float M, float L) {
+  const int lane = threadIdx.x & 63;
+  const int t = a.q_pos[qi];
+  const int rope0 = DIM - a.rope_dims;
+  for (int i = lane; i < 16 * DIM / 4; i += 64) {
+    const int h = i / (DIM / 4), d = 4 * (i - h * (DIM / 4));
+    const int hq = 16 * hg + h;
+    const float Lh = __shfl(L, h);
+    if (hq >= a.n_heads) continue;
+    const float inv = Lh > 0.f ? 1.0f / Lh : 0.f;
+    const float4 v = *(const float4*)&wb[h][d];
+    float4 r = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+    if (d >= rope0) {  // pairs (d, d+1) and (d+2, d+3) by -t theta_i
+      float c0, s0, c1, s1;
+      rope_cos_sin(-(double)t, a.rope.theta[(d - rope0) / 2], c0, s0);
+      rope_cos_sin(-(double)t, a.rope.theta[(d - rope0) / 2 + 1], c1, s1);
+      r = make_float4(r.x * c0 - r.y * s0, r.x * s0 + r.y * c0, r.z * c1 - r.w * s1, r.z * s1 + r.w * c1);
+    }
+    *(float4*)(a.out + ((int64_t)qi * a.n_heads + hq) * DIM + d) = r;
+  }
+  if (a.lse && lane < 16 && 16 * hg + lane < a.n_heads)
+    a.lse[(int64_t)qi * a.n_heads + 16 * hg + lane] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
 __device__ __forceinline__ bf16x8 f32x8_to_bf16(const float* x) {
   bf16x8 r;
 #pragma unroll
@@ -892,7 +933,7 @@ __global__ __launch_bounds__(kF8Threads) void attn_partial_fp8(Args a) {
 constexpr int kWWaves = 4;
 constexpr int kWThreads = 64 * kWWaves;
 static_assert(kRowsPerSplit % kWThreads == 0 && kRowsPerSplit % (16 * kWWaves) == 0, "split size");
-template <int DIM>
+template <int DIM, bool HG4>
 __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
   constexpr int NKS = DIM / 32;         // k-steps of a row
   constexpr int NDT = DIM / 16;         // 16-dim output tiles
@@ -909,9 +950,14 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
   __shared__ float ml_sh[kWWaves][16][2];
 
   int s, hg, qi;
-  if (!wg_coords(a, s, hg, qi)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if constexpr (HG4) {  // the workgroup's four waves take head groups 4 q .. 4 q + 3
+    if (!wg_coords_hq(a, s, hg, qi)) return;
+    hg = 4 * hg + wv;
+  } else {
+    if (!wg_coords(a, s, hg, qi)) return;
+  }
   const int ln = lane & 15, lg = lane >> 4;
   const int H = a.n_heads;
   const char* kvbase = (const char*)a.kv.rows;
@@ -974,7 +1020,9 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
   for (int u = 0; u < RPT; ++u) row_sh[tid + kWThreads * u] = use[u] ? rw[u] : safe;
   barrier_lds();
 
-  const int ntw = ntiles > wv ? (ntiles - wv + kWWaves - 1) / kWWaves : 0;  // this wave's tiles
+  // this wave's tiles: every tile of the split (HG4), else tiles wv, wv + 4, ...
+  const int ntw = HG4 ? ntiles : (ntiles > wv ? (ntiles - wv + kWWaves - 1) / kWWaves : 0);
+  auto tile_of = [&](int j) { return HG4 ? j : wv + kWWaves * j; };
   // identity B operands of the transposing MFMAs: B[k][n] = 1 where k = n (I_lo: dims 0-15 of
   // a k-step) or k = n + 16 (I_hi: dims 16-31); lane (n, g) holds B[8 g .. 8 g + 7][n]
   bf16x8 id_lo, id_hi;
@@ -996,7 +1044,7 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
   lds_char* slots = (lds_char*)slot_sh + 2 * wv * SLOT;  // tile j goes to slot j % 2
   const char* swabase = (const char*)a.swa.rows;
   auto dma_tile = [&](int j) __attribute__((always_inline)) {
-    const int tile = wv + kWWaves * max(min(j, ntw - 1), 0);
+    const int tile = tile_of(max(min(j, ntw - 1), 0));
     lds_char* slot = slots + (j & 1) * SLOT;
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
@@ -1037,7 +1085,7 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
     t[1] = mfma16x16x32(rk, id_hi, f32x4{0.f, 0.f, 0.f, 0.f});
   };
   auto qk_softmax = [&](int j, const Tile& tl, f32x4 (&tq)[kLead][2]) __attribute__((always_inline)) -> bf16x8 {
-    const int row0 = 16 * (wv + kWWaves * j);
+    const int row0 = 16 * tile_of(j);
     f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -1120,6 +1168,32 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
     pv(cur, tq, pb);
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // (the DMAs past the end) before the slots are reused
+
+  if constexpr (HG4) {
+    // each wave holds the whole result of its head group: no merge
+    const float L = rows_reduce(l_run, [](float x, float y) { return x + y; });
+    const int hq = 16 * hg + ln;
+    if (a.direct) {
+      // the finished rows through the wave's own slots (free now), one wave, the operations
+      // of attn_merge for a single split
+      float (*wb)[MROW] = reinterpret_cast<float (*)[MROW]>(slot_sh + 2 * wv * SLOT);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *(float4*)&wb[ln][16 * dt + 4 * lg] = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+      store_head_rows_wave<DIM>(a, hg, qi, wb, m_ref, L);
+      return;
+    }
+    const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + hq;
+    float* dst = a.part_o + pbase * DIM;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *(float4*)(dst + 16 * dt + 4 * lg) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (lg == 0) {
+      a.part_ml[pbase * 2 + 0] = m_ref;
+      a.part_ml[pbase * 2 + 1] = L;
+    }
+    return;
+  }
 
   // ---- merge the waves: per head M = max_w m_w, f_w = 2^(m_w - M); waves 2 and 3 put f O in
   // LDS, waves 0 and 1 add theirs to it in registers, wave 1 passes its sum to wave 0, and wave 0
@@ -1333,8 +1407,19 @@ void launch_q(const Args& args, int qdt, int dim, dim3 grid, hipStream_t stream)
 template <>
 void launch_q<CSA_BF16>(const Args& args, int qdt, int dim, dim3 grid, hipStream_t stream) {
   if (qdt == CSA_BF16) {
-    if (dim == 576) hipLaunchKernelGGL((attn_partial_w<576>), grid, dim3(kWThreads), 0, stream, args);
-    else hipLaunchKernelGGL((attn_partial_w<512>), grid, dim3(kWThreads), 0, stream, args);
+    // one split per query with head groups in fours and enough queries to fill the chip
+    // (chunked prefill): each wave takes one head group over all of the query's rows, so the
+    // four waves share the row addresses and no merge is needed; otherwise the waves split the
+    // rows of one head group
+    const bool hg4 = args.splits == 1 && args.hgp % 64 == 0 && (int64_t)args.units * (args.hgp / 64) >= 256;
+    if (hg4) {
+      const dim3 g4((unsigned)(8 * (int64_t)(args.hgp / 64) * ((args.units + 7) / 8)));
+      if (dim == 576) hipLaunchKernelGGL((attn_partial_w<576, true>), g4, dim3(kWThreads), 0, stream, args);
+      else hipLaunchKernelGGL((attn_partial_w<512, true>), g4, dim3(kWThreads), 0, stream, args);
+    } else {
+      if (dim == 576) hipLaunchKernelGGL((attn_partial_w<576, false>), grid, dim3(kWThreads), 0, stream, args);
+      else hipLaunchKernelGGL((attn_partial_w<512, false>), grid, dim3(kWThreads), 0, stream, args);
+    }
   } else {
     launch_dim<CSA_BF16, CSA_F32>(args, dim, grid, stream);
   }
