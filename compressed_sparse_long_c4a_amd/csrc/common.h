@@ -223,6 +223,20 @@ __device__ __forceinline__ T rows_reduce(T v, Op op) {
   return op(from_u32<T>(b[0]), from_u32<T>(b[1]));
 }
 
+// Four row sums at once: lane (l mod 16, row r) gets the sum of v_r over the four 16-lane rows
+// at lane l mod 16 (three swaps and three adds, where four rows_reduce calls take eight and
+// eight).  permlane16_swap(x, y) leaves x = [x0 y0 x2 y2] and y = [x1 y1 x3 y3] (by rows), so
+// x + y holds the row pairs (0, 1) and (2, 3) of both; permlane32_swap(a, b) leaves
+// a = [a0 a1 b0 b1] and b = [a2 a3 b2 b3], and a + b completes the sums.
+__device__ __forceinline__ float rows_sum4(float v0, float v1, float v2, float v3) {
+  const auto p = __builtin_amdgcn_permlane16_swap(as_u32(v0), as_u32(v1), false, false);
+  const float a = from_u32<float>(p[0]) + from_u32<float>(p[1]);  // [v0 01, v1 01, v0 23, v1 23]
+  const auto q = __builtin_amdgcn_permlane16_swap(as_u32(v2), as_u32(v3), false, false);
+  const float b = from_u32<float>(q[0]) + from_u32<float>(q[1]);  // [v2 01, v3 01, v2 23, v3 23]
+  const auto r = __builtin_amdgcn_permlane32_swap(as_u32(a), as_u32(b), false, false);
+  return from_u32<float>(r[0]) + from_u32<float>(r[1]);
+}
+
 // DPP move of src within 16-lane rows (lanes without a source read 0).
 template <int CTRL, typename T>
 __device__ __forceinline__ T dpp(T v) {

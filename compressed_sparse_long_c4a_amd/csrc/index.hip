@@ -62,10 +62,10 @@ __device__ __forceinline__ int query_entries(const int32_t* q_pos, int qi, int n
   return min((t + 1) / 4, n_max);
 }
 
-// Wave 0 of a 256-thread block scans a 256-bin histogram from the top bin down and finds the
-// bin holding the need-th largest element.  Writes {bin, count in higher bins} to out[0..1].
+// One wave scans a 256-bin histogram from the top bin down and finds the bin holding the
+// need-th largest element.  Writes {bin, count in higher bins} to out[0..1].
 __device__ void pick_bin_wave0(const uint32_t* hist, int need, int* out) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   // lane l owns bins 255-4l .. 252-4l (descending)
   uint32_t hb[4];
   uint32_t local = 0;
@@ -194,6 +194,39 @@ __device__ void emit_chunk(const ScoreArgs& a, int qi, int chunk, int nval, uint
 // the four waves cover the four 64-entry blocks 4 gi .. 4 gi + 3 together.  The physical ids
 // of the chunk's blocks are fetched once; key loads run one group ahead of the MFMA work
 // (two register buffers), so a wave always has a group of keys in flight.
+// One lane's share of a 16-key tile (its NW 16-byte words, as load_group reads them) as the
+// four bf16 B operands of the k-steps.  fp8: words 0 and 1 hold bytes 16 lg .. 16 lg + 15 and
+// 64 + 16 lg .. 64 + 16 lg + 15 of the key; fp4: word ks holds dims 32 lg + 8 ks .. +7, in scale
+// block 2 lg + ks / 2 (the block scale, a power of two, is applied in the conversion: exact in
+// bf16); bf16: word ks is the operand.
+template <int KEY_DT, int NW>
+__device__ __forceinline__ void key_operands(const uint4 (&raw)[NW], uint32_t sc4, bf16x8 (&kb)[4]) {
+  if constexpr (KEY_DT == CSA_FP8_E4M3) {
+    const uint32_t wd[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kb[ks] = fp8x8_to_bf16x8(wd[2 * ks], wd[2 * ks + 1]);
+  } else if constexpr (KEY_DT == CSA_FP4_E2M1) {
+    const uint32_t wd[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+    const float s0 = e8m0_to_f32(sc4 & 0xFFu), s1 = e8m0_to_f32(sc4 >> 8);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kb[ks] = fp4x8_to_bf16x8(wd[ks], ks < 2 ? s0 : s1);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+  }
+}
+
+// A operand of head tile mt, k-step ks: lane (head ln, group lg) holds the dims its key lanes
+// hold for that k-step (fp8: 64 (ks / 2) + 16 lg + 8 (ks % 2) + 0..7, the eight codes of half a
+// 16-byte load; fp4: 32 lg + 8 ks + 0..7, one word of the lane's load; bf16: 32 ks + 8 lg +
+// 0..7, one 16-byte load).
+template <int KEY_DT>
+__device__ __forceinline__ int q_operand_dim(int ks, int lg) {
+  return KEY_DT == CSA_FP8_E4M3   ? 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1)
+         : KEY_DT == CSA_FP4_E2M1 ? 32 * lg + 8 * ks
+                                  : 32 * ks + 8 * lg;
+}
+
 template <int KEY_DT>
 struct KeyGroup {
   static constexpr int NW = KEY_DT == CSA_FP8_E4M3 ? 2 : KEY_DT == CSA_FP4_E2M1 ? 1 : 4;  // 16-byte words per lane per tile
@@ -287,22 +320,7 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       bf16x8 kb[4];
-      if constexpr (KEY_DT == CSA_FP8_E4M3) {
-        const uint32_t wd[8] = {kg.raw[u][0].x, kg.raw[u][0].y, kg.raw[u][0].z, kg.raw[u][0].w,
-                                kg.raw[u][1].x, kg.raw[u][1].y, kg.raw[u][1].z, kg.raw[u][1].w};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb[ks] = fp8x8_to_bf16x8(wd[2 * ks], wd[2 * ks + 1]);
-      } else if constexpr (KEY_DT == CSA_FP4_E2M1) {
-        // word ks holds dims 32 lg + 8 ks .. +7, in scale block 2 lg + ks / 2; the block scale
-        // is applied in the conversion (a power of two: exact in bf16)
-        const uint32_t wd[4] = {kg.raw[u][0].x, kg.raw[u][0].y, kg.raw[u][0].z, kg.raw[u][0].w};
-        const float s0 = e8m0_to_f32(kg.sc4[u] & 0xFFu), s1 = e8m0_to_f32(kg.sc4[u] >> 8);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb[ks] = fp4x8_to_bf16x8(wd[ks], ks < 2 ? s0 : s1);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb[ks] = __builtin_bit_cast(bf16x8, kg.raw[u][ks]);
-      }
+      key_operands<KEY_DT, NW>(kg.raw[u], kg.sc4[u], kb);
       // k-step outer, head tile inner: consecutive MFMAs are independent
       f32x4 acc[HT];
 #pragma unroll
@@ -336,17 +354,12 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
     *(uint4*)&q_sh[(16 * p + (threadIdx.x >> 4)) * QROW + 8 * (threadIdx.x & 15)] = qv[p];
   if (threadIdx.x < 16 * HT) w_sh[threadIdx.x] = wv_h;
   __syncthreads();
-  // A operand: lane (head ln of tile mt, group lg) holds the dims its key lanes hold for
-  // k-step ks (fp8: 64 (ks / 2) + 16 lg + 8 (ks % 2) + 0..7, the eight codes of half a
-  // 16-byte load; fp4: 32 lg + 8 ks + 0..7, one word of the lane's load; bf16: 32 ks + 8 lg +
-  // 0..7, one 16-byte load).
+  // A operands (the dims each key lane holds, q_operand_dim)
 #pragma unroll
   for (int mt = 0; mt < HT; ++mt) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int d0 = KEY_DT == CSA_FP8_E4M3   ? 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1)
-                     : KEY_DT == CSA_FP4_E2M1 ? 32 * lg + 8 * ks
-                                              : 32 * ks + 8 * lg;
+      const int d0 = q_operand_dim<KEY_DT>(ks, lg);
       qa[mt][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)&q_sh[(16 * mt + ln) * QROW + d0]);
     }
     const float4 w4 = *(const float4*)&w_sh[16 * mt + 4 * lg];
@@ -424,6 +437,252 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
     bound = lo + ((uint32_t)misc[0] << shift);
   }
   emit_chunk(a, qi, chunk, nold_loc, bound, sc_sh, (int*)hist);
+}
+
+// ---- Query-tiled MFMA score kernel, for calls whose sequences bring many queries (a chunked
+// prefill).  There the chunk's keys are shared by all queries of the sequence, and with one
+// query per workgroup (index_score_mfma) every query loads and converts them again: the vector
+// L1 (~15 bytes per clock per compute unit in the operand layout) and the conversion VALU
+// bound the kernel.  Here a workgroup scores one chunk for kQT consecutive queries of one
+// sequence, one query per wave with all of its heads in registers.  In each group of kGT
+// tiles (16 entries each) wave w loads and converts tiles w and w + 4 only, and writes them
+// to LDS in the B-operand layout (one 16-byte word per lane and k-step); every wave reads all
+// kGT back.  Two LDS buffers: group g + 1 is converted while g is computed, one LDS barrier
+// per group.  The head sums of four tiles are completed together (rows_sum4), which leaves
+// lane l with entry 64 h + l of the group's half h: the scores leave in full lines as each group
+// ends and also stay in the wave's registers.  Each wave then finishes its query alone and
+// emits its candidates in entry order by ballots (same bound and output as index_score_mfma).
+constexpr int kQT = 4;   // queries per workgroup (one per wave)
+constexpr int kGT = 8;   // tiles per group
+
+// Workgroup t of the query-tiled grid -> sequence b and its queries q0 .. q0 + nq - 1 (tiles
+// of kQT consecutive queries inside each sequence, in sequence order); false past the last tile.
+__device__ bool query_tile(const int32_t* cu_q, int batch, int t, int& b, int& q0, int& nq) {
+  const int lane = threadIdx.x & 63;
+  int before = 0;  // tiles of the sequences before this block of 64
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int bb = b0 + lane;
+    int s0 = 0, s1 = 0;
+    if (bb < batch) {
+      s0 = cu_q[bb];
+      s1 = cu_q[bb + 1];
+    }
+    const int tiles = (s1 - s0 + kQT - 1) / kQT;
+    const int incl = wave_incl_scan(tiles) + before;
+    const unsigned long long hit = __ballot(bb < batch && t < incl);
+    if (hit) {
+      const int f = __ffsll(hit) - 1;
+      b = b0 + f;
+      const int first_tile = __builtin_amdgcn_readlane(incl - tiles, f);
+      q0 = __builtin_amdgcn_readlane(s0, f) + (t - first_tile) * kQT;
+      nq = min(kQT, __builtin_amdgcn_readlane(s1, f) - q0);
+      return true;
+    }
+    before = __builtin_amdgcn_readlane(incl, 63);
+  }
+  return false;
+}
+
+// The wave's LDS operations done (the wave's own ordering of its LDS phases; no barrier).
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int KEY_DT, int HT>
+__global__ __launch_bounds__(256) void index_score_qt(ScoreArgs a) {
+  using KG = KeyGroup<KEY_DT>;
+  constexpr int NW = KG::NW;
+  constexpr int NG = C / (16 * kGT);  // groups per chunk
+  constexpr int NS = C / 64;          // score slots per lane
+  __shared__ __attribute__((aligned(16))) uint4 kb_sh[2][kGT][4][64];
+  __shared__ float ksc_sh[2][kGT][16];
+  __shared__ uint32_t hist_sh[kQT][256];
+  __shared__ int misc_sh[kQT][4];
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const int chunk = blockIdx.x;
+  int b = 0, q0 = 0, nq = 0;
+  if (!query_tile(a.cu_q, a.batch, blockIdx.y, b, q0, nq)) return;
+  const int64_t j0 = (int64_t)chunk * C;
+  const int qi = q0 + wv;
+  const bool has_q = wv < nq;
+  const int H = a.n_heads;
+  // Loads that need only the tile are issued together: the wave's query and head weights
+  // (straight into the operand layout), the tile's positions and the chunk's physical block
+  // ids (lane i: block i, up to the end of the block-table row; ids past the chunk's entries
+  // are never used).
+  bf16x8 qa[HT][4];
+  float wt[HT][4];
+  const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)qi * H * 128;
+#pragma unroll
+  for (int mt = 0; mt < HT; ++mt) {
+    const int h = 16 * mt + ln;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qa[mt][ks] = __builtin_bit_cast(
+          bf16x8, has_q && h < H ? load_global16(qrow + (int64_t)h * 128 + q_operand_dim<KEY_DT>(ks, lg))
+                                 : make_uint4(0, 0, 0, 0));
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int hw = 16 * mt + 4 * lg + jj;
+      wt[mt][jj] = has_q && hw < H ? a.w[(int64_t)qi * H + hw] : 0.f;
+    }
+  }
+  const int64_t bt_left = (int64_t)a.cache.bt_stride - (j0 >> 6);
+  const int32_t* btrow = a.cache.bt + (int64_t)b * a.cache.bt_stride + (j0 >> 6);
+  const int32_t my_blk = lane < min((int64_t)C / 64, bt_left) ? btrow[lane] : 0;
+  // entries each query of the tile sees; the keys are loaded up to the largest
+  int n_w = 0, n_hi = 0;
+#pragma unroll
+  for (int i = 0; i < kQT; ++i) {
+    const int ni = i < nq ? query_entries(a.q_pos, q0 + i, a.n_max) : 0;
+    n_hi = max(n_hi, ni);
+    n_w = i == wv ? ni : n_w;
+  }
+  if (j0 >= n_hi) return;  // (uniform over the workgroup)
+  const int nloc = (int)min((int64_t)C, n_hi - j0);
+  const int nloc_w = (int)max((int64_t)0, min((int64_t)C, n_w - j0));  // 0: the wave only converts
+  const int ntiles = (nloc + 15) >> 4;
+  const int ngroups = (ntiles + kGT - 1) / kGT;
+
+  // the wave's two tiles of group g (tiles past the chunk's end repeat its last one; entries
+  // past it read its last entry)
+  struct Raw {
+    uint4 raw[2][NW];
+    uint32_t sc4[2];
+    float scale;  // fp8, lane (e, u < 2): scale of entry e of the wave's tile u
+  };
+  auto load_tiles = [&](int g, Raw& r) {
+    int64_t prow_s = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tile = min(kGT * g + 4 * u + wv, ntiles - 1);
+      const int eloc = min(tile * 16 + ln, nloc - 1);
+      const int blk = __builtin_amdgcn_readlane(my_blk, tile >> 2);
+      const int64_t prow = ((int64_t)blk << 6) + (eloc & 63);
+      prow_s = lg == u ? prow : prow_s;
+      const uint8_t* src = (const uint8_t*)a.cache.rows + prow * KG::ROW + 16 * lg;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) r.raw[u][i] = load_global16(src + 64 * i);
+      if constexpr (KEY_DT == CSA_FP4_E2M1) r.sc4[u] = ((const uint16_t*)a.cache.scales)[prow * 4 + lg];
+      else r.sc4[u] = 0u;
+    }
+    r.scale = KEY_DT == CSA_FP8_E4M3 ? a.cache.scales[prow_s] : 1.f;
+  };
+  auto store_tiles = [&](int buf, const Raw& r) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bf16x8 kb[4];
+      key_operands<KEY_DT, NW>(r.raw[u], r.sc4[u], kb);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kb_sh[buf][4 * u + wv][ks][lane] = __builtin_bit_cast(uint4, kb[ks]);
+    }
+    if (KEY_DT == CSA_FP8_E4M3 && lg < 2) ksc_sh[buf][4 * lg + wv][ln] = r.scale;
+  };
+
+  Raw raw;
+  load_tiles(0, raw);
+  store_tiles(0, raw);
+  if (ngroups > 1) load_tiles(1, raw);
+  barrier_lds();
+
+  // the scores leave group by group, in full lines (entries past the query's end stay inside
+  // its chunk slice), and stay in registers for the candidates: each group shifts the slots
+  // down by two and fills the top two, so after the loop slot s holds entry 64 s + lane - off
+  float* dst = a.scores + (int64_t)qi * a.n_cap + j0;
+  float sc[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) sc[i] = 0.f;
+  for (int g = 0; g < ngroups; ++g) {
+    const int buf = g & 1;
+    float sacc[kGT];  // lane (e, r): tile t's head sum over the lane's rows, entry e
+#pragma unroll
+    for (int t = 0; t < kGT; ++t) {
+      bf16x8 kb[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kb[ks] = __builtin_bit_cast(bf16x8, kb_sh[buf][t][ks][lane]);
+      f32x4 acc[HT];
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(qa[mt][ks], kb[ks], acc[mt]);
+      sacc[t] = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sacc[t] = fmaf(wt[mt][jj], relu_bits(acc[mt][jj]), sacc[t]);
+    }
+#pragma unroll
+    for (int i = 0; i < NS - 2; ++i) sc[i] = sc[i + 2];
+    // lane (e, r) of half h: the score of entry e of tile 4 h + r, i.e. entry 128 g + 64 h + lane
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float v = rows_sum4(sacc[4 * h], sacc[4 * h + 1], sacc[4 * h + 2], sacc[4 * h + 3]);
+      if constexpr (KEY_DT == CSA_FP8_E4M3) v *= ksc_sh[buf][4 * h + lg][ln];
+      sc[NS - 2 + h] = v;
+      if (nloc_w > 128 * g + 64 * h) dst[128 * g + 64 * h + lane] = v;
+    }
+    if (g + 1 < ngroups) {
+      store_tiles(buf ^ 1, raw);
+      if (g + 2 < ngroups) load_tiles(g + 2, raw);
+    }
+    barrier_lds();
+  }
+  if (nloc_w == 0) return;  // (no barrier follows)
+  if (chunk == 0 && lane == 0) a.new_from[qi] = n_w;
+  const int kc2 = chunk_quota(a.k, n_w);
+  if (kc2 == 0) return;  // the select takes every entry
+  const int off = 64 * (NS - 2 * ngroups);
+  uint32_t key[NS];
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int e = 64 * s + lane - off;
+    key[s] = e >= 0 && e < nloc_w ? f2key(sc[s]) : 0u;
+    lo = min(lo, key[s] ? key[s] : 0xFFFFFFFFu);
+    hi = max(hi, key[s]);
+  }
+  // the bound: the lower edge of the histogram bin (over the scored keys' range) that holds the
+  // kc2-th largest key; 0 (every scored entry) when the chunk holds at most kc2
+  uint32_t bound = 0u;
+  if (nloc_w > kc2) {
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    const int shift = max(0, bit_len(hi - lo) - 8);
+    uint32_t* hist = hist_sh[wv];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0u;
+    wait_lds();
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (key[s]) atomicAdd(&hist[((key[s] - lo) >> shift) & 255u], 1u);
+    wait_lds();
+    pick_bin_wave0(hist, kc2, misc_sh[wv]);
+    wait_lds();
+    bound = lo + ((uint32_t)misc_sh[wv][0] << shift);
+  }
+  // candidates in entry order: slot by slot, each taking lane's place from a ballot
+  uint2* cdst = a.cand + (int64_t)qi * a.n_cap + j0;
+  int cnt = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int e0 = 64 * s - off;  // (uniform)
+    if (e0 < 0 || e0 >= nloc_w) continue;
+    const bool take = e0 + lane < nloc_w && key[s] >= bound;
+    const unsigned long long m = __ballot(take);
+    if (take) {
+      const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      cdst[cnt + pos] = make_uint2(key[s], (uint32_t)(j0 + e0 + lane));
+      kmin = min(kmin, key[s]);
+      kmax = max(kmax, key[s]);
+    }
+    cnt += __popcll(m);
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) a.cand_info[(int64_t)qi * a.chunks + chunk] = make_int4(cnt, (int)kmin, (int)kmax, (int)bound);
 }
 
 // ---- float32 queries (any key dtype): plain per-entry dot products.
@@ -905,11 +1164,29 @@ hipError_t launch_compress_index_score(const IndexLaunch& a, const IndexWorkspac
   return hipGetLastError();
 }
 
+template <int KEY_DT>
+void launch_qt(const ScoreArgs& s, int ht, dim3 grid, hipStream_t stream) {
+  switch (ht) {
+    case 1: hipLaunchKernelGGL((index_score_qt<KEY_DT, 1>), grid, dim3(256), 0, stream, s); break;
+    case 2: hipLaunchKernelGGL((index_score_qt<KEY_DT, 2>), grid, dim3(256), 0, stream, s); break;
+    case 3: hipLaunchKernelGGL((index_score_qt<KEY_DT, 3>), grid, dim3(256), 0, stream, s); break;
+    default: hipLaunchKernelGGL((index_score_qt<KEY_DT, 4>), grid, dim3(256), 0, stream, s); break;
+  }
+}
+
 hipError_t launch_index_score(const IndexLaunch& a, const IndexWorkspace& ws, hipStream_t stream) {
   const ScoreArgs s = make_score_args(a, ws);
   const dim3 grid(ws.chunks, a.total_q);
   if (a.q_dtype == CSA_F32) {
     hipLaunchKernelGGL(index_score_f32, grid, dim3(256), 0, stream, s);
+  } else if (a.total_q >= 8 * a.batch) {
+    // many queries per sequence: workgroups of kQT queries share each chunk's keys (at most
+    // one partial tile per sequence, so batch + total_q / kQT workgroup rows cover them)
+    const int ht = (a.n_heads + 15) / 16;
+    const dim3 gq(ws.chunks, (unsigned)(((int64_t)a.total_q + (int64_t)a.batch * (kQT - 1)) / kQT));
+    if (a.idx_cache->dtype == CSA_FP8_E4M3) launch_qt<CSA_FP8_E4M3>(s, ht, gq, stream);
+    else if (a.idx_cache->dtype == CSA_FP4_E2M1) launch_qt<CSA_FP4_E2M1>(s, ht, gq, stream);
+    else launch_qt<CSA_BF16>(s, ht, gq, stream);
   } else {
     const int ht = (a.n_heads + 15) / 16;
     if (a.idx_cache->dtype == CSA_FP8_E4M3) launch_mfma<CSA_FP8_E4M3>(s, ht, grid, stream);

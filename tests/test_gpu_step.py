@@ -24,6 +24,12 @@ CASES = {
     # the partial kernel without the merge
     "c4a_fp8_chunk": dataclasses.replace(P.SMALL_DECODE, name="c4a_fp8_chunk", new_tokens=64, q_per_seq=64,
                                          n_heads=16),
+    # the query-tiled score kernel with bf16 indexer keys and 24 indexer heads (a partial head
+    # tile): ragged query counts per sequence (tiles of four queries ending early, a sequence of
+    # one query), the longest sequence spanning three chunks of entries (the last one ragged)
+    "c4a_bf16idx_ragged_prefill": C.scaled(C.C4A_PREFILL_64K, (4800, 2100, 16800), new_tokens=(9, 1, 16),
+                                           q_per_seq=(9, 1, 16), idx_dtype="bf16", idx_heads=24, k=128,
+                                           n_heads=16),
 }
 
 
