@@ -113,17 +113,8 @@ struct Args {
 template <int DIM, int NT>
 __device__ __forceinline__ void store_head_rows(const Args& a, int s, int hg, int qi,
                                                 const float (*mb)[DIM + 4], float (*hml)[2],
-                                                float Mh, float Lh,
-                                                const float (*mb2)[DIM + 4] = nullptr) {
-  // (mb2, when given, holds a second part of the same rows: the stored rows are mb + mb2)
-  auto row4 = [&](int h, int d) {
-    float4 v = *(const float4*)&mb[h][d];
-    if (mb2) {
-      const float4 w = *(const float4*)&mb2[h][d];
-      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
-    }
-    return v;
-  };
+                                                float Mh, float Lh) {
+  auto row4 = [&](int h, int d) { return *(const float4*)&mb[h][d]; };
   const int tid = threadIdx.x;
   if (a.direct) {
     if (tid < 16) {
@@ -980,10 +971,6 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, load_global16(qrow + 32 * ks));
   }
-  // Q^T lives in the accumulation registers (the MFMA reads its B operand from either file):
-  // the ordinary registers then hold O^T and leave room for the PV operands in flight
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qb[ks]));
   const int cu_v = seq_load(a.cu_q, a.batch);
   const int t = a.q_pos[qi];
   const int b = seq_pick(a.cu_q, a.batch, qi, cu_v);
@@ -1019,6 +1006,11 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
 #pragma unroll
   for (int u = 0; u < RPT; ++u) row_sh[tid + kWThreads * u] = use[u] ? rw[u] : safe;
   barrier_lds();
+  // Q^T lives in the accumulation registers (the MFMA reads its B operand from either file):
+  // the ordinary registers then hold O^T and leave room for the PV operands in flight.  (The
+  // move waits for the Q^T loads, so it comes after the later trips were issued.)
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qb[ks]));
 
   // this wave's tiles: every tile of the split (HG4), else tiles wv, wv + 4, ...
   const int ntw = HG4 ? ntiles : (ntiles > wv ? (ntiles - wv + kWWaves - 1) / kWWaves : 0);
@@ -1195,74 +1187,53 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
     return;
   }
 
-  // ---- merge the waves: per head M = max_w m_w, f_w = 2^(m_w - M); waves 2 and 3 put f O in
-  // LDS, waves 0 and 1 add theirs to it in registers, wave 1 passes its sum to wave 0, and wave 0
-  // stores (f0 O0 + f2 O2) + (f1 O1 + f3 O3) from registers
+  // ---- merge the waves: per head M = max_w m_w, f_w = 2^(m_w - M).  Each wave writes f_w O_w
+  // to its own 16 x DIM buffer (the tile slots, free now, hold exactly four), then every thread
+  // sums the four buffers for its share of the 16 heads' rows, which leave in full lines.
   const float l_w = rows_reduce(l_run, [](float x, float y) { return x + y; });
   if (lg == 0) {
     ml_sh[wv][ln][0] = m_ref;
     ml_sh[wv][ln][1] = l_w;
   }
-  __syncthreads();  // also: every wave is done with its slot (the merge buffers alias them)
+  __syncthreads();  // also: every wave is done with its slots (the merge buffers alias them)
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kWWaves; ++w) M = fmaxf(M, ml_sh[w][ln][0]);
   const float f = m_ref == -INFINITY ? 0.f : exp2f(m_ref - M);
+  typedef float WaveRows[16][MROW];
+  static_assert(kWWaves * sizeof(WaveRows) <= sizeof(slot_sh), "the slots hold the four wave buffers");
+  WaveRows* mb4 = reinterpret_cast<WaveRows*>(slot_sh);
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] *= f;
-  float (*mb)[MROW] = reinterpret_cast<float (*)[MROW]>(slot_sh);  // rows 0-15: A, 16-31: B
-  float* my = &mb[16 * (wv & 1) + ln][4 * lg];
-  // o += the 16 x DIM rows at src (this lane's part), six tiles of loads in flight at a time
-  auto add_from = [&](const float* src) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < NDT; c += 6) {
-      float4 v[6];
-#pragma unroll
-      for (int e = 0; e < 6; ++e)
-        if (c + e < NDT) v[e] = *(const float4*)(src + 16 * (c + e));
-#pragma unroll
-      for (int e = 0; e < 6; ++e)
-        if (c + e < NDT) o[c + e] += f32x4{v[e].x, v[e].y, v[e].z, v[e].w};
-    }
-  };
-  if (wv >= 2) {
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *(float4*)(my + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-  }
-  __syncthreads();
-  if (wv < 2) add_from(my);
-  if (wv == 1) {
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *(float4*)(my + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-  }
-  __syncthreads();
-  if (wv == 0) add_from(&mb[16 + ln][4 * lg]);
+  for (int dt = 0; dt < NDT; ++dt)
+    *(float4*)&mb4[wv][ln][16 * dt + 4 * lg] = make_float4(o[dt][0] * f, o[dt][1] * f, o[dt][2] * f, o[dt][3] * f);
   float L = 0.f;
 #pragma unroll
   for (int w = 0; w < kWWaves; ++w)
     if (ml_sh[w][ln][0] != -INFINITY) L += exp2f(ml_sh[w][ln][0] - M) * ml_sh[w][ln][1];
+  __syncthreads();
+  constexpr int C4 = DIM / 4;  // float4 columns of a row
+  const int64_t pbase0 = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg;
+  for (int i = tid; i < 16 * C4; i += kWThreads) {
+    const int h = i / C4, c = 4 * (i - h * C4);
+    float4 v = *(const float4*)&mb4[0][h][c];
+#pragma unroll
+    for (int w = 1; w < kWWaves; ++w) {
+      const float4 x = *(const float4*)&mb4[w][h][c];
+      v = make_float4(v.x + x.x, v.y + x.y, v.z + x.z, v.w + x.w);
+    }
+    if (a.direct) *(float4*)&mb4[0][h][c] = v;  // (the element this thread read)
+    else *(float4*)(a.part_o + (pbase0 + h) * DIM + c) = v;
+  }
   if (a.direct) {
     // one split: the finished rows (normalised, R_t^{-1}, lse) by every thread through LDS, with
     // the operations attn_merge applies to a single split
-    if (wv == 0) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        *(float4*)(my + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    }
     __syncthreads();
-    store_head_rows<DIM, kWThreads>(a, s, hg, qi, mb, hml_sh, M, L);
+    store_head_rows<DIM, kWThreads>(a, s, hg, qi, mb4[0], hml_sh, M, L);
     return;
   }
-  if (wv != 0) return;
-  // lane (head ln, group lg) holds dims 16 dt + 4 lg .. +3 of the split's partial row
-  const int64_t pbase = ((int64_t)qi * a.splits + s) * a.hgp + 16 * hg + ln;
-  float* dst = a.part_o + pbase * DIM;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-    *(float4*)(dst + 16 * dt + 4 * lg) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-  if (lg == 0) {
-    a.part_ml[pbase * 2 + 0] = M;
-    a.part_ml[pbase * 2 + 1] = L;
+  if (wv == 0 && lg == 0) {
+    a.part_ml[(pbase0 + ln) * 2 + 0] = M;
+    a.part_ml[(pbase0 + ln) * 2 + 1] = L;
   }
 }
 
