@@ -237,7 +237,7 @@ struct KeyGroup {
 };
 
 template <int KEY_DT, int HT>
-__global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
+__global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_mfma(ScoreArgs a) {
   constexpr int QROW = 136;  // bf16 per LDS query row (padded: rows start 16 bytes apart mod 256)
   __shared__ __attribute__((aligned(16))) float sc_sh[C];
   __shared__ __attribute__((aligned(16))) uint16_t q_sh[HT * 16 * QROW];
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
 
   uint32_t lane_keys[C / 256];  // the lane's key of each group: eight distinct entries
   auto compute_group = [&](int gi, const KeyGroup<KEY_DT>& kg) {
-    float mine = 0.f;  // lane (e, g): score of entry e of tile g
+    float sacc[4];  // lane (e, r): tile u's head sum over the lane's rows, entry e
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       bf16x8 kb[4];
@@ -329,14 +329,14 @@ __global__ __launch_bounds__(256) void index_score_mfma(ScoreArgs a) {
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(qa[mt][ks], kb[ks], acc[mt]);
-      float sacc = 0.f;
+      sacc[u] = 0.f;
 #pragma unroll
       for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sacc = fmaf(wt[mt][jj], relu_bits(acc[mt][jj]), sacc);
-      sacc = rows_reduce(sacc, [](float x, float y) { return x + y; });
-      mine = lg == u ? sacc : mine;
+        for (int jj = 0; jj < 4; ++jj) sacc[u] = fmaf(wt[mt][jj], relu_bits(acc[mt][jj]), sacc[u]);
     }
+    // lane (e, g): the score of entry e of tile g
+    float mine = rows_sum4(sacc[0], sacc[1], sacc[2], sacc[3]);
     if constexpr (KEY_DT == CSA_FP8_E4M3) mine *= kg.scale;
     // tile < C / 16 always, so every lane's slot is inside this chunk
     const int eloc = (16 * gi + 4 * lg + wv) * 16 + ln;
