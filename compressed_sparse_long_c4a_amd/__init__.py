@@ -332,13 +332,18 @@ def _index_common(cu_q, q_pos, q_idx, head_w):
 
 
 def index_topk(cu_q, q_pos, q_idx, head_w, idx_cache: PagedCache, k: int, max_context: int,
-               with_scores: bool = False, workspace: torch.Tensor | None = None):
-    """Top-k entry ids [total_q, k] int32 (ascending, -1 padded) and optionally their scores."""
+               with_scores: bool = False, workspace: torch.Tensor | None = None,
+               workspace_limit: int | None = None):
+    """Top-k entry ids [total_q, k] int32 (ascending, -1 padded) and optionally their scores.
+    workspace_limit (bytes): allocate at most this much workspace (at least one query's); the
+    library then takes the queries in slices that fit."""
     batch, total_q, heads = _index_common(cu_q, q_pos, q_idx, head_w)
     dev = q_idx.device
     topk = torch.empty((total_q, k), dtype=torch.int32, device=dev)
     scores = torch.empty((total_q, k), dtype=torch.float32, device=dev) if with_scores else None
     ws_bytes = index_workspace_size(total_q, max_context, k)
+    if workspace_limit is not None and total_q > 0:
+        ws_bytes = min(ws_bytes, max(int(workspace_limit), index_workspace_size(1, max_context, k)))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     st = lib().csa_index_topk(_stream(), batch, cu_q.data_ptr(), q_pos.data_ptr(), total_q, max_context,

@@ -120,13 +120,15 @@ size_t csa_index_workspace_size(int total_q, int max_context, int k) {
   return csa::index_workspace_bytes(total_q, max_context, k);
 }
 
+// ws_queries: how many queries the workspace must hold (the whole call, or one for
+// csa_index_topk, which takes the queries in slices that fit)
 static int index_check(int batch, const int32_t* cu_q, const int32_t* q_pos, int total_q,
-                       int max_context, int k, size_t ws_bytes, const void* ws) {
+                       int max_context, int k, size_t ws_bytes, const void* ws, int ws_queries) {
   if (batch <= 0 || total_q < 0 || !cu_q) return CSA_EINVAL;
   if (total_q > 0 && !q_pos) return CSA_EINVAL;
   if (max_context <= 0 || max_context > kMaxContextIndex) return CSA_EINVAL;
   if (k <= 0 || k > 65536) return CSA_EINVAL;
-  if (total_q > 0 && (!ws || ws_bytes < csa::index_workspace_bytes(total_q, max_context, k)))
+  if (total_q > 0 && (!ws || ws_bytes < csa::index_workspace_bytes(ws_queries, max_context, k)))
     return CSA_EWORKSPACE;
   return CSA_OK;
 }
@@ -151,7 +153,7 @@ int csa_index_score(csa_stream_t stream, int batch, const int32_t* cu_q, const i
                     int total_q, int max_context, const void* q_idx, int q_dtype, int n_heads_idx,
                     const float* head_w, const csa_cache* idx_cache, int k, void* workspace,
                     size_t workspace_bytes) {
-  int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace);
+  int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace, total_q);
   if (st != CSA_OK) return st;
   st = score_check(total_q, q_idx, q_dtype, n_heads_idx, head_w, idx_cache);
   if (st != CSA_OK || total_q == 0) return st;
@@ -164,7 +166,7 @@ int csa_index_score(csa_stream_t stream, int batch, const int32_t* cu_q, const i
 int csa_index_select(csa_stream_t stream, int batch, const int32_t* cu_q, const int32_t* q_pos,
                      int total_q, int max_context, int k, int32_t* topk_idx, float* topk_score,
                      void* workspace, size_t workspace_bytes) {
-  int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace);
+  int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace, total_q);
   if (st != CSA_OK) return st;
   if (total_q == 0) return CSA_OK;
   if (!topk_idx) return CSA_EINVAL;
@@ -177,18 +179,37 @@ int csa_index_topk(csa_stream_t stream, int batch, const int32_t* cu_q, const in
                    int total_q, int max_context, const void* q_idx, int q_dtype, int n_heads_idx,
                    const float* head_w, const csa_cache* idx_cache, int k, int32_t* topk_idx,
                    float* topk_score, void* workspace, size_t workspace_bytes) {
-  int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace);
+  int st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace,
+                       total_q > 0 ? 1 : 0);
   if (st != CSA_OK) return st;
   st = score_check(total_q, q_idx, q_dtype, n_heads_idx, head_w, idx_cache);
   if (st != CSA_OK) return st;
   if (total_q == 0) return CSA_OK;
   if (!topk_idx) return CSA_EINVAL;
-  csa::IndexLaunch L{batch, cu_q, q_pos, total_q, max_context, q_idx, q_dtype, n_heads_idx,
-                     head_w, idx_cache, k};
-  const csa::IndexWorkspace ws = csa::index_workspace_carve(workspace, total_q, max_context, k);
-  hipError_t e = csa::launch_index_score(L, ws, (hipStream_t)stream);
-  if (e != hipSuccess) return CSA_EHIP;
-  return hip_status(csa::launch_index_select(L, topk_idx, topk_score, ws, (hipStream_t)stream));
+  // the most queries whose workspace fits (the size grows with the query count)
+  int slice = total_q;
+  if (workspace_bytes < csa::index_workspace_bytes(total_q, max_context, k)) {
+    int lo = 1, hi = total_q - 1;
+    while (lo < hi) {
+      const int mid = lo + (hi - lo + 1) / 2;
+      if (csa::index_workspace_bytes(mid, max_context, k) <= workspace_bytes) lo = mid;
+      else hi = mid - 1;
+    }
+    slice = lo;
+  }
+  const size_t q_row = (size_t)n_heads_idx * 128 * (q_dtype == CSA_BF16 ? 2 : 4);
+  for (int q0 = 0; q0 < total_q; q0 += slice) {
+    const int n = std::min(slice, total_q - q0);
+    csa::IndexLaunch L{batch, cu_q, q_pos + q0, n, max_context, (const char*)q_idx + q0 * q_row, q_dtype,
+                       n_heads_idx, head_w + (int64_t)q0 * n_heads_idx, idx_cache, k, q0};
+    const csa::IndexWorkspace ws = csa::index_workspace_carve(workspace, n, max_context, k);
+    hipError_t e = csa::launch_index_score(L, ws, (hipStream_t)stream);
+    if (e != hipSuccess) return CSA_EHIP;
+    e = csa::launch_index_select(L, topk_idx + (int64_t)q0 * k, topk_score ? topk_score + (int64_t)q0 * k : nullptr,
+                                 ws, (hipStream_t)stream);
+    if (e != hipSuccess) return CSA_EHIP;
+  }
+  return CSA_OK;
 }
 
 // One launch for csa_compress_index_score when the entry scoring stays small: every new indexer
@@ -225,7 +246,7 @@ int csa_compress_index_score(csa_stream_t stream, int batch, const int32_t* ctx_
   int st = compress_prepare(batch, ctx_lens, cu_new, total_new, num_jobs, jobs, &CL, &work);
   if (st != CSA_OK) return st;
   if (idx_job < 0 || idx_job >= num_jobs) return CSA_EINVAL;
-  st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace);
+  st = index_check(batch, cu_q, q_pos, total_q, max_context, k, workspace_bytes, workspace, total_q);
   if (st != CSA_OK) return st;
   st = score_check(total_q, q_idx, q_dtype, n_heads_idx, head_w, idx_cache);
   if (st != CSA_OK) return st;

@@ -37,6 +37,9 @@ constexpr int kMaxChunks = 1024;   // chunks per query the select kernel can pre
 
 struct ScoreArgs {
   int batch, n_heads, k, chunks, n_max;
+  // the launch's queries are the call's q_base .. q_base + q_count - 1: q_pos, q, w and the
+  // workspace are indexed from the first of them, cu_q by the call's own query indices
+  int q_base, q_count;
   int64_t n_cap;
   const int32_t* cu_q;
   const int32_t* q_pos;
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
     return;
   }
   const int chunk = blockIdx.x, qi = blockIdx.y - a.comp_rows;
-  const int b = seq_of_wave(a.cu_q, a.batch, qi);
+  const int b = seq_of_wave(a.cu_q, a.batch, a.q_base + qi);
   const int n = query_entries(a.q_pos, qi, a.n_max);
   const int64_t j0 = (int64_t)chunk * C;
   if (j0 >= n) return;
@@ -456,16 +459,17 @@ constexpr int kQT = 4;   // queries per workgroup (one per wave)
 constexpr int kGT = 8;   // tiles per group
 
 // Workgroup t of the query-tiled grid -> sequence b and its queries q0 .. q0 + nq - 1 (tiles
-// of kQT consecutive queries inside each sequence, in sequence order); false past the last tile.
-__device__ bool query_tile(const int32_t* cu_q, int batch, int t, int& b, int& q0, int& nq) {
+// of kQT consecutive queries inside each sequence's part of the queries [qs, qe), in sequence
+// order); false past the last tile.
+__device__ bool query_tile(const int32_t* cu_q, int batch, int qs, int qe, int t, int& b, int& q0, int& nq) {
   const int lane = threadIdx.x & 63;
   int before = 0;  // tiles of the sequences before this block of 64
   for (int b0 = 0; b0 < batch; b0 += 64) {
     const int bb = b0 + lane;
     int s0 = 0, s1 = 0;
     if (bb < batch) {
-      s0 = cu_q[bb];
-      s1 = cu_q[bb + 1];
+      s0 = min(max(cu_q[bb], qs), qe);
+      s1 = min(max(cu_q[bb + 1], qs), qe);
     }
     const int tiles = (s1 - s0 + kQT - 1) / kQT;
     const int incl = wave_incl_scan(tiles) + before;
@@ -501,7 +505,8 @@ __global__ __launch_bounds__(256) void index_score_qt(ScoreArgs a) {
   const int ln = lane & 15, lg = lane >> 4;
   const int chunk = blockIdx.x;
   int b = 0, q0 = 0, nq = 0;
-  if (!query_tile(a.cu_q, a.batch, blockIdx.y, b, q0, nq)) return;
+  if (!query_tile(a.cu_q, a.batch, a.q_base, a.q_base + a.q_count, blockIdx.y, b, q0, nq)) return;
+  q0 -= a.q_base;  // (from here on the launch's own query indices)
   const int64_t j0 = (int64_t)chunk * C;
   const int qi = q0 + wv;
   const bool has_q = wv < nq;
@@ -694,7 +699,7 @@ __global__ __launch_bounds__(256) void index_score_f32(ScoreArgs a) {
   __shared__ int misc[4];
   __shared__ uint32_t red[4];
   const int chunk = blockIdx.x, qi = blockIdx.y;
-  const int b = seq_of_wave(a.cu_q, a.batch, qi);
+  const int b = seq_of_wave(a.cu_q, a.batch, a.q_base + qi);
   const int n = query_entries(a.q_pos, qi, a.n_max);
   const int64_t j0 = (int64_t)chunk * C;
   if (j0 >= n) return;
@@ -1090,6 +1095,8 @@ ScoreArgs make_score_args(const IndexLaunch& a, const IndexWorkspace& ws) {
   s.chunks = ws.chunks;
   s.n_max = a.max_context / 4;
   s.n_cap = ws.n_cap;
+  s.q_base = a.q_base;
+  s.q_count = a.total_q;
   s.cu_q = a.cu_q;
   s.q_pos = a.q_pos;
   s.q = a.q_idx;

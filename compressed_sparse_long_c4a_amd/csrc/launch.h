@@ -83,6 +83,10 @@ struct IndexLaunch {
   const float* head_w;
   const csa_cache* idx_cache;
   int k;
+  // A slice of a call's queries: q_pos, q_idx, head_w (and the outputs) point at the slice's
+  // first query, total_q counts the slice, and q_base is that query's index in the call (cu_q
+  // keeps the call's indices).  0 for a whole call.
+  int q_base = 0;
 };
 hipError_t launch_index_score(const IndexLaunch& a, const IndexWorkspace& ws, hipStream_t stream);
 // The compressor jobs of `c` and the index score in one launch (bf16 queries, <= 64 heads, ratio-4

@@ -211,7 +211,12 @@ int csa_compress_insert_many(csa_stream_t stream, int batch, const int32_t* ctx_
  *   idx_cache: dim 128, rows_per_block 64, dtype FP8_E4M3, FP4_E2M1 or BF16 (any
  *         dtype with CSA_F32 queries).
  *   1 <= k <= 65536.  topk_idx [total_q][k] int32.  topk_score [total_q][k] or NULL.
- *   workspace of at least csa_index_workspace_size(total_q, max_context, k) bytes.
+ *   workspace: csa_index_workspace_size(total_q, max_context, k) bytes take every query in
+ *         one pass (one score and one select launch).  Any smaller workspace of at least
+ *         csa_index_workspace_size(1, max_context, k) bytes is also accepted: the queries are
+ *         then taken in consecutive slices of as many as fit (two launches per slice, same
+ *         results), which bounds the memory of long chunked prefills; below that size the
+ *         call returns CSA_EWORKSPACE before any launch.
  */
 size_t csa_index_workspace_size(int total_q, int max_context, int k);
 
@@ -225,7 +230,8 @@ int csa_index_topk(csa_stream_t stream, int batch, const int32_t* cu_q, const in
  * separately.  csa_index_score writes every candidate's score (and per-chunk
  * selection bounds) into `workspace`; csa_index_select reads them back and
  * writes topk_idx / topk_score.  Called back to back on one stream with the
- * same arguments and workspace they are exactly csa_index_topk.
+ * same arguments and workspace they are exactly csa_index_topk.  Both need the
+ * whole call's workspace, csa_index_workspace_size(total_q, max_context, k).
  */
 int csa_index_score(csa_stream_t stream, int batch, const int32_t* cu_q, const int32_t* q_pos,
                     int total_q, int max_context, const void* q_idx, int q_dtype, int n_heads_idx,

@@ -72,6 +72,16 @@ def test_validation_rejects_before_launch(csa):
     ic = csa._CCache(1, 1, csa.FP8_E4M3, 128, 64, 10, 1, 8)
     assert L.csa_index_topk(None, 1, 1, 1, 1, 1024, 1, csa.BF16, 64, 1, P(ic), 8, 1, None, 1, 16) \
         == csa.EWORKSPACE
+    # csa_index_topk takes its queries in slices: one query's workspace is the least it accepts,
+    # while the score and select halves need the whole call's
+    one = L.csa_index_workspace_size(1, 1 << 20, 8)
+    four = L.csa_index_workspace_size(4, 1 << 20, 8)
+    assert one < four
+    assert L.csa_index_topk(None, 1, 1, 1, 4, 1 << 20, 1, csa.BF16, 64, 1, P(ic), 8, 1, None, 1, one - 1) \
+        == csa.EWORKSPACE
+    assert L.csa_index_score(None, 1, 1, 1, 4, 1 << 20, 1, csa.BF16, 64, 1, P(ic), 8, 1, four - 1) \
+        == csa.EWORKSPACE
+    assert L.csa_index_select(None, 1, 1, 1, 4, 1 << 20, 8, 1, None, 1, four - 1) == csa.EWORKSPACE
     assert L.csa_index_topk(None, 1, 1, 1, 1, 1024, 1, csa.BF16, 64, 1, P(ic), 0, 1, None, 1, 1 << 40) \
         == csa.EINVAL
     assert L.csa_index_topk(None, 1, 1, 1, 1, 1024, 1, csa.BF16, 65, 1, P(ic), 8, 1, None, 1, 1 << 40) \

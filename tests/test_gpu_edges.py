@@ -104,6 +104,47 @@ def test_clustered_winners_take_the_full_scan(gpu):
     assert not rep["fail"], rep["fail"][:10]
 
 
+SLICE_CASES = [
+    # ragged chunked prefill (the query-tiled score kernel when whole; a slice boundary cuts
+    # through sequences and query tiles)
+    D(C.C4A_PREFILL_64K, name="slices_prefill", ctx_after=(6000, 3000, 9000), new_tokens=(37, 3, 64),
+      q_per_seq=(37, 3, 64), k=256, n_heads=16, stages=("index",)),
+    # decode, one query per sequence
+    D(C.C4A_1M_B4_FP8, name="slices_decode", ctx_after=(70000, 69999, 5000, 9), k=512, n_heads=16,
+      stages=("index",)),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("cfg", SLICE_CASES, ids=lambda c: c.name)
+def test_index_topk_in_slices(gpu, cfg):
+    """csa_index_topk with a workspace for fewer queries than the call takes them in slices
+    (slices of 10, 3 and 1 queries, those smaller than the call): the ids and scores must equal
+    the one-pass call's bit for bit, and the one-pass call must pass the oracle's top-k checks."""
+    import compressed_sparse_long_c4a_amd as csa
+    from compressed_sparse_long_c4a_amd import pipeline
+    from tests import oracle_step as O
+    print(f"case {cfg.name}", flush=True)
+    d = inputs.draw(cfg)
+    g = pipeline.to_device(d)
+    args = (g["cu_q"], g["q_pos"], g["q_idx"], g["head_w"], g["idx"], cfg.k, cfg.max_context)
+    whole, whole_sc = csa.index_topk(*args, with_scores=True)
+    torch.cuda.synchronize()
+    nq = whole.shape[0]
+    for per in [p for p in (10, 3, 1) if p < nq]:
+        limit = csa.index_workspace_size(per, cfg.max_context, cfg.k)
+        assert limit < csa.index_workspace_size(nq, cfg.max_context, cfg.k)
+        part, part_sc = csa.index_topk(*args, with_scores=True, workspace_limit=limit)
+        torch.cuda.synchronize()
+        assert torch.equal(part, whole), f"ids differ with slices of {per}"
+        assert torch.equal(part_sc, whole_sc), f"scores differ with slices of {per}"
+    res = O.run_oracle(cfg, d)
+    ids = whole.cpu().numpy()
+    for i in range(nq):
+        ok, why = O.topk_acceptable(ids[i], res["scores"][i], cfg.k)
+        assert ok, f"query {i}: {why}"
+
+
 @pytest.mark.gpu
 def test_max_k(gpu):
     """k = 65536, the largest the ABI accepts, over a 300K-token context (75,000 entries): the
