@@ -953,6 +953,25 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
   __shared__ uint2 tail_sh[kNewCand];  // the first entries the call's compressor inserted
   const int qi = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
+  // The loads that need nothing but the query index and the workspace geometry go out first,
+  // in one trip with the query's position (n only decides which of them are used; they read
+  // the query's own slice of the workspace whatever it holds):
+  // per chunk (one per thread): candidate count, key range and bound
+  const uint2* gcand = a.cand + (int64_t)qi * a.n_cap;
+  const int4 inf = a.cand_info[(int64_t)qi * a.chunks + min(tid, a.chunks - 1)];
+  // speculatively, the first 64 slots of every chunk's list (a chunk's quota is ~2.5 times its
+  // share of the winners, so its list rarely holds more): wave w reads chunks w, w + 16, ..., up
+  // to 8 of them (slots past a list's end are discarded)
+  constexpr int kPieces = 8;
+  uint2 v[kPieces];
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u) {
+    const int c = min(w + u * kSelWaves, a.chunks - 1);
+    v[u] = gcand[(int64_t)c * C + lane];
+  }
+  // the entries the call's compressor inserted: where they start, and the first 64 of them
+  const int nf_w = a.new_from[qi];
+  const uint2 nc = a.new_cand[(int64_t)qi * kNewCand + lane];
   const int n = query_entries(a.q_pos, qi, a.n_max);
   const int kprime = min(a.k, n);
   int32_t* out = a.topk_idx + (int64_t)qi * a.k;
@@ -971,26 +990,9 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
     return;
   }
   const int nchunks = (n + C - 1) / C;
-  const uint2* gcand = a.cand + (int64_t)qi * a.n_cap;
   hist[tid] = 0;  // (published by the barriers of the count scan below)
   hist[tid + kSelThreads] = 0;
-  // (the loads above and below need nothing but the query index and the workspace geometry,
-  // so they all go out in one trip; n only decides which of them are used)
-  // per chunk (one per thread): candidate count, key range and bound
-  const int4 inf = a.cand_info[(int64_t)qi * a.chunks + min(tid, a.chunks - 1)];
-  // speculatively, the first 64 slots of every chunk's list (a chunk's quota is ~2.5 times its
-  // share of the winners, so its list rarely holds more): wave w reads chunks w, w + 16, ..., up
-  // to 8 of them (slots past a list's end are discarded)
-  constexpr int kPieces = 8;
-  uint2 v[kPieces];
-#pragma unroll
-  for (int u = 0; u < kPieces; ++u) {
-    const int c = min(w + u * kSelWaves, a.chunks - 1);
-    v[u] = gcand[(int64_t)c * C + lane];
-  }
-  // the entries the call's compressor inserted: where they start, and the first 64 of them
-  const int nf = min(max(a.new_from[qi], 0), n);
-  const uint2 nc = a.new_cand[(int64_t)qi * kNewCand + lane];
+  const int nf = min(max(nf_w, 0), n);
   if (w == 0) tail_sh[lane] = nc;  // (published by the scan's barriers)
   const bool has = tid < nchunks;
   const int cnt = has ? min(max(inf.x, 0), C) : 0;
