@@ -255,34 +255,43 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
     return;
   }
   const int chunk = blockIdx.x, qi = blockIdx.y - a.comp_rows;
-  const int b = seq_of_wave(a.cu_q, a.batch, a.q_base + qi);
-  const int n = query_entries(a.q_pos, qi, a.n_max);
-  const int64_t j0 = (int64_t)chunk * C;
-  if (j0 >= n) return;
-  const int nloc = (int)min((int64_t)C, n - j0);
-  // entries [nold_loc, nloc) of the chunk are this step's (fused launch only)
-  const int nold = a.ctx_lens ? a.ctx_lens[b] / 4 : 0x7FFFFFFF;
-  const int nold_loc = (int)max((int64_t)0, min((int64_t)nloc, (int64_t)nold - j0));
-  const bool any_old = nold_loc > 0;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const int H = a.n_heads;
   constexpr int NW = KeyGroup<KEY_DT>::NW;
-
-  // physical block ids of the chunk (C / 64 = 32 blocks): lane i of every wave holds block i
-  const int nblk = (nloc + 63) >> 6;
-  const int32_t* btrow = a.cache.bt + (int64_t)b * a.cache.bt_stride + (j0 >> 6);
-  const int32_t my_blk = lane < nblk ? btrow[lane] : 0;
-  // the query (heads x 128 bf16) and head weights are read once per workgroup, 16 bytes per
-  // thread and pass, and shared through LDS
+  // First trip: everything that needs only the workgroup's coordinates goes out together -- the
+  // query (heads x 128 bf16, 16 bytes per thread and pass; rows past the last head are read
+  // clamped and zeroed after) and head weights, read once per workgroup and shared through
+  // LDS, the sequence table and the query's position.
+  const int t_q = a.q_pos[qi];
   uint4 qv[HT];
   const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)qi * H * 128;
 #pragma unroll
   for (int p = 0; p < HT; ++p) {
-    const int h = 16 * p + (threadIdx.x >> 4);
-    qv[p] = h < H ? *(const uint4*)(qrow + (int64_t)h * 128 + 8 * (threadIdx.x & 15)) : make_uint4(0, 0, 0, 0);
+    const int h = min(16 * p + (int)(threadIdx.x >> 4), H - 1);
+    qv[p] = load_global16(qrow + (int64_t)h * 128 + 8 * (threadIdx.x & 15));
   }
-  const float wv_h = threadIdx.x < 16 * HT && threadIdx.x < H ? a.w[(int64_t)qi * H + threadIdx.x] : 0.f;
+  const float w_ld = a.w[(int64_t)qi * H + min((int)threadIdx.x, H - 1)];
+  const int cu_v = seq_load(a.cu_q, a.batch);
+  asm volatile("" ::"s"(t_q));  // (the position's load stays in this trip, not behind the next)
+  const int n = min((t_q + 1) / 4, a.n_max);  // (query_entries)
+  const int b = seq_pick(a.cu_q, a.batch, a.q_base + qi, cu_v);
+#pragma unroll
+  for (int p = 0; p < HT; ++p)
+    if (16 * p + (int)(threadIdx.x >> 4) >= H) qv[p] = make_uint4(0, 0, 0, 0);
+  const float wv_h = threadIdx.x < 16 * HT && threadIdx.x < H ? w_ld : 0.f;
+  const int64_t j0 = (int64_t)chunk * C;
+  if (j0 >= n) return;
+  const int nloc = (int)min((int64_t)C, n - j0);
+  // Second trip: the physical block ids of the chunk (C / 64 = 32 blocks: lane i of every wave
+  // holds block i) and this step's first entry (fused launch only: entries [nold_loc, nloc) of
+  // the chunk are this step's).
+  const int nblk = (nloc + 63) >> 6;
+  const int32_t* btrow = a.cache.bt + (int64_t)b * a.cache.bt_stride + (j0 >> 6);
+  const int32_t my_blk = lane < nblk ? btrow[lane] : 0;
+  const int nold = a.ctx_lens ? a.ctx_lens[b] / 4 : 0x7FFFFFFF;
+  const int nold_loc = (int)max((int64_t)0, min((int64_t)nloc, (int64_t)nold - j0));
+  const bool any_old = nold_loc > 0;
   hist[threadIdx.x] = 0u;  // (the bound's histogram; ordered by the barrier after the query copy)
 
   const int ntiles = (nloc + 15) >> 4;
