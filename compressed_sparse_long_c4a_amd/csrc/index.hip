@@ -780,24 +780,20 @@ constexpr int kDigitBits = 11;              // radix digit: 2048 bins, two per t
 constexpr int kBins = 1 << kDigitBits;
 
 // Exclusive prefix sums of two values over the select block at once; totals in tot[0..1].
-// sh holds 2 kSelWaves ints.
+// sh holds 2 kSelWaves ints; every caller has passed a barrier since sh was last read.
 __device__ __forceinline__ int2 sel_exscan2(int v0, int v1, int* sh, int* tot) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i0 = wave_incl_scan(v0), i1 = wave_incl_scan(v1);
-  __syncthreads();
   if (lane == 63) { sh[w] = i0; sh[kSelWaves + w] = i1; }
   __syncthreads();
-  int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
-#pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) {
-    const int x0 = sh[i], x1 = sh[kSelWaves + i];
-    b0 += i < w ? x0 : 0;
-    b1 += i < w ? x1 : 0;
-    t0 += x0;
-    t1 += x1;
-  }
-  tot[0] = t0;
-  tot[1] = t1;
+  // the wave totals: lane i < 16 takes wave i's, and a scan over the wave gives every prefix
+  const int x0 = wave_incl_scan(lane < kSelWaves ? sh[lane] : 0);
+  const int x1 = wave_incl_scan(lane < kSelWaves ? sh[kSelWaves + lane] : 0);
+  tot[0] = __builtin_amdgcn_readlane(x0, kSelWaves - 1);
+  tot[1] = __builtin_amdgcn_readlane(x1, kSelWaves - 1);
+  const int b0 = w > 0 ? __builtin_amdgcn_readlane(x0, w - 1) : 0;
+  const int b1 = w > 0 ? __builtin_amdgcn_readlane(x1, w - 1) : 0;
   return make_int2(b0 + i0 - v0, b1 + i1 - v1);
 }
 
@@ -839,7 +835,7 @@ struct CandScores {
 // it are selected: a most-significant-digit radix select on d = key - lo, 11 bits per pass (keys
 // decided by a higher digit drop out of later passes).  With `have`, hist already holds the
 // first pass's histogram (built while the candidates were gathered).  Once the bin that holds the answer has
-// at most 64 keys, one wave ranks them directly instead of further passes.
+// at most 64 keys, they are ranked all against all instead of further passes.
 template <class Cand>
 __device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, bool have, Cand cand,
                              uint32_t* hist, int* misc, int* scan_sh, uint32_t* small_sh,
@@ -848,11 +844,13 @@ __device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, bool h
   uint32_t prefix = 0;  // decided high digits of d
   int need = kprime;
   int top = bit_len(hi - lo);
+  if (have) {  // (this barrier publishes the caller's candidates and histogram)
+    if (tid == 0) misc[2] = 0;
+    __syncthreads();
+  }
   while (top > 0) {
     const int shift = max(0, top - kDigitBits);
-    if (have) {
-      if (tid == 0) misc[2] = 0;
-    } else {
+    if (!have) {
       hist[tid] = 0;
       hist[tid + kSelThreads] = 0;
       if (tid == 0) misc[2] = 0;
@@ -861,9 +859,9 @@ __device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, bool h
         const uint32_t d = cand(g).x - lo;
         if (top >= 32 || (d >> top) == (prefix >> top)) atomicAdd(&hist[(d >> shift) & (kBins - 1)], 1u);
       }
+      __syncthreads();
     }
     have = false;
-    __syncthreads();
     // thread t owns bins 2047 - 2t and 2046 - 2t (descending); the thread whose running count
     // from the top crosses `need` holds the bin of the kprime-th largest key
     const uint32_t h0 = hist[kBins - 1 - 2 * tid], h1 = hist[kBins - 2 - 2 * tid];
@@ -881,7 +879,7 @@ __device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, bool h
     const int in_bin = misc[3];
     top = shift;
     if (top > 0 && in_bin <= 64) {
-      // collect the bin's keys (any order) and rank them in one wave
+      // collect the bin's keys (any order) and rank them all against all
       for (int g = tid; g < m; g += kSelThreads) {
         const uint32_t key = cand(g).x;
         if (((key - lo) >> top) == (prefix >> top)) {
@@ -890,16 +888,29 @@ __device__ void radix_select(int m, int kprime, uint32_t lo, uint32_t hi, bool h
         }
       }
       __syncthreads();
-      if (tid < kWave) {
-        const uint32_t mine = lane < in_bin ? small_sh[lane] : 0u;
+      {
+        // all against all: thread (i = tid / 16, j = tid % 16) compares key i with keys
+        // 4 j .. 4 j + 3; the sums over the 16 lanes of a row (one key) end in its lane 15
+        const int i = tid >> 4, j = tid & 15;
+        const uint32_t mine = small_sh[i];
         int greater = 0, equal = 0;
-        for (int i = 0; i < in_bin; ++i) {
-          const uint32_t other = (uint32_t)__builtin_amdgcn_readlane((int)mine, i);
-          greater += other > mine;
-          equal += other == mine;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int o = 4 * j + e;
+          const uint32_t other = small_sh[o];
+          greater += (o < in_bin && other > mine) ? 1 : 0;
+          equal += (o < in_bin && other == mine) ? 1 : 0;
         }
+        greater += dpp<kDppRowShr<1>>(greater);
+        equal += dpp<kDppRowShr<1>>(equal);
+        greater += dpp<kDppRowShr<2>>(greater);
+        equal += dpp<kDppRowShr<2>>(equal);
+        greater += dpp<kDppRowShr<4>>(greater);
+        equal += dpp<kDppRowShr<4>>(equal);
+        greater += dpp<kDppRowShr<8>>(greater);
+        equal += dpp<kDppRowShr<8>>(equal);
         // the need-th largest: greater < need <= greater + equal (any holder of it may write)
-        if (lane < in_bin && greater < need && need <= greater + equal) {
+        if (j == 15 && i < in_bin && greater < need && need <= greater + equal) {
           misc[0] = (int)(mine - lo);
           misc[1] = need - greater;
         }
@@ -925,20 +936,9 @@ __device__ void write_winners(const SelArgs& a, int qi, int m, uint32_t tau, int
   const int tid = threadIdx.x;
   const int per = (m + kSelThreads - 1) / kSelThreads;
   const int g0 = min(m, tid * per), g1 = min(m, g0 + per);
-  int gt = 0, eq = 0;
-  for (int g = g0; g < g1; ++g) {
-    const uint32_t key = cand(g).x;
-    gt += key > tau;
-    eq += key == tau;
-  }
-  int tot2[2];
-  const int2 ex = sel_exscan2(gt, eq, scan_sh, tot2);
-  int tr = ex.y;                                 // ties before this range
-  int pos = ex.x + min(ex.y, ties_needed);       // winners before this range
   int32_t* out = a.topk_idx + (int64_t)qi * a.k;
   float* outs = a.topk_score ? a.topk_score + (int64_t)qi * a.k : nullptr;
-  for (int g = g0; g < g1; ++g) {
-    const uint2 c = cand(g);
+  auto place = [&](uint2 c, int& tr, int& pos) {
     bool take = c.x > tau;
     if (c.x == tau) { take = tr < ties_needed; ++tr; }
     if (take) {
@@ -948,7 +948,37 @@ __device__ void write_winners(const SelArgs& a, int qi, int m, uint32_t tau, int
       }
       ++pos;
     }
+  };
+  int tot2[2];
+  if (std::is_same<Cand, CandLds>::value && per <= kSelCap / kSelThreads) {
+    // candidates in LDS (at most 8 per thread): one read, kept in registers for both passes
+    constexpr int R = kSelCap / kSelThreads;
+    uint2 cc[R];
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < R; ++e) {
+      cc[e] = g0 + e < g1 ? cand(g0 + e) : make_uint2(0u, 0u);
+      gt += (g0 + e < g1 && cc[e].x > tau) ? 1 : 0;
+      eq += (g0 + e < g1 && cc[e].x == tau) ? 1 : 0;
+    }
+    const int2 ex = sel_exscan2(gt, eq, scan_sh, tot2);
+    int tr = ex.y;                            // ties before this range
+    int pos = ex.x + min(ex.y, ties_needed);  // winners before this range
+#pragma unroll
+    for (int e = 0; e < R; ++e)
+      if (g0 + e < g1) place(cc[e], tr, pos);
+    return;
   }
+  int gt = 0, eq = 0;
+  for (int g = g0; g < g1; ++g) {
+    const uint32_t key = cand(g).x;
+    gt += key > tau;
+    eq += key == tau;
+  }
+  const int2 ex = sel_exscan2(gt, eq, scan_sh, tot2);
+  int tr = ex.y;                                 // ties before this range
+  int pos = ex.x + min(ex.y, ties_needed);       // winners before this range
+  for (int g = g0; g < g1; ++g) place(cand(g), tr, pos);
 }
 
 __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
@@ -958,7 +988,7 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
   __shared__ uint32_t small_sh[64];
   __shared__ int misc[4];
   __shared__ int scan_sh[2 * kSelWaves];
-  __shared__ uint32_t red[3 * kSelWaves];
+  __shared__ uint4 red4[kSelWaves];
   __shared__ uint2 tail_sh[kNewCand];  // the first entries the call's compressor inserted
   const int qi = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -1005,51 +1035,40 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
   if (w == 0) tail_sh[lane] = nc;  // (published by the scan's barriers)
   const bool has = tid < nchunks;
   const int cnt = has ? min(max(inf.x, 0), C) : 0;
-  uint32_t lo = wave_min_u32(has && cnt ? (uint32_t)inf.y : 0xFFFFFFFFu);
-  uint32_t hi = wave_max_u32(has && cnt ? (uint32_t)inf.z : 0u);
-  const uint32_t bmax = wave_max_u32(has ? (uint32_t)inf.w : 0u);
-  if (lane == 0) {
-    red[w] = lo;
-    red[kSelWaves + w] = hi;
-    red[2 * kSelWaves + w] = bmax;
-  }
-  int tot2[2];
-  off_sh[tid] = sel_exscan2(cnt, 0, scan_sh, tot2).x;  // (its barriers also publish red)
-  const int m_chunks = tot2[0];
   const int n_new = n - nf;
-  const int m = m_chunks + n_new;
-  uint32_t maxb = 0u;
-#pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) {
-    lo = min(lo, red[i]);
-    hi = max(hi, red[kSelWaves + i]);
-    maxb = max(maxb, red[2 * kSelWaves + i]);
-  }
   // new entry r: listed (r < 64) or its stored score
   auto new_entry = [&](int r) -> uint2 {
     const int j = nf + r;
     return r < kNewCand ? tail_sh[r] : make_uint2(f2key(sc[j]), (uint32_t)j);
   };
-  if (n_new > 0) {  // their keys widen the range
-    for (int r = tid; r < n_new; r += kSelThreads) {
-      const uint32_t key = new_entry(r).x;
-      lo = min(lo, key);
-      hi = max(hi, key);
-    }
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
-    __syncthreads();
-    if (lane == 0) {
-      red[w] = lo;
-      red[kSelWaves + w] = hi;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kSelWaves; ++i) {
-      lo = min(lo, red[i]);
-      hi = max(hi, red[kSelWaves + i]);
-    }
+  // key range of the candidates (the new entries' keys included: wave 0 holds the first 64
+  // in nc), the largest bound and the longest list: one exchange through LDS
+  uint32_t lo = has && cnt ? (uint32_t)inf.y : 0xFFFFFFFFu;
+  uint32_t hi = has && cnt ? (uint32_t)inf.z : 0u;
+  if (w == 0 && lane < n_new) {
+    lo = min(lo, nc.x);
+    hi = max(hi, nc.x);
   }
+  for (int r = kNewCand + tid; r < n_new; r += kSelThreads) {
+    const uint32_t key = f2key(sc[nf + r]);
+    lo = min(lo, key);
+    hi = max(hi, key);
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  const uint32_t bmax = wave_max_u32(has ? (uint32_t)inf.w : 0u);
+  const uint32_t cmax = wave_max_u32((uint32_t)cnt);
+  if (lane == 0) red4[w] = make_uint4(lo, hi, bmax, cmax);
+  int tot2[2];
+  off_sh[tid] = sel_exscan2(cnt, 0, scan_sh, tot2).x;  // (its barrier also publishes red4)
+  const int m_chunks = tot2[0];
+  const int m = m_chunks + n_new;
+  const uint4 r4 = lane < kSelWaves ? red4[lane] : make_uint4(0xFFFFFFFFu, 0u, 0u, 0u);
+  lo = wave_min_u32(r4.x);
+  hi = wave_max_u32(r4.y);
+  const uint32_t maxb = wave_max_u32(r4.z);
+  // every list held by the first trip's loads: nothing beyond them to fetch
+  const bool lists_loaded = nchunks <= kPieces * kSelWaves && wave_max_u32(r4.w) <= 64u;
   if (tid == 0) off_sh[nchunks] = m_chunks;
   __syncthreads();
   uint32_t tau;
@@ -1069,14 +1088,16 @@ __global__ __launch_bounds__(kSelThreads) void index_select(SelArgs a) {
       if (lane < len) put(off_sh[c] + lane, v[u]);
     }
     // the rest: chunks beyond the first 8 per wave, and lists longer than 64
-    for (int c = w; c < nchunks; c += kSelWaves) {
-      const int len = off_sh[c + 1] - off_sh[c];
-      const int j0 = c < w + kPieces * kSelWaves ? 64 : 0;
-      for (int j = j0 + lane; j < len; j += 64) put(off_sh[c] + j, gcand[(int64_t)c * C + j]);
+    if (!lists_loaded) {
+      for (int c = w; c < nchunks; c += kSelWaves) {
+        const int len = off_sh[c + 1] - off_sh[c];
+        const int j0 = c < w + kPieces * kSelWaves ? 64 : 0;
+        for (int j = j0 + lane; j < len; j += 64) put(off_sh[c] + j, gcand[(int64_t)c * C + j]);
+      }
     }
     // the new entries, after every chunk's candidates (their ids are the largest)
     for (int r = tid; r < n_new; r += kSelThreads) put(m_chunks + r, new_entry(r));
-    __syncthreads();
+    // (radix_select's first barrier publishes the candidates and the histogram)
     const CandLds in_lds{cand_sh};
     radix_select(m, kprime, lo, hi, true, in_lds, hist, misc, scan_sh, small_sh, tau, ties_needed);
     if (tau >= maxb) {

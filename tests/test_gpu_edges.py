@@ -104,6 +104,18 @@ def test_clustered_winners_take_the_full_scan(gpu):
     assert not rep["fail"], rep["fail"][:10]
 
 
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("clustered", [False, True], ids=["spread", "clustered"])
+def test_select_past_128_chunks(gpu, clustered):
+    """Contexts past 1M tokens (more than 128 chunks of 2,048 entries per query): the select
+    kernel's candidate lists beyond those its first trip loads, on the candidate path and on
+    the full-scan fallback."""
+    cfg = D(C.C4A_1M_B4_FP8, name="c4a_select_wide", ctx_after=(1300000, 1100000), n_heads=16, k=2048)
+    print(f"case {cfg.name} clustered={clustered}", flush=True)
+    rep = P.run_step_parity(cfg, verbose=True, prep=_cluster_winners if clustered else None, fast=True)
+    assert not rep["fail"], rep["fail"][:10]
+
 SLICE_CASES = [
     # ragged chunked prefill (the query-tiled score kernel when whole; a slice boundary cuts
     # through sequences and query tiles)
