@@ -609,12 +609,15 @@ __global__ __launch_bounds__(kThreads) void attn_partial(Args a) {
 // per-head step maximum and then P are exchanged through LDS, and every wave accumulates O^T
 // over the step's 128 rows for its own eighth of the dimensions (five or four 16-dim tiles of
 // 576), so the partial output leaves the workgroup from registers, with no merge inside it.
-// Rows gathered from random blocks arrive after a long latency, so each wave keeps kRing steps
-// of its rows in flight in registers, and every load of the prologue and of the ring is issued
-// unconditionally (clamped, or pointed at one cached row when there is nothing left to load):
-// with no branch around them, the wait counters wait for exactly the loads a value needs and
-// the next steps' rows stay in flight meanwhile.  The dependent trips are: (query position,
-// sequence, list entries, query heads) -> block table -> (row scales, then rows).
+// Rows gathered from random blocks arrive after a long latency, so a wave issues the loads of
+// its next step's rows as soon as it has staged the current step's in LDS (kRing steps in
+// flight: the vector L1 passes one step's rows in less time than the step's work takes, and
+// keeping a second step in flight only delayed the first one's rows in the prologue), and
+// every load of the prologue and of the ring is issued unconditionally (clamped, or pointed at
+// one cached row when there is nothing left to load): with no branch around them, the wait
+// counters wait for exactly the loads a value needs and the next step's rows stay in flight
+// meanwhile.  The dependent trips are: (query position, sequence, list entries, query heads)
+// -> block table -> (row scales, then rows).
 // The waves stage the fp8 codes they loaded in LDS; PV reads them back transposed with
 // ds_read_b64_tr_b8 (a 16-lane group reads an 8-row x 16-byte block and lane l receives column
 // l of the 8 rows), which is exactly the A operand of V^T with K = 32 rows: the MFMA rows of
@@ -625,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial(Args a) {
 constexpr int kF8Waves = 8;
 constexpr int kF8Threads = 64 * kF8Waves;
 constexpr int kStepF8 = 16 * kF8Waves;  // rows per step: one 16-row QK tile per wave
-constexpr int kRing = 2;                // register tiles per wave (steps in flight)
+constexpr int kRing = 1;                // register tiles per wave (steps in flight)
 static_assert(kRowsPerSplitF8 % kF8Threads == 0 && kRowsPerSplitF8 % kStepF8 == 0, "fp8 split size");
 template <int DIM>
 __global__ __launch_bounds__(kF8Threads) void attn_partial_fp8(Args a) {
