@@ -273,6 +273,15 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
   }
   const float w_ld = a.w[(int64_t)qi * H + min((int)threadIdx.x, H - 1)];
   const int cu_v = seq_load(a.cu_q, a.batch);
+  // Speculatively, in the same trip: the chunk's block ids (lane i: block i of the chunk) and
+  // the entry count of sequence bg = the query's own index -- a decode call holds one query per
+  // sequence, so the guess holds there and the second trip below is skipped (the loads stay
+  // inside sequence bg's block-table row whatever they fetch).
+  const int64_t j0 = (int64_t)chunk * C;
+  const int bg = min(a.q_base + qi, a.batch - 1);
+  const int32_t blk_g =
+      a.cache.bt[(int64_t)bg * a.cache.bt_stride + min((int)(j0 >> 6) + lane, a.cache.bt_stride - 1)];
+  const int ctx_g = a.ctx_lens ? a.ctx_lens[bg] : 0;
   asm volatile("" ::"s"(t_q));  // (the position's load stays in this trip, not behind the next)
   const int n = min((t_q + 1) / 4, a.n_max);  // (query_entries)
   const int b = seq_pick(a.cu_q, a.batch, a.q_base + qi, cu_v);
@@ -280,16 +289,22 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
   for (int p = 0; p < HT; ++p)
     if (16 * p + (int)(threadIdx.x >> 4) >= H) qv[p] = make_uint4(0, 0, 0, 0);
   const float wv_h = threadIdx.x < 16 * HT && threadIdx.x < H ? w_ld : 0.f;
-  const int64_t j0 = (int64_t)chunk * C;
   if (j0 >= n) return;
   const int nloc = (int)min((int64_t)C, n - j0);
-  // Second trip: the physical block ids of the chunk (C / 64 = 32 blocks: lane i of every wave
-  // holds block i) and this step's first entry (fused launch only: entries [nold_loc, nloc) of
-  // the chunk are this step's).
+  // Second trip, when the guess missed: the physical block ids of the chunk (C / 64 = 32
+  // blocks: lane i of every wave holds block i) and this step's first entry (fused launch only:
+  // entries [nold_loc, nloc) of the chunk are this step's).
   const int nblk = (nloc + 63) >> 6;
-  const int32_t* btrow = a.cache.bt + (int64_t)b * a.cache.bt_stride + (j0 >> 6);
-  const int32_t my_blk = lane < nblk ? btrow[lane] : 0;
-  const int nold = a.ctx_lens ? a.ctx_lens[b] / 4 : 0x7FFFFFFF;
+  int32_t my_blk;
+  int nold;
+  if (b == bg) {  // (uniform)
+    my_blk = lane < nblk ? blk_g : 0;
+    nold = a.ctx_lens ? ctx_g / 4 : 0x7FFFFFFF;
+  } else {
+    const int32_t* btrow = a.cache.bt + (int64_t)b * a.cache.bt_stride + (j0 >> 6);
+    my_blk = lane < nblk ? btrow[lane] : 0;
+    nold = a.ctx_lens ? a.ctx_lens[b] / 4 : 0x7FFFFFFF;
+  }
   const int nold_loc = (int)max((int64_t)0, min((int64_t)nloc, (int64_t)nold - j0));
   const bool any_old = nold_loc > 0;
   hist[threadIdx.x] = 0u;  // (the bound's histogram; ordered by the barrier after the query copy)
