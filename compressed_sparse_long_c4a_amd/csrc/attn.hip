@@ -1293,23 +1293,28 @@ __global__ __launch_bounds__(256) void attn_merge(MergeArgs a) {
 #pragma unroll
   for (int j = 0; j < kMergeCols; ++j) col[j] = min(lane + 64 * j, dim4 - 1);
   float4 v[kMergeRound][kMergeCols];
-  auto load_round = [&](int s0) {  // clamped, unconditional: every load of the round in flight
+  // (m, l) of split lane (the first 64 splits) first, then the partial rows of the first round:
+  // one trip; rounds hold only existing splits (the condition is uniform)
+  const float2 ml0 = lane < a.splits ? *(const float2*)&ml[lane * mls] : make_float2(-INFINITY, 0.f);
+  auto load_round = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < kMergeRound; ++u) {
-      const int64_t sb = (int64_t)min(s0 + u, a.splits - 1) * stride4;
+      if (s0 + u < a.splits) {
+        const int64_t sb = (int64_t)(s0 + u) * stride4;
 #pragma unroll
-      for (int j = 0; j < kMergeCols; ++j) v[u][j] = src[sb + col[j]];
+        for (int j = 0; j < kMergeCols; ++j) v[u][j] = src[sb + col[j]];
+      }
     }
   };
   load_round(0);
   const int t = a.q_pos[qi];
 
   // M = max_s m_s (log2 units), L = sum_s 2^(m_s - M) l_s
-  float M = -INFINITY;
-  for (int s = lane; s < a.splits; s += 64) M = fmaxf(M, ml[s * mls]);
+  float M = ml0.x;
+  for (int s = 64 + lane; s < a.splits; s += 64) M = fmaxf(M, ml[s * mls]);
   M = wave_max(M);
-  float L = 0.f;
-  for (int s = lane; s < a.splits; s += 64) {
+  float L = (ml0.x == -INFINITY) ? 0.f : exp2f(ml0.x - M) * ml0.y;
+  for (int s = 64 + lane; s < a.splits; s += 64) {
     const float m = ml[s * mls];
     L += (m == -INFINITY) ? 0.f : exp2f(m - M) * ml[s * mls + 1];
   }
@@ -1324,14 +1329,14 @@ __global__ __launch_bounds__(256) void attn_merge(MergeArgs a) {
     if (s0 > 0) load_round(s0);
     if ((s0 & 63) == 0) {
       const int s = s0 + lane;
-      const float m = s < a.splits ? ml[s * mls] : -INFINITY;
+      const float m = s0 == 0 ? ml0.x : s < a.splits ? ml[s * mls] : -INFINITY;
       wl = (m == -INFINITY) ? 0.f : exp2f(m - M);
     }
 #pragma unroll
     for (int u = 0; u < kMergeRound; ++u) {
-      const float w = s0 + u < a.splits
-          ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), (s0 & 63) + u))
-          : 0.f;
+      if (s0 + u >= a.splits) break;  // (uniform)
+      const float w =
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), (s0 & 63) + u));
 #pragma unroll
       for (int j = 0; j < kMergeCols; ++j) {
         acc[j].x = fmaf(w, v[u][j].x, acc[j].x);
