@@ -983,14 +983,25 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
     ent[u] = a.has_topk ? a.topk[(int64_t)qi * a.k + min(pos, a.k - 1)] : pos;
   }
   // Q^T as the B operand: lane (head ln, group lg) holds q[h][32 ks + 8 lg .. +7] (heads past
-  // the last repeat it; their rows are never stored)
-  bf16x8 qb[NKS];
-  {
-    const int h = min(16 * hg + ln, H - 1);
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)qi * H + h) * DIM + 8 * lg;
+  // the last repeat it; their rows are never stored).  The workgroup's query heads (16, or 64
+  // with HG4) come through LDS: loaded in whole lines (a head's 16-byte chunks in consecutive
+  // lanes) into the tile slots, free until the first DMA, and read back in the operand layout
+  // (loaded straight into the operand layout, every instruction read 64 bytes of each of 16
+  // heads, which the vector L1 passes at ~15 B/clk).
+  constexpr int NQH = HG4 ? 4 * 16 : 16;  // heads staged
+  constexpr int QCH = DIM / 8;            // 16-byte chunks per head
+  constexpr int QROWB = 2 * DIM + 16;     // LDS bytes per staged head (padded)
+  constexpr int QPT = (NQH * QCH + kWThreads - 1) / kWThreads;
+  const int hbase = HG4 ? 16 * (hg - wv) : 16 * hg;  // the workgroup's first head
+  uint4 qst[QPT];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, load_global16(qrow + 32 * ks));
+  for (int p = 0; p < QPT; ++p) {
+    const int f = min(p * kWThreads + tid, NQH * QCH - 1);
+    const int hh = f / QCH, c = f - hh * QCH;
+    const int h = min(hbase + hh, H - 1);
+    qst[p] = load_global16((const uint16_t*)a.q + ((int64_t)qi * H + h) * DIM + 8 * c);
   }
+  bf16x8 qb[NKS];
   const int cu_v = seq_load(a.cu_q, a.batch);
   const int t = a.q_pos[qi];
   const int b = seq_pick(a.cu_q, a.batch, qi, cu_v);
@@ -1025,10 +1036,22 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
   const uint32_t safe = (uint32_t)__shfl((int)rw[0], 0) | 0x40000000u;
 #pragma unroll
   for (int u = 0; u < RPT; ++u) row_sh[tid + kWThreads * u] = use[u] ? rw[u] : safe;
-  barrier_lds();
+  static_assert(NQH * QROWB <= (int)sizeof(slot_sh), "the query heads fit the tile slots");
+#pragma unroll
+  for (int p = 0; p < QPT; ++p) {
+    const int f = p * kWThreads + tid;
+    const int hh = f / QCH, c = f - hh * QCH;
+    if (f < NQH * QCH) *(uint4*)(slot_sh + hh * QROWB + 16 * c) = qst[p];
+  }
+  barrier_lds();  // the row words and the query heads
+  {
+    const char* qrow = slot_sh + ((HG4 ? 16 * wv : 0) + ln) * QROWB + 16 * lg;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qb[ks] = *(const bf16x8*)(qrow + 64 * ks);
+  }
+  barrier_lds();  // every wave has its Q^T: the slots may take rows
   // Q^T lives in the accumulation registers (the MFMA reads its B operand from either file):
-  // the ordinary registers then hold O^T and leave room for the PV operands in flight.  (The
-  // move waits for the Q^T loads, so it comes after the later trips were issued.)
+  // the ordinary registers then hold O^T and leave room for the PV operands in flight.
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qb[ks]));
 
