@@ -397,7 +397,8 @@ int csa_compress_index_score_launches(int num_jobs, const csa_compress_job* jobs
 
 /*
  * csa_read_probe -- a measurement utility, not a step of the method: reads `bytes` bytes of the
- * device buffer `buf` once each with 16-byte loads and writes one word per workgroup to `sink`
+ * device buffer `buf` once each with 16-byte non-temporal loads (eight in flight per thread)
+ * and writes one word per workgroup to `sink`
  * (the XOR of the words it read, so no load can be dropped).  Timed on a buffer larger than
  * the 256 MB infinity cache it gives the device's achievable streaming read bandwidth, the
  * ceiling beside the 8 TB/s peak against which the indexer score kernel is reported.
