@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
     return;
   }
   const int chunk = blockIdx.x, qi = blockIdx.y - a.comp_rows;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, lg = lane >> 4;
   const int H = a.n_heads;
   constexpr int NW = KeyGroup<KEY_DT>::NW;
@@ -305,39 +305,49 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
     my_blk = lane < nblk ? btrow[lane] : 0;
     nold = a.ctx_lens ? a.ctx_lens[b] / 4 : 0x7FFFFFFF;
   }
-  const int nold_loc = (int)max((int64_t)0, min((int64_t)nloc, (int64_t)nold - j0));
+  // (uniform: kept in a scalar register for the address arithmetic below)
+  const int nold_loc = __builtin_amdgcn_readfirstlane(
+      (int)max((int64_t)0, min((int64_t)nloc, (int64_t)nold - j0)));
   const bool any_old = nold_loc > 0;
   hist[threadIdx.x] = 0u;  // (the bound's histogram; ordered by the barrier after the query copy)
 
-  const int ntiles = (nloc + 15) >> 4;
+  const int ntiles = __builtin_amdgcn_readfirstlane((nloc + 15) >> 4);
   bf16x8 qa[HT][4];
   float wt[HT][4];
 
   // Loads and stores are unconditional (the wait counters then let the next group stay in
   // flight): entries past the chunk's end read the chunk's last row and write their unused
   // scores inside this chunk's own slice of the workspace.
+  // The address of a key row splits into a wave-uniform part (the tile's block and its place in
+  // the block: scalar arithmetic, a scalar base of the load) and the lane's row in the tile.
+  constexpr int ROW = KeyGroup<KEY_DT>::ROW;
   auto load_group = [&](int gi, KeyGroup<KEY_DT>& kg) {
-    int64_t prow_g = 0;  // row of entry ln of tile lg: one scale load covers the four tiles
+    int64_t rb_g = 0;  // for the scale: the first row of tile lg (lane group lg) ...
+    int ln_g = 0;      // ... and the lane's row in it
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       // the tile (wave-uniform) is clamped to the last one holding an old entry, so both its
-      // block and the entry (clamped to the last old one) lie before this step's entries: the
-      // rows the compressor workgroups of a fused launch write are never read
+      // block and the entry (clamped to the last old one, in the tile's own block) lie before
+      // this step's entries: the rows the compressor workgroups of a fused launch write are
+      // never read
       const int tile = min(min(16 * gi + 4 * u + wv, ntiles - 1), (nold_loc - 1) >> 4);
-      const int eloc = min(tile * 16 + ln, nold_loc - 1);
       const int blk = __builtin_amdgcn_readlane(my_blk, tile >> 2);
-      const int64_t prow = ((int64_t)blk << 6) + (eloc & 63);
-      prow_g = lg == u ? prow : prow_g;
+      const int64_t rbase = ((int64_t)blk << 6) + 16 * (tile & 3);  // (uniform)
+      const int lnc = min(ln, nold_loc - 1 - 16 * tile);
+      rb_g = lg == u ? rbase : rb_g;
+      ln_g = lg == u ? lnc : ln_g;
       // load i reads one 64-byte half line of each of the tile's 16 rows: lane group lg takes
       // bytes 64 i + 16 lg .. +15 (the K order of the A operand matches)
       // (fp4: one load, dims 32 lg .. 32 lg + 31, and the scale bytes 2 lg, 2 lg + 1 of the
       // row's eight, one per 16 dims)
-      const uint4* src = (const uint4*)((const uint8_t*)a.cache.rows + prow * KeyGroup<KEY_DT>::ROW + 16 * lg);
+      const uint8_t* tb = (const uint8_t*)a.cache.rows + rbase * ROW;
+      const uint4* src = (const uint4*)(tb + lnc * ROW + 16 * lg);
 #pragma unroll
       for (int i = 0; i < NW; ++i) kg.raw[u][i] = src[4 * i];
-      if constexpr (KEY_DT == CSA_FP4_E2M1) kg.sc4[u] = ((const uint16_t*)a.cache.scales)[prow * 4 + lg];
+      if constexpr (KEY_DT == CSA_FP4_E2M1)
+        kg.sc4[u] = ((const uint16_t*)a.cache.scales)[(rbase + lnc) * 4 + lg];
     }
-    if constexpr (KEY_DT == CSA_FP8_E4M3) kg.scale = a.cache.scales[prow_g];
+    if constexpr (KEY_DT == CSA_FP8_E4M3) kg.scale = a.cache.scales[rb_g + ln_g];
     else kg.scale = 1.f;
   };
 
