@@ -261,9 +261,19 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
   constexpr int NW = KeyGroup<KEY_DT>::NW;
   // First trip: everything that needs only the workgroup's coordinates goes out together -- the
   // query (heads x 128 bf16, 16 bytes per thread and pass; rows past the last head are read
-  // clamped and zeroed after) and head weights, read once per workgroup and shared through
+  // clamped and stored to LDS as zeros) and head weights, read once per workgroup and shared through
   // LDS, the sequence table and the query's position.
-  const int t_q = a.q_pos[qi];
+  // Speculatively, in the same trip: the chunk's block ids (lane i: block i of the chunk) and
+  // the entry count of sequence bg = the query's own index -- a decode call holds one query per
+  // sequence, so the guess holds there and the second trip below is skipped (the loads stay
+  // inside sequence bg's block-table row whatever they fetch).  The key loads wait for the
+  // block ids and the sequence table only: those go out first (vector loads complete in issue
+  // order), the query and weights behind them.
+  const int64_t j0 = (int64_t)chunk * C;
+  const int bg = min(a.q_base + qi, a.batch - 1);
+  const int32_t blk_g =
+      a.cache.bt[(int64_t)bg * a.cache.bt_stride + min((int)(j0 >> 6) + lane, a.cache.bt_stride - 1)];
+  const int cu_v = seq_load(a.cu_q, a.batch);
   uint4 qv[HT];
   const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)qi * H * 128;
 #pragma unroll
@@ -272,22 +282,11 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
     qv[p] = load_global16(qrow + (int64_t)h * 128 + 8 * (threadIdx.x & 15));
   }
   const float w_ld = a.w[(int64_t)qi * H + min((int)threadIdx.x, H - 1)];
-  const int cu_v = seq_load(a.cu_q, a.batch);
-  // Speculatively, in the same trip: the chunk's block ids (lane i: block i of the chunk) and
-  // the entry count of sequence bg = the query's own index -- a decode call holds one query per
-  // sequence, so the guess holds there and the second trip below is skipped (the loads stay
-  // inside sequence bg's block-table row whatever they fetch).
-  const int64_t j0 = (int64_t)chunk * C;
-  const int bg = min(a.q_base + qi, a.batch - 1);
-  const int32_t blk_g =
-      a.cache.bt[(int64_t)bg * a.cache.bt_stride + min((int)(j0 >> 6) + lane, a.cache.bt_stride - 1)];
+  const int t_q = a.q_pos[qi];
   const int ctx_g = a.ctx_lens ? a.ctx_lens[bg] : 0;
   asm volatile("" ::"s"(t_q));  // (the position's load stays in this trip, not behind the next)
   const int n = min((t_q + 1) / 4, a.n_max);  // (query_entries)
   const int b = seq_pick(a.cu_q, a.batch, a.q_base + qi, cu_v);
-#pragma unroll
-  for (int p = 0; p < HT; ++p)
-    if (16 * p + (int)(threadIdx.x >> 4) >= H) qv[p] = make_uint4(0, 0, 0, 0);
   const float wv_h = threadIdx.x < 16 * HT && threadIdx.x < H ? w_ld : 0.f;
   if (j0 >= n) return;
   const int nloc = (int)min((int64_t)C, n - j0);
@@ -303,6 +302,7 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
   } else {
     const int32_t* btrow = a.cache.bt + (int64_t)b * a.cache.bt_stride + (j0 >> 6);
     my_blk = lane < nblk ? btrow[lane] : 0;
+    asm volatile("" ::"v"(my_blk));  // (waited for here: the common path waits for less)
     nold = a.ctx_lens ? a.ctx_lens[b] / 4 : 0x7FFFFFFF;
   }
   // (uniform: kept in a scalar register for the address arithmetic below)
@@ -385,34 +385,36 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
   // conditions, so the wait counters keep one group of keys in flight behind the MFMA work
   constexpr int NG = C / 256;
   KeyGroup<KEY_DT> kg[2];
-  if (any_old) load_group(0, kg[0]);
-#pragma unroll
-  for (int p = 0; p < HT; ++p)
-    *(uint4*)&q_sh[(16 * p + (threadIdx.x >> 4)) * QROW + 8 * (threadIdx.x & 15)] = qv[p];
-  if (threadIdx.x < 16 * HT) w_sh[threadIdx.x] = wv_h;
-  __syncthreads();
-  // A operands (the dims each key lane holds, q_operand_dim)
-#pragma unroll
-  for (int mt = 0; mt < HT; ++mt) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int d0 = q_operand_dim<KEY_DT>(ks, lg);
-      qa[mt][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)&q_sh[(16 * mt + ln) * QROW + d0]);
-    }
-    const float4 w4 = *(const float4*)&w_sh[16 * mt + 4 * lg];
-    wt[mt][0] = w4.x;
-    wt[mt][1] = w4.y;
-    wt[mt][2] = w4.z;
-    wt[mt][3] = w4.w;
-  }
-
   if (any_old) {
+    // (the query copy sits on this path only, so its wait leaves the first group in flight)
+    load_group(0, kg[0]);
+#pragma unroll
+    for (int p = 0; p < HT; ++p)
+      *(uint4*)&q_sh[(16 * p + (threadIdx.x >> 4)) * QROW + 8 * (threadIdx.x & 15)] =
+          16 * p + (int)(threadIdx.x >> 4) < H ? qv[p] : make_uint4(0, 0, 0, 0);  // (rows past H: 0)
+    if (threadIdx.x < 16 * HT) w_sh[threadIdx.x] = wv_h;
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);  // (no key work hoisted above the barrier: it would wait)
+    // A operands (the dims each key lane holds, q_operand_dim)
+#pragma unroll
+    for (int mt = 0; mt < HT; ++mt) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int d0 = q_operand_dim<KEY_DT>(ks, lg);
+        qa[mt][ks] = __builtin_bit_cast(bf16x8, *(const uint4*)&q_sh[(16 * mt + ln) * QROW + d0]);
+      }
+      const float4 w4 = *(const float4*)&w_sh[16 * mt + 4 * lg];
+      wt[mt][0] = w4.x;
+      wt[mt][1] = w4.y;
+      wt[mt][2] = w4.z;
+      wt[mt][3] = w4.w;
+    }
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       if (gi + 1 < NG) load_group(gi + 1, kg[(gi + 1) & 1]);
       compute_group(gi, kg[gi & 1]);
     }
-  } else {  // every entry of the chunk is this step's
+  } else {  // every entry of the chunk is this step's: no query needed
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) lane_keys[gi] = 0u;
   }
