@@ -245,8 +245,7 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
   __shared__ __attribute__((aligned(16))) float sc_sh[C];
   __shared__ __attribute__((aligned(16))) uint16_t q_sh[HT * 16 * QROW];
   __shared__ __attribute__((aligned(16))) float w_sh[HT * 16];
-  __shared__ uint32_t hist[256];
-  __shared__ int misc[4];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4 * 256];  // a histogram per wave
   __shared__ uint32_t red[4], red2[4];
   __shared__ CompressSmem<8> csm;
   if ((int)blockIdx.y < a.comp_rows) {  // a compressor workgroup of the fused launch
@@ -309,7 +308,7 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
   const int nold_loc = __builtin_amdgcn_readfirstlane(
       (int)max((int64_t)0, min((int64_t)nloc, (int64_t)nold - j0)));
   const bool any_old = nold_loc > 0;
-  hist[threadIdx.x] = 0u;  // (the bound's histogram; ordered by the barrier after the query copy)
+  ((uint4*)hist)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);  // (ordered by the range barrier)
 
   const int ntiles = __builtin_amdgcn_readfirstlane((nloc + 15) >> 4);
   bf16x8 qa[HT][4];
@@ -444,38 +443,105 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
     red2[wv] = khi;
   }
   __syncthreads();
-  // the chunk's scores leave in full lines, 16 bytes per thread and pass (this step's entries,
-  // written by the compressor, are skipped)
-  if (nold_loc == nloc) {
-    float4* dst = (float4*)(a.scores + (int64_t)qi * a.n_cap + j0);
+  // From here thread t takes entries 8 t .. 8 t + 7 (wave w: entries 512 w .. 512 w + 511): the
+  // chunk's scores leave in full lines (this step's entries, written by the compressor, are
+  // skipped), and the candidates are listed in entry order.
+  const int base = 8 * threadIdx.x;
+  const float4 s0 = *(const float4*)&sc_sh[base], s1 = *(const float4*)&sc_sh[base + 4];
+  const float v8[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  {
+    float* dst = a.scores + (int64_t)qi * a.n_cap + j0 + base;
+    if (nold_loc == nloc) {
+      ((float4*)dst)[0] = s0;
+      ((float4*)dst)[1] = s1;
+    } else {
 #pragma unroll
-    for (int p = 0; p < C / 1024; ++p)
-      dst[p * 256 + threadIdx.x] = *(const float4*)&sc_sh[4 * (p * 256 + threadIdx.x)];
-  } else {
-    float* dst = a.scores + (int64_t)qi * a.n_cap + j0;
-    for (int e = threadIdx.x; e < C; e += 256)
-      if (e < nold_loc || e >= nloc) dst[e] = any_old ? sc_sh[e] : 0.f;
+      for (int i = 0; i < 8; ++i)
+        if (base + i < nold_loc || base + i >= nloc) dst[i] = any_old ? v8[i] : 0.f;
+    }
   }
   if (chunk == 0 && threadIdx.x == 0) a.new_from[qi] = min(nold, n);
   // the candidates: a lower bound of the kc2-th largest scored entry (one 256-bin histogram over
-  // the scored entries' key range, from the keys the lanes hold) and every scored entry at or
-  // above it; a chunk with at most kc2 scored entries gives them all
+  // the scored entries' key range) and every scored entry at or above it; a chunk with at most
+  // kc2 scored entries gives them all
   const int kc2 = chunk_quota(a.k, n);
   if (kc2 == 0) return;  // the select takes every entry
+  const uint32_t lo = min(min(red[0], red[1]), min(red[2], red[3]));
+  const uint32_t hi = max(max(red2[0], red2[1]), max(red2[2], red2[3]));
+  uint32_t key[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) key[i] = f2key(v8[i]);
   uint32_t bound = 0u;
-  if (nold_loc > kc2) {
-    const uint32_t lo = min(min(red[0], red[1]), min(red[2], red[3]));
-    const uint32_t hi = max(max(red2[0], red2[1]), max(red2[2], red2[3]));
-    const int shift = max(0, bit_len(hi - lo) - 8);
+  int wbase, total;  // the wave's first list slot, the chunk's candidate count
+  if (nold_loc > kc2) {  // (uniform)
+    // each wave counts its own entries, so after one barrier every wave finds the crossing bin
+    // and the count of candidates in the waves before it from the four histograms
+    // (key 0, left out of the range, is left out here too: it is below every bound >= lo)
+    const int shift = max(0, bit_len(hi - lo) - 8);  // ((hi - lo) >> shift < 256)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (lane_keys[i]) atomicAdd(&hist[((lane_keys[i] - lo) >> shift) & 255u], 1u);
+      if (base + i < nold_loc && key[i]) atomicAdd(&hist[256 * wv + (((key[i] - lo) >> shift) & 255u)], 1u);
     __syncthreads();
-    if (wv == 0) pick_bin_wave0(hist, kc2, misc);  // (the crossing lane writes misc[0])
-    __syncthreads();
-    bound = lo + ((uint32_t)misc[0] << shift);
+    // lane l: bins 255 - 4 l - i, i = 0..3, of each wave's histogram
+    uint32_t hb[4][4], tot[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint4 h4 = *(const uint4*)&hist[256 * w + 252 - 4 * lane];
+      hb[w][0] = h4.w;
+      hb[w][1] = h4.z;
+      hb[w][2] = h4.y;
+      hb[w][3] = h4.x;
+    }
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tot[i] = hb[0][i] + hb[1][i] + hb[2][i] + hb[3][i];
+      local += tot[i];
+    }
+    // the bin where the count from the top first reaches kc2 (the histogram holds nold_loc >
+    // kc2 entries, so some lane's inclusive count does)
+    const uint32_t incl = (uint32_t)wave_incl_scan((int)local);
+    const unsigned long long hit = __ballot(incl >= (uint32_t)kc2);
+    const int first = hit ? __ffsll(hit) - 1 : 63;
+    uint32_t cum = incl - local;
+    int binl = 252 - 4 * lane;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!found && cum + tot[i] >= (uint32_t)kc2) {
+        binl = 255 - 4 * lane - i;
+        found = true;
+      }
+      cum += tot[i];
+    }
+    const int bsel = __builtin_amdgcn_readlane(binl, first);
+    bound = lo + ((uint32_t)bsel << shift);
+    // a scored key is >= bound exactly when its bin is >= bsel; both counts (<= C each) share
+    // one 32-bit sum: the waves before this one (low half) and all four (high half)
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (255 - 4 * lane - i >= bsel)
+        packed += (tot[i] << 16) + (wv > 0 ? hb[0][i] : 0u) + (wv > 1 ? hb[1][i] : 0u) + (wv > 2 ? hb[2][i] : 0u);
+    packed = wave_reduce(packed, [](uint32_t x, uint32_t y) { return x + y; });
+    wbase = (int)(packed & 0xFFFFu);
+    total = (int)(packed >> 16);
+  } else {  // every scored entry
+    wbase = min(nold_loc, 512 * wv);
+    total = nold_loc;
   }
-  emit_chunk(a, qi, chunk, nold_loc, bound, sc_sh, (int*)hist);
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cnt += base + i < nold_loc && key[i] >= bound ? 1 : 0;
+  int off = wbase + wave_incl_scan(cnt) - cnt;
+  uint2* cdst = a.cand + (int64_t)qi * a.n_cap + j0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (base + i < nold_loc && key[i] >= bound) cdst[off++] = make_uint2(key[i], (uint32_t)(j0 + base + i));
+  // the list's key range: its largest key is the chunk's; the bound stands in for its least when
+  // the bound selects (a lower bound of every listed key, which is all the select needs)
+  if (threadIdx.x == 0)
+    a.cand_info[(int64_t)qi * a.chunks + chunk] = make_int4(total, (int)(nold_loc > kc2 ? bound : lo), (int)hi, (int)bound);
 }
 
 // ---- Query-tiled MFMA score kernel, for calls whose sequences bring many queries (a chunked
