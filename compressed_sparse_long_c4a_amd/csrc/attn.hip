@@ -683,7 +683,7 @@ __global__ __launch_bounds__(kF8Threads) void attn_partial_fp8(Args a) {
   const int n_w = min(a.window, t + 1);
   const int n_rows = n_c + n_w;
   const int nrows = (n_w > 0 || n_vis > 0) ? max(0, min(a.rows_per_split, n_rows - r_begin)) : 0;
-  // padded to whole steps; rows_per_split is a multiple of kStepF8
+  // padded to whole steps (the last one may be partial: rows_per_split is a multiple of 32)
   const int nrows_p = (nrows + kStepF8 - 1) / kStepF8 * kStepF8;
   const int steps = nrows_p / kStepF8;
 
@@ -786,18 +786,27 @@ __global__ __launch_bounds__(kF8Threads) void attn_partial_fp8(Args a) {
   // One step over the tile in `tl`, which is refilled with step `next` (or the stand-in row).
   auto step = [&](int i, Tile& tl, int next) {
     const int r0 = kStepF8 * i;
+    // rows of the step that exist: a split's last step may hold fewer than kStepF8; its 32-row
+    // blocks past them are neither staged, nor multiplied, nor read by PV (their P is 0: the
+    // padding rows' scale is 0)
+    const int live = nrows - r0;
+    const bool my_live = 32 * kb < live;  // (wave-uniform)
     barrier_lds();  // #0: every wave is past the previous step's PV (the row buffer is free)
+    if (my_live) {
 #pragma unroll
-    for (int j = 0; j < NSEG; ++j) *(uint4*)(v_sh + lrow_j[j] * VROW + lofs_j[j]) = tl.d[j];
+      for (int j = 0; j < NSEG; ++j) *(uint4*)(v_sh + lrow_j[j] * VROW + lofs_j[j]) = tl.d[j];
+    }
     load_step(next, tl);
     // S^T of this wave's 16 rows over the full width, two accumulation chains (the rows back
     // from LDS in the operand layout; this wave wrote them)
     f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if (my_live) {
 #pragma unroll
-    for (int m = 0; m < NSEG; ++m) {
-      const uint4 x = *(const uint4*)(vrow_w + 64 * m);
-      acc2[0] = mfma16x16x32(fp8x8_to_bf16x8(x.x, x.y), qb[2 * m], acc2[0]);
-      acc2[1] = mfma16x16x32(fp8x8_to_bf16x8(x.z, x.w), qb[2 * m + 1], acc2[1]);
+      for (int m = 0; m < NSEG; ++m) {
+        const uint4 x = *(const uint4*)(vrow_w + 64 * m);
+        acc2[0] = mfma16x16x32(fp8x8_to_bf16x8(x.x, x.y), qb[2 * m], acc2[0]);
+        acc2[1] = mfma16x16x32(fp8x8_to_bf16x8(x.z, x.w), qb[2 * m + 1], acc2[1]);
+      }
     }
     const f32x4 sacc = acc2[0] + acc2[1];
     const float4 rs4 = *(const float4*)&scale_sh[r0 + srow0];
@@ -848,6 +857,7 @@ __global__ __launch_bounds__(kF8Threads) void attn_partial_fp8(Args a) {
     // O^T += V^T . P^T over the step, one 32-row block at a time (P_hi and P_lo MFMAs)
 #pragma unroll
     for (int kh = 0; kh < kF8Waves / 2; ++kh) {
+      if (32 * kh >= live) break;  // (uniform across the workgroup)
       const bf16x8 pa = __builtin_bit_cast(bf16x8, p_sh[2 * kh][lane]);
       const bf16x8 pb = __builtin_bit_cast(bf16x8, p_sh[2 * kh + 1][lane]);
       const bf16x8 phi = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
@@ -1466,9 +1476,11 @@ AttnPlan attn_plan(int total_q, int n_heads, int ratio, int has_topk, int k, int
   p.head_groups = (n_heads + 15) / 16;
   const int64_t blocks32 = std::max<int64_t>(1, (p.max_rows + 31) / 32);
   const int64_t units = (int64_t)total_q * p.head_groups;
-  // aim at one workgroup per compute unit (256 CUs); a split is a whole number of 128-row
-  // steps (the fp8-row kernel's step; the generic kernel's is 32 rows)
-  const int64_t sb = 4;  // 32-row blocks per step
+  // aim at one workgroup per compute unit (256 CUs).  The generic kernel's splits are whole
+  // numbers of 128-row blocks; the fp8-row kernel's are cut at 32 rows (its last step may be
+  // partial: the 32-row blocks past the split's rows are skipped), so that e.g. 4 queries x 8
+  // head groups x 2,176 rows take 8 splits of 288 rows on 256 compute units, not 6 of 384 on 192
+  const int64_t sb = rows_cap == kAttnRowsCapFp8 ? 1 : 4;  // 32-row blocks per unit of a split
   int64_t bpw = std::max<int64_t>(sb, (blocks32 * units + 255) / 256);
   bpw = std::min<int64_t>((std::min(bpw, blocks32) + sb - 1) / sb * sb, rows_cap / 32);
   // (max_rows <= kAttnMaxRows keeps splits <= 512 and the partial workspace finite)
