@@ -12,7 +12,8 @@ trials of K steps replayed from a HIP graph (one step per cache replica in the g
 pages deploy with full graphs; the same K steps issued eagerly are timed too
 (ms_per_step_eager), and so is the pages' two-stream schedule, eagerly and from a graph.  The
 dominant kernel (the index score launch) is timed with HIP events around 20 of its launches
-back to back in a graph, which is what the kernel trace's average duration measures; the
+back to back in a graph, in short trials after the GPU has rested (as its launches inside the
+step run), which is what the kernel trace's average duration measures; the
 events around each launch inside the eager loop also hold the command processor's dispatch
 (launch_us_in_step).
 
@@ -370,15 +371,26 @@ def graph_of(fn, reps):
     return graph
 
 
-def back_to_back_ms(launch, reps, n: int = 20) -> float:
+def back_to_back_ms(launch, reps, n: int = 20, trials: int = 10, rest_s: float = 0.02) -> float:
     """Milliseconds per call of launch(g): n calls back to back in one HIP graph, g rotating over
-    the cache replicas reps, median of the timed trials."""
+    the cache replicas reps; each trial replays the graph once after the GPU has been idle for
+    rest_s, and the median trial is taken.  Short rested trials see the kernel as the step does
+    (between the step's latency-bound launches); hundreds of HBM-bound launches in a row raise the
+    board's power to ~1.25 kW and lower the gfx clock, and the launch times then drift upward."""
     import torch
     graph = graph_of(lambda _g: [launch(reps[i % len(reps)]) for i in range(n)], reps[:1])
-    ms = statistics.median(time_graph(graph, 10)) / n
+    out = []
+    for _ in range(trials):
+        time.sleep(rest_s)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / n)
     del graph
     torch.cuda.synchronize()
-    return ms
+    return statistics.median(out)
 
 
 def time_graph(graph, replays: int, trials: int = TRIALS) -> list:

@@ -952,6 +952,42 @@ __global__ __launch_bounds__(kF8Threads) void attn_partial_fp8(Args a) {
 // Q^T and the whole O^T of its heads; the waves' (m, l, O) are merged through LDS at the end and
 // one partial row per head leaves from registers.
 constexpr int kWWaves = 4;
+
+// NKS 16-byte LDS reads, k-step ks from base a(ks % 2) + 1024 (ks / 2), issued in one asm block
+// that waits for all of them (so no result register is live while its read is in flight).
+typedef unsigned int lds_u32x4 __attribute__((ext_vector_type(4)));
+#define CSA_R(i, b, o) "ds_read_b128 %" #i ", %" #b " offset:" #o "\n\t"
+template <int NKS>
+__device__ __forceinline__ void lds_read_tile(uint4 (&d)[NKS], uint32_t a0, uint32_t a1) {
+  static_assert(NKS == 16 || NKS == 18, "row widths of 512 or 576 bf16");
+  lds_u32x4 v[18];
+  if constexpr (NKS == 18) {
+    asm volatile(CSA_R(0, 18, 0) CSA_R(1, 19, 0) CSA_R(2, 18, 1024) CSA_R(3, 19, 1024)
+                 CSA_R(4, 18, 2048) CSA_R(5, 19, 2048) CSA_R(6, 18, 3072) CSA_R(7, 19, 3072)
+                 CSA_R(8, 18, 4096) CSA_R(9, 19, 4096) CSA_R(10, 18, 5120) CSA_R(11, 19, 5120)
+                 CSA_R(12, 18, 6144) CSA_R(13, 19, 6144) CSA_R(14, 18, 7168) CSA_R(15, 19, 7168)
+                 CSA_R(16, 18, 8192) CSA_R(17, 19, 8192) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+                   "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
+                   "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17])
+                 : "v"(a0), "v"(a1)
+                 : "memory");
+  } else {
+    asm volatile(CSA_R(0, 16, 0) CSA_R(1, 17, 0) CSA_R(2, 16, 1024) CSA_R(3, 17, 1024)
+                 CSA_R(4, 16, 2048) CSA_R(5, 17, 2048) CSA_R(6, 16, 3072) CSA_R(7, 17, 3072)
+                 CSA_R(8, 16, 4096) CSA_R(9, 17, 4096) CSA_R(10, 16, 5120) CSA_R(11, 17, 5120)
+                 CSA_R(12, 16, 6144) CSA_R(13, 17, 6144) CSA_R(14, 16, 7168) CSA_R(15, 17, 7168)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+                   "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
+                   "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+                 : "v"(a0), "v"(a1)
+                 : "memory");
+  }
+#pragma unroll
+  for (int k = 0; k < NKS; ++k) d[k] = make_uint4(v[k][0], v[k][1], v[k][2], v[k][3]);
+}
+#undef CSA_R
 constexpr int kWThreads = 64 * kWWaves;
 static_assert(kRowsPerSplit % kWThreads == 0 && kRowsPerSplit % (16 * kWWaves) == 0, "split size");
 template <int DIM, bool HG4>
@@ -1103,17 +1139,18 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
                                          16, 0, 0);
     }
   };
+  // k-step ks of row ln sits at byte 64 ks + 16 lg of the row: line ks / 2 of its place, piece
+  // p = (4 (ks % 2) + lg) % 8, stored at piece p ^ (ln % 8); so the reads of even and of odd
+  // k-steps each take one base address plus 1024 (ks / 2).  They are issued from one asm block
+  // that also waits for them: the compiler cannot tell which slot an LDS DMA writes, and before
+  // a plain LDS read of a slot it waits for every DMA in flight (the next tile's too), which
+  // would undo the two-tile prefetch; the DMA of this tile is waited for explicitly instead.
   auto read_tile = [&](int j, Tile& tl) __attribute__((always_inline)) {
-    const lds_char* slot = slots + (j & 1) * SLOT;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int byte = 64 * ks + 16 * lg;  // of row ln
-      const int p = (byte >> 4) & 7;
-      const int off = ((ln >> 3) * NL + (byte >> 7)) * 1024 + (ln & 7) * 128 + ((p ^ (ln & 7)) << 4);
-      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(slot + off);
-      tl.d[ks] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
+    const uint32_t slot = (uint32_t)(uintptr_t)(slots + (j & 1) * SLOT);
+    const uint32_t rbase = slot + (ln >> 3) * NL * 1024 + (ln & 7) * 128;
+    const uint32_t a0 = rbase + (((lg & 7) ^ (ln & 7)) << 4);        // even k-steps
+    const uint32_t a1 = rbase + ((((4 + lg) & 7) ^ (ln & 7)) << 4);  // odd k-steps
+    lds_read_tile<NKS>(tl.d, a0, a1);
   };
 
   f32x4 o[NDT];  // O^T: dim tile 16 dt .. +15 x 16 heads
@@ -1197,16 +1234,15 @@ __global__ __launch_bounds__(kWThreads) void attn_partial_w(Args a) {
   // The wave's own wait counts order its DMA and its LDS reads (no other load of this wave is in
   // flight in the loop): with tile j + 1's DMA issued after tile j's, tile j has landed once at
   // most that many loads are outstanding, and its slot may take tile j + 2 once the operand
-  // reads are back (lgkmcnt 0).
-  constexpr int kVmcnt0 = 0x0F70, kLgkmcnt0 = 0xC07F;
+  // reads are back (read_tile waits for them).
+  constexpr int kVmcnt0 = 0x0F70;
   constexpr int kVmcntTile = 0x0F70 | ((2 * NL) & 15) | (((2 * NL) >> 4) << 14);  // vmcnt(2 NL)
   dma_tile(0);
   dma_tile(1);
   for (int j = 0; j < ntw; ++j) {
     Tile cur;
     __builtin_amdgcn_s_waitcnt(kVmcntTile);
-    read_tile(j, cur);
-    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+    read_tile(j, cur);  // (its reads are complete when it returns: the slot is free)
     dma_tile(j + 2);
     f32x4 tq[kLead][2];
     const bf16x8 pb = qk_softmax(j, cur, tq);
