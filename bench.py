@@ -373,16 +373,19 @@ def graph_of(fn, reps):
 
 def back_to_back_ms(launch, reps, n: int = 20, trials: int = 10, rest_s: float = 0.02) -> float:
     """Milliseconds per call of launch(g): n calls back to back in one HIP graph, g rotating over
-    the cache replicas reps; each trial replays the graph once after the GPU has been idle for
-    rest_s, and the median trial is taken.  Short rested trials see the kernel as the step does
-    (between the step's latency-bound launches); hundreds of HBM-bound launches in a row raise the
-    board's power to ~1.25 kW and lower the gfx clock, and the launch times then drift upward."""
+    the cache replicas reps.  Each trial starts after the GPU has been idle for rest_s, replays
+    the graph once untimed (the clocks come back up from idle, and the timed replay's packets are
+    queued while it runs, so the host's submission is not timed) and then once between events;
+    the median trial is taken.  Short trials see the kernel as the step does (between the step's
+    latency-bound launches); hundreds of HBM-bound launches in a row raise the board's power to
+    ~1.25 kW and lower the gfx clock, and the launch times then drift upward."""
     import torch
     graph = graph_of(lambda _g: [launch(reps[i % len(reps)]) for i in range(n)], reps[:1])
     out = []
     for _ in range(trials):
         time.sleep(rest_s)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        graph.replay()
         a.record()
         graph.replay()
         b.record()
