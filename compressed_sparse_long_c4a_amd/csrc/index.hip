@@ -557,8 +557,13 @@ __global__ __launch_bounds__(256, KEY_DT == CSA_BF16 ? 2 : 3) void index_score_m
 // lane l with entry 64 h + l of the group's half h: the scores leave in full lines as each group
 // ends and also stay in the wave's registers.  Each wave then finishes its query alone and
 // emits its candidates in entry order by ballots (same bound and output as index_score_mfma).
-constexpr int kQT = 4;   // queries per workgroup (one per wave)
-constexpr int kGT = 8;   // tiles per group
+// (eight queries per workgroup, one workgroup of eight waves per compute unit, converted each
+// chunk once per compute unit but ran in lock-step and lost the overlap of two independent
+// four-wave workgroups: prefill score 1,129 against 1,023 us)
+constexpr int kQT = 4;        // queries per workgroup (one per wave)
+constexpr int kGT = 8;        // tiles per group
+constexpr int kTPW = kGT / kQT;  // tiles a wave loads and converts per group
+static_assert(kGT % kQT == 0, "whole tiles per wave");
 
 // Workgroup t of the query-tiled grid -> sequence b and its queries q0 .. q0 + nq - 1 (tiles
 // of kQT consecutive queries inside each sequence's part of the queries [qs, qe), in sequence
@@ -593,7 +598,7 @@ __device__ bool query_tile(const int32_t* cu_q, int batch, int qs, int qe, int t
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int KEY_DT, int HT>
-__global__ __launch_bounds__(256) void index_score_qt(ScoreArgs a) {
+__global__ __launch_bounds__(64 * kQT) void index_score_qt(ScoreArgs a) {
   using KG = KeyGroup<KEY_DT>;
   constexpr int NW = KG::NW;
   constexpr int NG = C / (16 * kGT);  // groups per chunk
@@ -654,15 +659,15 @@ __global__ __launch_bounds__(256) void index_score_qt(ScoreArgs a) {
   // the wave's two tiles of group g (tiles past the chunk's end repeat its last one; entries
   // past it read its last entry)
   struct Raw {
-    uint4 raw[2][NW];
-    uint32_t sc4[2];
-    float scale;  // fp8, lane (e, u < 2): scale of entry e of the wave's tile u
+    uint4 raw[kTPW][NW];
+    uint32_t sc4[kTPW];
+    float scale;  // fp8, lane (e, u < kTPW): scale of entry e of the wave's tile u
   };
   auto load_tiles = [&](int g, Raw& r) {
     int64_t prow_s = 0;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tile = min(kGT * g + 4 * u + wv, ntiles - 1);
+    for (int u = 0; u < kTPW; ++u) {
+      const int tile = min(kGT * g + kQT * u + wv, ntiles - 1);
       const int eloc = min(tile * 16 + ln, nloc - 1);
       const int blk = __builtin_amdgcn_readlane(my_blk, tile >> 2);
       const int64_t prow = ((int64_t)blk << 6) + (eloc & 63);
@@ -677,13 +682,13 @@ __global__ __launch_bounds__(256) void index_score_qt(ScoreArgs a) {
   };
   auto store_tiles = [&](int buf, const Raw& r) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kTPW; ++u) {
       bf16x8 kb[4];
       key_operands<KEY_DT, NW>(r.raw[u], r.sc4[u], kb);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kb_sh[buf][4 * u + wv][ks][lane] = __builtin_bit_cast(uint4, kb[ks]);
+      for (int ks = 0; ks < 4; ++ks) kb_sh[buf][kQT * u + wv][ks][lane] = __builtin_bit_cast(uint4, kb[ks]);
     }
-    if (KEY_DT == CSA_FP8_E4M3 && lg < 2) ksc_sh[buf][4 * lg + wv][ln] = r.scale;
+    if (KEY_DT == CSA_FP8_E4M3 && lg < kTPW) ksc_sh[buf][kQT * lg + wv][ln] = r.scale;
   };
 
   Raw raw;
@@ -1299,10 +1304,10 @@ hipError_t launch_compress_index_score(const IndexLaunch& a, const IndexWorkspac
 template <int KEY_DT>
 void launch_qt(const ScoreArgs& s, int ht, dim3 grid, hipStream_t stream) {
   switch (ht) {
-    case 1: hipLaunchKernelGGL((index_score_qt<KEY_DT, 1>), grid, dim3(256), 0, stream, s); break;
-    case 2: hipLaunchKernelGGL((index_score_qt<KEY_DT, 2>), grid, dim3(256), 0, stream, s); break;
-    case 3: hipLaunchKernelGGL((index_score_qt<KEY_DT, 3>), grid, dim3(256), 0, stream, s); break;
-    default: hipLaunchKernelGGL((index_score_qt<KEY_DT, 4>), grid, dim3(256), 0, stream, s); break;
+    case 1: hipLaunchKernelGGL((index_score_qt<KEY_DT, 1>), grid, dim3(64 * kQT), 0, stream, s); break;
+    case 2: hipLaunchKernelGGL((index_score_qt<KEY_DT, 2>), grid, dim3(64 * kQT), 0, stream, s); break;
+    case 3: hipLaunchKernelGGL((index_score_qt<KEY_DT, 3>), grid, dim3(64 * kQT), 0, stream, s); break;
+    default: hipLaunchKernelGGL((index_score_qt<KEY_DT, 4>), grid, dim3(64 * kQT), 0, stream, s); break;
   }
 }
 
