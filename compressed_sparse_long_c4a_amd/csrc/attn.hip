@@ -618,8 +618,9 @@ __global__ __launch_bounds__(kThreads) void attn_partial(Args a) {
 // counters wait for exactly the loads a value needs and the next step's rows stay in flight
 // meanwhile.  The dependent trips are: (query position, sequence, list entries, query heads)
 // -> block table -> (row scales, then rows).
-// The waves stage the fp8 codes they loaded in LDS (three barriers per step: the row buffer is
-// free, the tiles' maxima, P), read their own rows back for QK, and PV reads them transposed with
+// The waves stage the fp8 codes they loaded in LDS (two barriers per step: the row buffer is
+// free; the tiles' maxima with P against the current softmax reference, and a third when the
+// reference moves), read their own rows back for QK, and PV reads them transposed with
 // ds_read_b64_tr_b8 (a 16-lane group reads an 8-row x 16-byte block and lane l receives column
 // l of the 8 rows), which is exactly the A operand of V^T with K = 32 rows: the MFMA rows of
 // the two QK tiles of a 32-row block are interleaved (tile h holds rows 8 (r / 4) + 4 h + r % 4)
@@ -819,23 +820,11 @@ __global__ __launch_bounds__(kF8Threads) void attn_partial_fp8(Args a) {
       mloc = fmaxf(mloc, z[j]);
     }
     mloc = rows_reduce(mloc, [](float x, float y) { return fmaxf(x, y); });
-    if (lg == 0) mx_sh[wv][ln] = mloc;
-    barrier_lds();  // #1: the tiles' maxima
-    float mblk = mx_sh[0][ln];
-#pragma unroll
-    for (int w = 1; w < kF8Waves; ++w) mblk = fmaxf(mblk, mx_sh[w][ln]);
-    // the reference moves only when a step's maximum exceeds it by more than kSlack (always
-    // when it has none yet); every wave takes the same decision
-    const bool move = mblk > m_ref + kSlack;
-    if (__ballot(move)) {
-      const float m_new = move ? mblk : m_ref;
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DTW; ++dt) o[dt] *= alpha;
-    }
-    {
+    // P of this wave's tile against the reference m_ref, published with the tile's maximum:
+    // unless the step's maximum moves the reference (the first step, then rarely), that P is
+    // final and one barrier publishes both; when it moves, every wave rescales, recomputes P
+    // and passes one more barrier (the decision is the same in every wave)
+    auto make_p = [&]() -> float {
       float pvv[4], psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -843,7 +832,6 @@ __global__ __launch_bounds__(kF8Threads) void attn_partial_fp8(Args a) {
         psum += p;
         pvv[j] = p * rs[j];
       }
-      l_run += psum;
       bf16x8 hl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -852,8 +840,28 @@ __global__ __launch_bounds__(kF8Threads) void attn_partial_fp8(Args a) {
         hl[4 + j] = (__bf16)(pvv[j] - (float)hi);
       }
       p_sh[wv][lane] = __builtin_bit_cast(uint4, hl);
+      return psum;
+    };
+    float psum = make_p();
+    if (lg == 0) mx_sh[wv][ln] = mloc;
+    barrier_lds();  // #1: the tiles' maxima, their P and the staged rows
+    float mblk = mx_sh[0][ln];
+#pragma unroll
+    for (int w = 1; w < kF8Waves; ++w) mblk = fmaxf(mblk, mx_sh[w][ln]);
+    // the reference moves only when a step's maximum exceeds it by more than kSlack (always
+    // when it has none yet)
+    const bool move = mblk > m_ref + kSlack;
+    if (__ballot(move)) {
+      const float m_new = move ? mblk : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DTW; ++dt) o[dt] *= alpha;
+      psum = make_p();  // (no wave reads P before the barrier below)
+      barrier_lds();    // #1b: P against the moved reference
     }
-    barrier_lds();  // #2: P of the tiles and the staged rows
+    l_run += psum;
     // O^T += V^T . P^T over the step, one 32-row block at a time (P_hi and P_lo MFMAs)
 #pragma unroll
     for (int kh = 0; kh < kF8Waves / 2; ++kh) {
